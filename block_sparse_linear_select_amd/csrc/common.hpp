@@ -1,0 +1,157 @@
+// Device-side building blocks shared by the gfx950 kernels: operand
+// fragments for 16x16x32 matrix-core steps, conversions and small wave
+// utilities.  Everything here is written for CDNA4 wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64;     // tokens per tile (query and key)
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct bf16_t { uint16_t bits; };   // storage type of a bfloat16 element
+struct fp8_t { uint8_t bits; };     // storage type of an OCP E4M3FN element
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float -> bfloat16 bits (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP E4M3FN code -> float (bias 7, subnormals at exponent 0; NaN codes do
+// not occur in valid inputs and decode to a large finite value here).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 0x7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;  // m/8 * 2^-6
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// ---------------------------------------------------------------------------
+// Fragments.  A fragment is what one lane holds of a 16 x 32 operand of a
+// 16x16x32 step: lane l holds row (l % 16) and the 8 contraction indices
+// k = 8*(l/16) + s, s = 0..7.  The accumulator of a step is 16x16 float with
+// lane l holding column (l % 16), rows 4*(l/16) + i, i = 0..3.
+// For bf16 the step is one v_mfma_f32_16x16x32_bf16; for float it is eight
+// v_mfma_f32_16x16x4_f32 steps, step s contracting index 8*(l/16) + s.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+  u32x4 w;  // 8 bf16, element s in the low/high half of word s/2
+  __device__ __forceinline__ void zero() { w = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void set_pair(int j, float a, float b) { w[j] = pack_bf16x2(a, b); }
+};
+
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = 0.f;
+  }
+  __device__ __forceinline__ void set_pair(int j, float a, float b) { v[2 * j] = a; v[2 * j + 1] = b; }
+};
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.w),
+                                              __builtin_bit_cast(bf16x8_t, b.w), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+// Load 8 consecutive elements (one fragment's worth) from memory of type T.
+__device__ __forceinline__ void load8(Frag<bf16_t>& f, const bf16_t* p) {
+  f.w = *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  float4 a = q[0], b = q[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Raw 8-element chunk of the storage type, kept in registers between a
+// global load and an LDS store.
+template <typename T> struct Chunk8;
+template <> struct Chunk8<bf16_t> { u32x4 w; };
+template <> struct Chunk8<float> { float4 a, b; };
+template <> struct Chunk8<fp8_t> { uint2 w; };
+
+__device__ __forceinline__ void gload8(Chunk8<bf16_t>& c, const bf16_t* p) { c.w = *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void gload8(Chunk8<float>& c, const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  c.a = q[0]; c.b = q[1];
+}
+__device__ __forceinline__ void gload8(Chunk8<fp8_t>& c, const fp8_t* p) { c.w = *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void zero8(Chunk8<bf16_t>& c) { c.w = u32x4{0, 0, 0, 0}; }
+__device__ __forceinline__ void zero8(Chunk8<float>& c) { c.a = make_float4(0, 0, 0, 0); c.b = c.a; }
+__device__ __forceinline__ void zero8(Chunk8<fp8_t>& c) { c.w = make_uint2(0, 0); }
+
+// Element e (0..7) of a chunk as float.
+__device__ __forceinline__ float elem(const Chunk8<bf16_t>& c, int e) {
+  uint32_t w = c.w[e >> 1];
+  return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+__device__ __forceinline__ float elem(const Chunk8<float>& c, int e) {
+  switch (e) {
+    case 0: return c.a.x; case 1: return c.a.y; case 2: return c.a.z; case 3: return c.a.w;
+    case 4: return c.b.x; case 5: return c.b.y; case 6: return c.b.z; default: return c.b.w;
+  }
+}
+__device__ __forceinline__ float elem(const Chunk8<fp8_t>& c, int e) {
+  uint32_t w = (e < 4) ? c.w.x : c.w.y;
+  return e4m3_to_f32((w >> (8 * (e & 3))) & 0xFFu);
+}
+
+// ---------------------------------------------------------------------------
+// wave utilities
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+// max / sum over the four 16-lane groups that share a column
+__device__ __forceinline__ float group4_max(float x) {
+  x = fmaxf(x, wave_xor(x, 16));
+  return fmaxf(x, wave_xor(x, 32));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  x += wave_xor(x, 16);
+  return x + wave_xor(x, 32);
+}
+
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// XCD-aware block order: consecutive logical blocks land on the same XCD
+// (hardware hands block i to XCD i % 8), so neighbouring query tiles of one
+// head share that XCD's L2.  Returns -1 for the padding blocks.
+__device__ __forceinline__ long xcd_remap(long i, long n_logical) {
+  long per = (n_logical + 7) / 8;
+  long l = (i % 8) * per + i / 8;
+  return l < n_logical ? l : -1;
+}
+
+}  // namespace hsa

@@ -1,0 +1,216 @@
+// Tile selection: pooled score grid, per-row top-k and CSR emission.
+//
+// The sparse branch keeps only the high-energy query/key tile interactions
+// (SparkDiffusion news article, section 05); at 90% / 97% sparsity that is 10% /
+// 3% of the 64x64 tiles (same article, section 01), taken here as a fixed top-k
+// per query-tile row.  Scores are float64 dot products of the float64 tile
+// means, so the kept set is decided at the precision of the definition;
+// ties are broken towards the lower tile index.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hsa {
+
+// -------------------------------------------------------------- scores
+// sigma[a][b] = qbar_a . kbar_b for one (b, h), float64 16x16x4 matrix-core
+// steps.  Block: 4 waves, one 16-row block of a; each wave walks the 16-column
+// blocks w, w+4, ...  Means are stored transposed ([d][T]) so that a lane
+// group reads 16 consecutive tiles.
+template <int D>
+__global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict__ qbarT,
+                                                const double* __restrict__ kbarT, double* __restrict__ scores) {
+  const int bh = blockIdx.y, rb = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const double* qb = qbarT + (size_t)bh * D * T;
+  const double* kb = kbarT + (size_t)bh * D * T;
+  double* out = scores + (size_t)bh * T * T;
+  const int row = 16 * rb + l16;
+  double af[D / 4];
+#pragma unroll
+  for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)(4 * s + g) * T + row] : 0.0;
+  const int ncb = (T + 15) / 16;
+  for (int cb = w; cb < ncb; cb += 4) {
+    const int col = 16 * cb + l16;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < D / 4; ++s) {
+      double bf = col < T ? kb[(size_t)(4 * s + g) * T + col] : 0.0;
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], bf, acc, 0, 0, 0);
+    }
+    if (col < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int rr = 16 * rb + 4 * g + i;
+        if (rr < T) out[(size_t)rr * T + col] = acc[i];
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- top-k
+// Order-preserving 64-bit key of a float64 (larger key <=> larger value;
+// -0 is folded onto +0 so that equal values tie).
+__device__ __forceinline__ uint64_t order_key(double x) {
+  if (x == 0.0) x = 0.0;
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row
+
+// One wave per row: radix-select the k-th largest key (8 passes of 8 bits),
+// keep every key above it and the lowest-index keys equal to it, add the
+// diagonal if forced, and write the kept tiles in ascending order.
+__global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int force_diag, int direct,
+                                              const double* __restrict__ scores, int32_t* __restrict__ out_cols,
+                                              int32_t* __restrict__ out_cnt, int32_t* __restrict__ row_ptr) {
+  __shared__ uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + w;
+  const bool live = row < rows;
+  const int a = live ? row % T : 0;
+  const double* src = scores + (size_t)(live ? row : 0) * T;
+  const int nj = (T + 63) / 64;
+
+  uint64_t key[kMaxJ];
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    int b = lane + 64 * j;
+    key[j] = (j < nj && b < T && live) ? order_key(src[b]) : 0ull;
+  }
+
+  uint64_t prefix = 0, mask = 0;
+  int need = topk;
+  uint32_t* hw = hist[w];
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = lane; i < 256; i += 64) hw[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (j < nj && (key[j] & mask) == prefix && key[j] != 0ull)
+        atomicAdd(&hw[(key[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    // lane l owns digits 4l .. 4l+3; count from the top digit down
+    uint32_t h0 = hw[4 * lane], h1 = hw[4 * lane + 1], h2 = hw[4 * lane + 2], h3 = hw[4 * lane + 3];
+    uint32_t mine = h0 + h1 + h2 + h3;
+    // inclusive suffix sum over lanes (lanes above hold larger digits)
+    uint32_t suf = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    uint32_t above = suf - mine;  // count in digits > 4l+3
+    int found = -1, rest = 0;
+    uint32_t hh[4] = {h0, h1, h2, h3};
+    uint32_t cum = above;
+#pragma unroll
+    for (int dd = 3; dd >= 0; --dd) {
+      if (found < 0 && cum < (uint32_t)need && cum + hh[dd] >= (uint32_t)need) {
+        found = 4 * lane + dd;
+        rest = need - (int)cum;
+      }
+      cum += hh[dd];
+    }
+    uint64_t bal = __ballot(found >= 0);
+    int src_lane = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
+    int digit = __shfl(found, src_lane, 64);
+    need = __shfl(rest, src_lane, 64);
+    prefix |= ((uint64_t)(digit < 0 ? 0 : digit)) << shift;
+    mask |= 255ull << shift;
+    __syncthreads();
+  }
+  const uint64_t kth = prefix;
+
+  // selection flags: strictly above the threshold, then ties by lowest index
+  uint32_t sel = 0;  // bit j: element j of this lane is kept
+  int taken = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    if (j >= nj) break;
+    bool above = key[j] > kth;
+    bool eq = key[j] == kth && key[j] != 0ull;
+    uint64_t be = __ballot(eq);
+    int before = __popcll(be & lt_mask);
+    if (above || (eq && taken + before < need)) sel |= 1u << j;
+    taken += __popcll(be);
+  }
+  if (force_diag && lane == (a & 63)) sel |= 1u << (a >> 6);
+
+  // emit ascending
+  int base_pos = 0;
+  const size_t obase = direct ? (size_t)row * topk : (size_t)row * (topk + 1);
+#pragma unroll
+  for (int j = 0; j < kMaxJ; ++j) {
+    if (j >= nj) break;
+    bool s = (sel >> j) & 1u;
+    uint64_t bs = __ballot(s);
+    if (s && live) out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
+    base_pos += __popcll(bs);
+  }
+  if (live && lane == 0) {
+    if (direct) {
+      row_ptr[row] = row * topk;
+      if (row == rows - 1) row_ptr[rows] = rows * topk;
+    } else {
+      out_cnt[row] = base_pos;
+    }
+  }
+}
+
+// Exclusive scan of the per-row counts into row_ptr (single block).
+__global__ __launch_bounds__(1024) void k_scan(int rows, const int32_t* __restrict__ cnt, int32_t* __restrict__ row_ptr) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < rows; base += 1024) {
+    int i = base + threadIdx.x;
+    int v = i < rows ? cnt[i] : 0;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int t = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += t;
+      __syncthreads();
+    }
+    if (i < rows) row_ptr[i] = carry + part[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) row_ptr[rows] = carry;
+}
+
+__global__ void k_compact(int rows, int stride, const int32_t* __restrict__ tmp, const int32_t* __restrict__ cnt,
+                          const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+  int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  int n = cnt[row], o = row_ptr[row];
+  for (int i = 0; i < n; ++i) col_idx[o + i] = tmp[(size_t)row * stride + i];
+}
+
+hipError_t launch_select(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+  const int bh = s.B * s.H;
+  dim3 g1((s.T + 15) / 16, bh);
+  if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
+  else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = bh * s.T;
+  const int direct = s.force_diag ? 0 : 1;
+  k_topk<<<(rows + 3) / 4, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores,
+                                         direct ? col_idx : w.sel_tmp, w.sel_cnt, row_ptr);
+  e = hipGetLastError();
+  if (e != hipSuccess || direct) return e;
+  k_scan<<<1, 1024, 0, st>>>(rows, w.sel_cnt, row_ptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_compact<<<(rows + 255) / 256, 256, 0, st>>>(rows, s.topk + 1, w.sel_tmp, w.sel_cnt, row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -1,0 +1,42 @@
+// Launchers of the streaming pass and the state finalize (bf16 and fp8
+// inputs; the float32 instantiations live in k_stream_f32.hip).
+#include "stream.hpp"
+
+namespace hsa {
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_rope_table(const Shape& s, float2* tab, hipStream_t st) {
+  int n = rope_entries(s);
+  k_rope_table<<<(n + 255) / 256, 256, 0, st>>>(s.gt, s.gh, s.gw, s.rank, (double)s.rope_base, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* qs, const float* ks, const float* vs,
+                              const void* uk, bool pool, bool state, const Scratch& w,
+                              double* qbar_out, double* kbar_out, hipStream_t st) {
+  StreamArgs a{};
+  a.N = s.N; a.N_pad = s.N_pad; a.T = s.T;
+  a.nchunk = stream_chunks(s);
+  a.tpc = (s.T + a.nchunk - 1) / a.nchunk;
+  a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
+  a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
+  a.qbarT = w.qbarT; a.kbarT = w.kbarT; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
+  a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope;
+  switch (s.dt) {
+    case Dt::F32: return launch_stream_f32(s, a, pool, state, st);
+    case Dt::BF16: return stream_by_shape<bf16_t, bf16_t>(s, a, pool, state, st);
+    default: return stream_by_shape<fp8_t, bf16_t>(s, a, pool, state, st);
+  }
+}
+
+hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const Scratch& w, hipStream_t st) {
+  FinalArgs a{};
+  a.nchunk = stream_chunks(s); a.H = s.H; a.B = s.B;
+  a.part_s = w.part_s; a.part_z = w.part_z; a.wo = wo; a.uq = uq;
+  a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag;
+  if (s.dt == Dt::F32) return launch_finalize_f32(s, a, st);
+  return finalize_by_shape<bf16_t>(s, a, st);
+}
+
+}  // namespace hsa

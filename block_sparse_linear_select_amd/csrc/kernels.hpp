@@ -1,0 +1,80 @@
+// Internal interface between the C-ABI shim (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsa {
+
+enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+// Validated sizes as the kernels see them.
+struct Shape {
+  int B, H, N, N_pad, d, T;
+  int gt, gh, gw;
+  int topk, force_diag, kmax;
+  int rank;
+  float scale;      // softmax scale
+  float rope_base;
+  Dt dt;
+};
+
+// RoPE table: for axis a (t, h, w) with D_a feature dims, the float2
+// (cos, sin) of pos * base^(-2m/D_a) at tab[rope_off(a) + pos * D_a/2 + m].
+inline int rope_dims(int rank, int axis) { return axis < 2 ? 3 * rank / 8 : rank / 4; }
+inline int rope_entries(const Shape& s) {
+  return s.gt * rope_dims(s.rank, 0) / 2 + s.gh * rope_dims(s.rank, 1) / 2 + s.gw * rope_dims(s.rank, 2) / 2;
+}
+
+// Number of token chunks per (b, h) in the streaming pass over K/V.
+inline int stream_chunks(const Shape& s) {
+  int c = 32;
+  if (c > s.T) c = s.T;
+  return c;
+}
+
+// Device scratch of one call, carved out of the caller's workspace.
+struct Scratch {
+  double* qbarT = nullptr;     // [BH][d][T] tile means of Q
+  double* kbarT = nullptr;     // [BH][d][T] tile means of K
+  double* scores = nullptr;    // [BH][T][T] float64 pooled scores
+  int32_t* sel_tmp = nullptr;  // [BH*T][kmax] per-row selection (forced-diagonal path)
+  int32_t* sel_cnt = nullptr;  // [BH*T]
+  int32_t* row_ptr = nullptr;  // [BH*T + 1] internal CSR when the caller exports none
+  int32_t* col_idx = nullptr;  // [BH*T*kmax]
+  float* part_s = nullptr;     // [BH][chunks][r][d] partial states
+  float* part_z = nullptr;     // [BH][chunks][r]
+  void* sp_frag = nullptr;     // [BH] S' = S W_o as readout fragments (hi, lo)
+  float* z = nullptr;          // [BH][r]
+  void* uq_frag = nullptr;     // [H] U_q^T as readout fragments
+  float2* rope = nullptr;      // RoPE table
+};
+
+// Workspace planning: byte offsets of each region for a given call.
+struct Plan {
+  size_t total = 0;
+  size_t off_qbarT = 0, off_kbarT = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
+  size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
+  size_t off_z = 0, off_uq = 0, off_rope = 0;
+  bool select = false, csr_internal = false, linear = false;
+};
+
+Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear);
+Scratch bind_plan(const Plan& p, void* ws);
+
+// Launchers: each enqueues its kernels on `st` and returns hipSuccess or the
+// launch error.
+hipError_t launch_rope_table(const Shape& s, float2* tab, hipStream_t st);
+hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, const void* v,
+                              const float* qs, const float* ks, const float* vs,
+                              const void* uk, bool pool, bool state, const Scratch& w,
+                              double* qbar_out, double* kbar_out, hipStream_t st);
+hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const Scratch& w, hipStream_t st);
+hipError_t launch_select(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
+hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
+                         const float* qs, const float* ks, const float* vs,
+                         const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,
+                         const Scratch& w, void* o, float* lse, hipStream_t st);
+
+}  // namespace hsa

@@ -1,0 +1,456 @@
+// Kernels of the streaming pass over Q, K, V (one read of each) and the finalize step of the
+// linear branch.
+//
+//  * Tile pooling: float64 column sums of the valid rows of every 64-token tile
+//    of Q and K, divided by the valid count (the mean-pooled tile statistic used
+//    to find the high-energy tiles; SparkDiffusion news article, section 05).
+//  * Linear key/value state of the rotary low-rank branch (same section: a
+//    low-rank linear branch with rotary position information):
+//      F = K U_k (matrix cores), phi = elu(F) + 1, z += sum_j phi_j,
+//      k'_j = rope(phi_j, p_j),  S^T += V^T k'  (matrix cores, contraction
+//      over tokens).  Each block writes one partial (S, z); the finalize kernel
+//      adds the partials in a fixed order, so results are bitwise reproducible.
+//
+// The pass is HBM-bound: every element of Q, K, V is read once with 16-byte
+// loads, the next tile is prefetched into registers while the current one is
+// processed, and all arithmetic runs from LDS and registers.
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hsa {
+
+// ----------------------------------------------------------------- RoPE table
+static __global__ void k_rope_table(int gt, int gh, int gw, int rank, double base, float2* tab) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  int dims[3] = {3 * rank / 8, 3 * rank / 8, rank / 4};
+  int sizes[3] = {gt, gh, gw};
+  int off = 0;
+  for (int ax = 0; ax < 3; ++ax) {
+    int half = dims[ax] / 2, n = sizes[ax] * half;
+    if (i < off + n) {
+      int j = i - off, pos = j / half, m = j % half;
+      double theta = pow(base, -2.0 * (double)m / (double)dims[ax]);
+      double ang = (double)pos * theta;
+      tab[i] = make_float2((float)cos(ang), (float)sin(ang));
+      return;
+    }
+    off += n;
+  }
+}
+
+// Location of feature pair jp (0 .. r/2-1) in the RoPE table: axis, m and the
+// table offset of that axis.
+struct RopeSlot { int axis, m, half, off; };
+__device__ __forceinline__ RopeSlot rope_slot(int jp, int rank, int gt, int gh) {
+  int ht = 3 * rank / 16, hh = 3 * rank / 16, hw = rank / 8;  // pairs per axis
+  RopeSlot s;
+  if (jp < ht) { s.axis = 0; s.m = jp; s.half = ht; s.off = 0; }
+  else if (jp < ht + hh) { s.axis = 1; s.m = jp - ht; s.half = hh; s.off = gt * ht; }
+  else { s.axis = 2; s.m = jp - ht - hh; s.half = hw; s.off = gt * ht + gh * hh; }
+  return s;
+}
+
+__device__ __forceinline__ int pack_pos(int tok, int gh, int gw) {
+  int hw = gh * gw;
+  int t = tok / hw, rem = tok - t * hw;
+  int h = rem / gw, w = rem - h * gw;
+  return (t << 20) | (h << 10) | w;
+}
+__device__ __forceinline__ int pos_axis(int packed, int axis) {
+  return axis == 0 ? (packed >> 20) : (axis == 1 ? ((packed >> 10) & 1023) : (packed & 1023));
+}
+
+// ------------------------------------------------------ operand conversions
+template <typename T, typename OT> struct Conv;
+// Same type: raw copy.
+template <typename T> struct Conv<T, T> {
+  __device__ static void row(T* dst, const Chunk8<T>& c);
+};
+template <> __device__ void Conv<bf16_t, bf16_t>::row(bf16_t* dst, const Chunk8<bf16_t>& c) {
+  *reinterpret_cast<u32x4*>(dst) = c.w;
+}
+template <> __device__ void Conv<float, float>::row(float* dst, const Chunk8<float>& c) {
+  reinterpret_cast<float4*>(dst)[0] = c.a;
+  reinterpret_cast<float4*>(dst)[1] = c.b;
+}
+// FP8 codes -> exact bf16 values (E4M3 values fit bf16's 8-bit significand).
+template <> struct Conv<fp8_t, bf16_t> {
+  __device__ static void row(bf16_t* dst, const Chunk8<fp8_t>& c) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(elem(c, 2 * j), elem(c, 2 * j + 1));
+    *reinterpret_cast<u32x4*>(dst) = w;
+  }
+};
+
+// Write 4 consecutive values of operand type at dst.
+__device__ __forceinline__ void st4(bf16_t* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ void st4(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+// Position of key k (0..63) of a tile inside the transposed V layout used
+// as the A operand of a contraction over tokens: within each 32-key chunk,
+// key 16h + 4g + i sits at 8g + 4h + i, so that lane group g reads its eight
+// contraction slots with one 16-byte load.
+__device__ __forceinline__ int vt_pos(int key) {
+  int c = key >> 5, kk = key & 31;
+  int h = kk >> 4, g = (kk >> 2) & 3, i = kk & 3;
+  return 32 * c + 8 * g + 4 * h + i;
+}
+
+// --------------------------------------------------------- streaming pass
+struct StreamArgs {
+  int N, N_pad, T, nchunk, tpc;
+  int gt, gh, gw;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  const void* uk;  // [H][d][r] in the parameter type
+  int H;
+  double* qbarT;
+  double* kbarT;
+  double* qbar_out;
+  double* kbar_out;
+  float* part_s;
+  float* part_z;
+  const float2* rope;
+};
+
+template <typename T, typename OT, int D, int R, bool POOL, bool STATE>
+__global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
+  constexpr int CPR = D / 8;              // 8-element chunks per row
+  constexpr int NCONT = 256 / CPR;        // threads sharing a column chunk
+  constexpr int KCH = 64 * CPR / 256;     // row chunks per thread per tile
+  constexpr int NVU = 16 * CPR;           // V units (4 keys x 8 dims)
+  constexpr int KSTR = D + 8;             // LDS row stride of K (elements)
+  constexpr int VSTR = 64 + 8;            // LDS row stride of V^T
+  constexpr int NRB = R / 16;             // 16-wide blocks of the rank
+  constexpr int NDG = 4 / NRB;            // waves sharing an r block
+  constexpr int DBW = (D / 16) / NDG;     // 16-wide d blocks per wave
+  static_assert(R == 16 || R == 32 || R == 64, "rank");
+  static_assert(D == 64 || D == 128, "head dim");
+
+  __shared__ __align__(16) OT Ks[STATE ? 64 * KSTR : 1];
+  __shared__ __align__(16) OT Vt[STATE ? D * VSTR : 1];
+  __shared__ double redq[POOL ? NCONT * D : 1];
+  __shared__ double redk[POOL ? NCONT * D : 1];
+  __shared__ int spos[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int h = bh % a.H;
+  const int t0 = chunk * a.tpc;
+  const int t1 = min(a.T, t0 + a.tpc);
+  if (t0 >= t1) return;
+
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const T* Q = reinterpret_cast<const T*>(a.q) + base;
+  const T* K = reinterpret_cast<const T*>(a.k) + base;
+  const T* V = reinterpret_cast<const T*>(a.v) + base;
+  const int col8 = tid % CPR;
+  const int row0 = tid / CPR;
+
+  // per-wave linear-branch constants
+  const int rb = w % NRB, dg = w / NRB;
+  const int r = 16 * rb + l16;
+  Frag<OT> uf[D / 32];
+  RopeSlot rs;
+  float zacc = 0.f;
+  f32x4 accS[DBW];
+  if constexpr (STATE) {
+    const OT* U = reinterpret_cast<const OT*>(a.uk) + (size_t)h * D * R;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      float tmp[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const OT* p = U + (size_t)(32 * c + 8 * g + s) * R + r;
+        if constexpr (sizeof(OT) == 4) tmp[s] = *reinterpret_cast<const float*>(p);
+        else tmp[s] = bf16_bits_to_f32(reinterpret_cast<const bf16_t*>(p)->bits);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) uf[c].set_pair(j, tmp[2 * j], tmp[2 * j + 1]);
+    }
+    rs = rope_slot(r >> 1, R, a.gt, a.gh);
+#pragma unroll
+    for (int j = 0; j < DBW; ++j) accS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  Chunk8<T> qc[KCH], kc[KCH], vc[4];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      int row = row0 + i * NCONT;
+      int gr = t * 64 + row;
+      size_t off = (size_t)gr * D + col8 * 8;
+      if (gr < a.N) {
+        gload8(kc[i], K + off);
+        if constexpr (POOL) gload8(qc[i], Q + off);
+      } else {
+        zero8(kc[i]);
+        if constexpr (POOL) zero8(qc[i]);
+      }
+    }
+    if constexpr (STATE) {
+      if (tid < NVU) {
+        int kg = tid % 16, c8 = tid / 16;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          int gr = t * 64 + 4 * kg + ii;
+          if (gr < a.N) gload8(vc[ii], V + (size_t)gr * D + c8 * 8);
+          else zero8(vc[ii]);
+        }
+      }
+    }
+  };
+
+  load_tile(t0);
+  for (int t = t0; t < t1; ++t) {
+    // ---- registers -> LDS
+    if constexpr (POOL) {
+      double pq[8], pk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { pq[e] = 0.0; pk[e] = 0.0; }
+#pragma unroll
+      for (int i = 0; i < KCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pq[e] += (double)elem(qc[i], e); pk[e] += (double)elem(kc[i], e); }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        redq[row0 * D + col8 * 8 + e] = pq[e];
+        redk[row0 * D + col8 * 8 + e] = pk[e];
+      }
+    }
+    if constexpr (STATE) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Ks[(row0 + i * NCONT) * KSTR + col8 * 8], kc[i]);
+      if (tid < NVU) {
+        int kg = tid % 16, c8 = tid / 16;
+        int p0 = vt_pos(4 * kg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(vc[0], e), elem(vc[1], e), elem(vc[2], e), elem(vc[3], e));
+      }
+      if (tid < 64) spos[tid] = pack_pos(min(t * 64 + tid, a.N - 1), a.gh, a.gw);
+    }
+    __syncthreads();
+    if (t + 1 < t1) load_tile(t + 1);
+
+    if constexpr (STATE) {
+      const float sk = a.ks ? a.ks[(size_t)bh * a.T + t] : 1.f;
+      const float sv = a.vs ? a.vs[(size_t)bh * a.T + t] : 1.f;
+      f32x4 accF[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        accF[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          Frag<OT> kf;
+          load8(kf, &Ks[(16 * tb + l16) * KSTR + 32 * c + 8 * g]);
+          mma(accF[tb], kf, uf[c]);
+        }
+      }
+      float kp[4][4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int tok = 16 * tb + 4 * g + i;
+          float phi = (t * 64 + tok < a.N) ? elu1(accF[tb][i] * sk) : 0.f;
+          zacc += phi;
+          float other = __shfl_xor(phi, 1, 64);
+          int pa = pos_axis(spos[tok], rs.axis);
+          float2 cs = a.rope[rs.off + pa * rs.half + rs.m];
+          float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
+          kp[tb][i] = rot * sv;
+        }
+      }
+      Frag<OT> kf2[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kf2[c].set_pair(0, kp[2 * c][0], kp[2 * c][1]);
+        kf2[c].set_pair(1, kp[2 * c][2], kp[2 * c][3]);
+        kf2[c].set_pair(2, kp[2 * c + 1][0], kp[2 * c + 1][1]);
+        kf2[c].set_pair(3, kp[2 * c + 1][2], kp[2 * c + 1][3]);
+      }
+#pragma unroll
+      for (int j = 0; j < DBW; ++j) {
+        int db = dg * DBW + j;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<OT> vf;
+          load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
+          mma(accS[j], vf, kf2[c]);
+        }
+      }
+    }
+    if constexpr (POOL) {
+      if (tid < D) {
+        double sq = 0.0, sk2 = 0.0;
+        for (int c = 0; c < NCONT; ++c) { sq += redq[c * D + tid]; sk2 += redk[c * D + tid]; }
+        const double cnt = (double)min(64, a.N - t * 64);
+        if (a.qs) sq *= (double)a.qs[(size_t)bh * a.T + t];
+        if (a.ks) sk2 *= (double)a.ks[(size_t)bh * a.T + t];
+        const double mq = sq / cnt, mk = sk2 / cnt;
+        a.qbarT[((size_t)bh * D + tid) * a.T + t] = mq;
+        a.kbarT[((size_t)bh * D + tid) * a.T + t] = mk;
+        if (a.qbar_out) a.qbar_out[((size_t)bh * a.T + t) * D + tid] = mq;
+        if (a.kbar_out) a.kbar_out[((size_t)bh * a.T + t) * D + tid] = mk;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (STATE) {
+    const size_t pbase = ((size_t)bh * a.nchunk + chunk);
+#pragma unroll
+    for (int j = 0; j < DBW; ++j) {
+      int db = dg * DBW + j;
+      *reinterpret_cast<float4*>(&a.part_s[(pbase * R + r) * D + 16 * db + 4 * g]) =
+          make_float4(accS[j][0], accS[j][1], accS[j][2], accS[j][3]);
+    }
+    float zt = group4_sum(zacc);
+    if (dg == 0 && g == 0) a.part_z[pbase * R + r] = zt;
+  }
+}
+
+// ------------------------------------------------------------- finalize
+// Per (b, h): S = sum of the partial states (fixed order), S' = S W_o, and the
+// readout operands: S'^T as A fragments (float, or bf16 hi + lo), z, and
+// U_q^T as A fragments.
+struct FinalArgs {
+  int nchunk, H, B;
+  const float* part_s;
+  const float* part_z;
+  const void* wo;   // [H][d][d]
+  const void* uq;   // [H][d][r]
+  void* sp_frag;
+  float* z;
+  void* uq_frag;
+};
+
+template <typename OT, int D, int R>
+__global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
+  constexpr int NRC = (R + 31) / 32;
+  constexpr int NDB = D / 16;
+  constexpr int NRB = R / 16;
+  __shared__ float S[R * D];
+  __shared__ float Sp[R * D];
+  const int tid = threadIdx.x, bh = blockIdx.x, h = bh % a.H;
+  const float* ps = a.part_s + (size_t)bh * a.nchunk * R * D;
+  for (int e = tid; e < R * D; e += 256) {
+    float s = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) s += ps[(size_t)c * R * D + e];
+    S[e] = s;
+  }
+  if (tid < R) {
+    float s = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) s += a.part_z[((size_t)bh * a.nchunk + c) * R + tid];
+    a.z[(size_t)bh * R + tid] = s;
+  }
+  __syncthreads();
+  const OT* W = reinterpret_cast<const OT*>(a.wo) + (size_t)h * D * D;
+  for (int e = tid; e < R * D; e += 256) {
+    int rr = e / D, col = e % D;
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) {
+      float wv;
+      if constexpr (sizeof(OT) == 4) wv = reinterpret_cast<const float*>(W)[(size_t)d * D + col];
+      else wv = bf16_bits_to_f32(reinterpret_cast<const bf16_t*>(W)[(size_t)d * D + col].bits);
+      s = fmaf(S[rr * D + d], wv, s);
+    }
+    Sp[e] = s;
+  }
+  __syncthreads();
+  // S'^T fragments: frag (db, rc), lane l, slot s -> S'[r][e] with
+  // e = 16 db + l%16, r = 32 rc + 16 (s/4) + 4 (l/16) + s%4 (zero past R).
+  const int nfe = NDB * NRC * 64 * 8;
+  for (int idx = tid; idx < nfe; idx += 256) {
+    int s = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
+    int rc = fr % NRC, db = fr / NRC;
+    int e = 16 * db + (l & 15);
+    int rr = 32 * rc + 16 * (s >> 2) + 4 * (l >> 4) + (s & 3);
+    float x = rr < R ? Sp[rr * D + e] : 0.f;
+    if constexpr (sizeof(OT) == 4) {
+      reinterpret_cast<float*>(a.sp_frag)[(size_t)bh * nfe + idx] = x;
+    } else {
+      uint16_t hi = (uint16_t)f32_to_bf16_bits(x);
+      float rem = x - bf16_bits_to_f32(hi);
+      uint16_t lo = (uint16_t)f32_to_bf16_bits(rem);
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.sp_frag) + (size_t)bh * 2 * nfe;
+      out[idx] = hi;
+      out[nfe + idx] = lo;
+    }
+  }
+  // U_q^T fragments: frag (rb, c), lane l, slot s -> U_q[d][r] with
+  // r = 16 rb + l%16, d = 32 c + 8 (l/16) + s.  Written by the b = 0 blocks.
+  if (bh < a.H) {
+    const int nue = NRB * (D / 32) * 64 * 8;
+    const OT* U = reinterpret_cast<const OT*>(a.uq) + (size_t)h * D * R;
+    OT* out = reinterpret_cast<OT*>(a.uq_frag) + (size_t)h * nue;
+    for (int idx = tid; idx < nue; idx += 256) {
+      int s = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
+      int c = fr % (D / 32), rbk = fr / (D / 32);
+      int rr = 16 * rbk + (l & 15), d = 32 * c + 8 * (l >> 4) + s;
+      out[idx] = U[(size_t)d * R + rr];
+    }
+  }
+}
+
+
+// Launch helpers shared by the bf16/fp8 translation unit and the float32 one.
+template <typename T, typename OT, int D, int R>
+static hipError_t stream_dispatch(const Shape& s, const StreamArgs& a, bool pool, bool state, hipStream_t st) {
+  dim3 grid(a.nchunk, s.B * s.H);
+  if (pool && state) k_stream<T, OT, D, R, true, true><<<grid, 256, 0, st>>>(a);
+  else if (pool) k_stream<T, OT, D, R, true, false><<<grid, 256, 0, st>>>(a);
+  else k_stream<T, OT, D, R, false, true><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, typename OT>
+static hipError_t stream_by_shape(const Shape& s, const StreamArgs& a, bool pool, bool state, hipStream_t st) {
+  if (!state) {  // pooling only: the rank does not matter
+    return s.d == 64 ? stream_dispatch<T, OT, 64, 16>(s, a, pool, state, st)
+                     : stream_dispatch<T, OT, 128, 16>(s, a, pool, state, st);
+  }
+  if (s.d == 64) {
+    if (s.rank == 16) return stream_dispatch<T, OT, 64, 16>(s, a, pool, state, st);
+    if (s.rank == 32) return stream_dispatch<T, OT, 64, 32>(s, a, pool, state, st);
+    return stream_dispatch<T, OT, 64, 64>(s, a, pool, state, st);
+  }
+  if (s.rank == 16) return stream_dispatch<T, OT, 128, 16>(s, a, pool, state, st);
+  if (s.rank == 32) return stream_dispatch<T, OT, 128, 32>(s, a, pool, state, st);
+  return stream_dispatch<T, OT, 128, 64>(s, a, pool, state, st);
+}
+
+template <typename OT, int D, int R>
+static hipError_t finalize_dispatch(const Shape& s, const FinalArgs& a, hipStream_t st) {
+  k_finalize<OT, D, R><<<s.B * s.H, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename OT>
+static hipError_t finalize_by_shape(const Shape& s, const FinalArgs& a, hipStream_t st) {
+  if (s.d == 64) {
+    if (s.rank == 16) return finalize_dispatch<OT, 64, 16>(s, a, st);
+    if (s.rank == 32) return finalize_dispatch<OT, 64, 32>(s, a, st);
+    return finalize_dispatch<OT, 64, 64>(s, a, st);
+  }
+  if (s.rank == 16) return finalize_dispatch<OT, 128, 16>(s, a, st);
+  if (s.rank == 32) return finalize_dispatch<OT, 128, 32>(s, a, st);
+  return finalize_dispatch<OT, 128, 64>(s, a, st);
+}
+
+hipError_t launch_stream_f32(const Shape& s, const StreamArgs& a, bool pool, bool state, hipStream_t st);
+hipError_t launch_finalize_f32(const Shape& s, const FinalArgs& a, hipStream_t st);
+
+}  // namespace hsa

@@ -1,0 +1,191 @@
+/*
+ * hsa_attn.h -- C ABI of the block-sparse + rotary low-rank linear hybrid
+ * attention for video diffusion transformers, on AMD gfx950 (MI355X).
+ *
+ * The operation (SparkDiffusion news article, section 05 "RoLA"; RoLA paper
+ * title in the arXiv 2609.23153 listing, "Sources"): a block-sparse softmax
+ * branch keeps the high-energy query/key tile interactions, and a low-rank
+ * linear-attention branch with rotary position information restores the
+ * global context that the sparsification drops; the two are summed.  Raising
+ * sparsity from 90% to 97% keeps 3% instead of 10% of the tiles (same article,
+ * section 01), which here is a fixed top-k of 64x64 tiles per query-tile row.
+ * Reports must state density and block size (Video-Generation-101 handbook
+ * chapter on sparse computation, sections 1 and 6), which the CSR and the
+ * descriptor carry.
+ *
+ * Per (b, h) slice, with N valid tokens padded to N_pad = 64*T:
+ *   pooling   qbar_a, kbar_a = mean of the valid rows of tile a
+ *   scores    sigma_ab = qbar_a . kbar_b
+ *   select    M_a = top-k tiles by (sigma desc, index asc) [union {a}]
+ *   sparse    O_s,i = softmax over the valid keys of M_a of (scale * q_i . k_j) applied to v
+ *   features  phi(x) = elu(x) + 1 of q U_q and k U_k (rank r)
+ *   3D RoPE   r dims split 3r/8 : 3r/8 : r/4 over (t, h, w), adjacent pairs,
+ *             pair m of an axis block of D dims turns by p_axis * base^(-2m/D)
+ *   linear    O_l,i = (rho_i phi_q,i)^T S / (phi_q,i . z),
+ *             S = sum_j rho_j phi_k,j v_j^T, z = sum_j phi_k,j over valid j
+ *   output    O_i = O_s,i + O_l,i W_o (valid rows), 0 (pad rows)
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers, owned by the caller; the
+ *     library never frees or retains them past the call's stream work.
+ *   - Q, K, V, O: [B, H, N_pad, d] row-major, d innermost.  Rows >= N may
+ *     hold anything: they are never read as keys, and output rows >= N are
+ *     written as zeros.
+ *   - U_q, U_k: [H, d, r] row-major; W_o: [H, d, d] row-major (O_l W_o with
+ *     O_l a row vector).  Element type: float for in_dtype F32, bf16
+ *     otherwise (also for FP8 inputs).
+ *   - FP8 inputs: OCP E4M3FN byte codes; *_scale are float [B, H, T], the
+ *     value of a code is code * scale of its (b, h, tile).  Scales must be
+ *     NULL for the other dtypes.
+ *   - CSR: row_ptr int32 [B*H*T + 1] over the flattened (b, h, a) rows,
+ *     starting at 0 and non-decreasing; col_idx int32, each row sorted
+ *     ascending.  Output CSR capacity is B*H*T*(topk + force_diag) entries.
+ *     In an input CSR, entries outside [0, T) are skipped and a row with no
+ *     entries yields O_s = 0 for its queries.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises the host or copies device data to
+ *     the host.  The library allocates no device memory: scratch space comes
+ *     from the caller's workspace of at least hsa_attn_workspace_size()
+ *     bytes, 256-byte aligned, which must stay untouched until the stream
+ *     work completes.  Calls on different streams with separate workspaces
+ *     are independent.
+ *   - Every argument is validated before the first launch: a validation
+ *     error (NULL, SHAPE, DTYPE, WORKSPACE, CSR) means nothing was enqueued.
+ *     HSA_ATTN_ERR_HIP reports a failed launch (earlier kernels of the call
+ *     may have been enqueued).  After any non-zero return,
+ *     hsa_attn_last_error() (thread-local) holds a message.
+ */
+#ifndef HSA_ATTN_H
+#define HSA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HSA_ATTN_F32 = 0,      /* float32 */
+  HSA_ATTN_BF16 = 1,     /* bfloat16 */
+  HSA_ATTN_FP8_E4M3 = 2  /* OCP float8 E4M3FN with per-tile float32 scales */
+};
+
+enum {
+  HSA_ATTN_OK = 0,
+  HSA_ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  HSA_ATTN_ERR_SHAPE = -2,     /* inconsistent or unsupported sizes */
+  HSA_ATTN_ERR_DTYPE = -3,     /* unsupported dtype combination or scales mismatch */
+  HSA_ATTN_ERR_WORKSPACE = -4, /* workspace too small or misaligned */
+  HSA_ATTN_ERR_CSR = -5,       /* malformed CSR arguments (e.g. only one of a pair given) */
+  HSA_ATTN_ERR_HIP = -6        /* a kernel launch failed */
+};
+
+enum { /* which call a workspace size is asked for */
+  HSA_ATTN_CALL_BLOCK_SELECT = 0,
+  HSA_ATTN_CALL_SPARSE = 1,
+  HSA_ATTN_CALL_LINEAR = 2,
+  HSA_ATTN_CALL_HYBRID = 3
+};
+
+typedef struct hsa_attn_desc {
+  int32_t B, H;             /* batch, heads (>= 1) */
+  int32_t N, N_pad;         /* valid tokens; padded length: N_pad % 64 == 0, 0 <= N_pad - N < 64, N >= 1 */
+  int32_t d;                /* head dim: 64 or 128 */
+  int32_t tile;             /* must be 64 */
+  int32_t grid_t, grid_h, grid_w; /* latent grid, grid_t*grid_h*grid_w == N, frame-major raster */
+  int32_t topk;             /* tiles kept per row, 1 <= topk <= T */
+  int32_t force_diag;       /* 0 or 1: also keep tile a in row a (union) */
+  int32_t rank;             /* r: 16, 32 or 64 (multiple of 16) */
+  float softmax_scale;      /* usually 1/sqrt(d) */
+  float rope_base;          /* usually 10000 */
+  int32_t in_dtype;         /* HSA_ATTN_F32 | HSA_ATTN_BF16 | HSA_ATTN_FP8_E4M3 */
+  int32_t out_dtype;        /* F32 with F32 inputs; BF16 with BF16 or FP8 inputs */
+} hsa_attn_desc;
+
+/* Bytes of workspace `call` needs for `desc` (written to *bytes). */
+int hsa_attn_workspace_size(const hsa_attn_desc* desc, int call, size_t* bytes);
+
+/* Thread-local message describing the last non-zero return on this thread. */
+const char* hsa_attn_last_error(void);
+
+/* Library version string. */
+const char* hsa_attn_version(void);
+
+/*
+ * Per-kernel timing (a profiling aid, off by default).  While enabled, every
+ * kernel the library enqueues is bracketed by HIP events recorded on the same
+ * stream, for up to `max_launches` launches per kernel kind; enabling again
+ * resets the counts, 0 disables.  hsa_attn_timing_read() waits for the last
+ * recorded event and writes, for each kind in HSA_ATTN_KERNEL_* order, the
+ * summed milliseconds and the launch count.  Timing adds event records to the
+ * stream but no synchronisation to the calls themselves.
+ */
+enum {
+  HSA_ATTN_KERNEL_ROPE = 0,      /* RoPE cos/sin table */
+  HSA_ATTN_KERNEL_STREAM = 1,    /* tile pooling + linear key/value state pass */
+  HSA_ATTN_KERNEL_FINALIZE = 2,  /* state reduction, S W_o, readout operands */
+  HSA_ATTN_KERNEL_SELECT = 3,    /* pooled scores, top-k, CSR */
+  HSA_ATTN_KERNEL_ATTEND = 4,    /* block-sparse flash attention + linear readout */
+  HSA_ATTN_KERNEL_KINDS = 5
+};
+int hsa_attn_timing_enable(int max_launches);
+int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
+
+/*
+ * Tile selection: mean-pool Q and K per 64-token tile (float64 sums of the
+ * valid rows), score every (query tile, key tile) pair by the float64 dot
+ * product of the means, keep the top-k key tiles of every row (ties: lower
+ * index first; plus the diagonal tile if force_diag) and emit them as CSR.
+ *   row_ptr [B*H*T + 1], col_idx [B*H*T*(topk+force_diag)]: outputs.
+ *   qbar_out, kbar_out: optional float64 [B, H, T, d] tile means (NULL to skip).
+ */
+int hsa_block_select(const hsa_attn_desc* desc, const void* q, const void* k,
+                     const float* q_scale, const float* k_scale,
+                     int32_t* row_ptr, int32_t* col_idx,
+                     double* qbar_out, double* kbar_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse softmax branch on a given CSR: for each query tile, flash
+ * attention over the kept key tiles with float32 softmax statistics.
+ *   o_sparse: [B, H, N_pad, d] in out_dtype (rows >= N zero).
+ *   lse_out: optional float [B, H, N_pad] natural-log sum of exp(scale*q.k)
+ *   over the kept valid keys (NULL to skip; rows >= N undefined).
+ */
+int hsa_sparse_attn(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    const int32_t* row_ptr, const int32_t* col_idx,
+                    void* o_sparse, float* lse_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rotary low-rank linear branch alone, already multiplied by W_o:
+ *   o_lin = O_l W_o, [B, H, N_pad, d] in out_dtype (rows >= N zero).
+ * The key/value state is reduced in a fixed order (bitwise reproducible).
+ */
+int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    const void* U_q, const void* U_k, const void* W_o,
+                    void* o_lin, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole hybrid: O = O_s + O_l W_o.
+ *   row_ptr_in / col_idx_in: if both non-NULL, use this mask and skip
+ *   selection; if both NULL, select as hsa_block_select does.
+ *   row_ptr_out / col_idx_out: if both non-NULL (and no mask was given),
+ *   also export the selected CSR; both NULL to skip.
+ *   o: [B, H, N_pad, d] in out_dtype.
+ */
+int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    const void* U_q, const void* U_k, const void* W_o,
+                    const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                    int32_t* row_ptr_out, int32_t* col_idx_out,
+                    void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_ATTN_H */

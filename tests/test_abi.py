@@ -1,0 +1,104 @@
+"""The C ABI library: it loads, exports what include/hsa_attn.h declares, and
+rejects bad arguments before any launch (these calls touch no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_linear_select_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsa_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = _declared()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    assert B.version().startswith("hsa_attn")
+
+
+def _cfg(**kw):
+    base = dict(B=1, H=2, N=390, N_pad=448, d=128, grid=(3, 10, 13), topk=3, force_diag=False, rank=32,
+                softmax_scale=128 ** -0.5, rope_base=10000.0, dtype="bf16")
+    base.update(kw)
+    return B.Config(**base)
+
+
+def _ws(cfg, call):
+    n = ctypes.c_size_t(0)
+    d = cfg.desc()
+    rc = B.lib().hsa_attn_workspace_size(ctypes.byref(d), call, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(d=96), -2), (dict(N_pad=512), -2), (dict(N_pad=440), -2), (dict(grid=(3, 10, 12)), -2),
+    (dict(topk=0), -2), (dict(topk=8), -2), (dict(rank=24), -2), (dict(B=0), -2),
+])
+def test_bad_descriptors_are_rejected(bad, code):
+    rc, _ = _ws(_cfg(**bad), B.CALL_HYBRID)
+    assert rc == code
+    assert B.lib().hsa_attn_last_error()
+
+
+def test_bad_dtype_pair_is_rejected():
+    d = _cfg().desc()
+    d.out_dtype = B.F32
+    n = ctypes.c_size_t(0)
+    assert B.lib().hsa_attn_workspace_size(ctypes.byref(d), B.CALL_HYBRID, ctypes.byref(n)) == -3
+
+
+def test_workspace_grows_with_the_problem():
+    sizes = []
+    for grid, npad in (((3, 10, 13), 448), ((6, 10, 13), 832), ((12, 10, 13), 1600)):
+        cfg = _cfg(grid=grid, N=grid[0] * grid[1] * grid[2], N_pad=npad)
+        rc, n = _ws(cfg, B.CALL_HYBRID)
+        assert rc == 0
+        sizes.append(n)
+        rc2, n2 = _ws(cfg, B.CALL_SPARSE)
+        assert rc2 == 0 and n2 == 0  # the sparse branch needs no scratch
+        assert _ws(cfg, B.CALL_LINEAR)[1] < n
+    assert sizes == sorted(sizes) and len(set(sizes)) == 3
+
+
+def test_null_and_workspace_errors_enqueue_nothing():
+    L = B.lib()
+    cfg = _cfg()
+    d = cfg.desc()
+    vp = ctypes.c_void_p
+    # missing tensors
+    assert L.hsa_hybrid_attn(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                             None, None, None, None, None, None, 0, None) == -1
+    fake = vp(1 << 20)  # never dereferenced: validation fails first
+    # workspace too small
+    rc = L.hsa_hybrid_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, fake,
+                           None, None, None, None, fake, fake, 16, None)
+    assert rc == -4
+    # misaligned workspace
+    need = _ws(cfg, B.CALL_HYBRID)[1]
+    rc = L.hsa_hybrid_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, fake,
+                           None, None, None, None, fake, vp((1 << 20) + 8), need, None)
+    assert rc == -4
+    # half a CSR
+    rc = L.hsa_hybrid_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, fake,
+                           fake, None, None, None, fake, fake, need, None)
+    assert rc == -5
+    # scales with bf16 inputs
+    rc = L.hsa_sparse_attn(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, fake, fake, None,
+                           None, 0, None)
+    assert rc == -3
+    # fp8 without scales
+    d8 = _cfg(dtype="fp8").desc()
+    rc = L.hsa_block_select(ctypes.byref(d8), fake, fake, None, None, fake, fake, None, None, fake, need, None)
+    assert rc == -3
+    assert b"scale" in L.hsa_attn_last_error()

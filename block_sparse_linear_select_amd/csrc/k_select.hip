@@ -39,9 +39,10 @@ __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict_
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], bf, acc, 0, 0, 0);
     }
     if (col < T) {
+      // float64 16x16x4 accumulator: register i of lane group g holds row 4i + g
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int rr = 16 * rb + 4 * g + i;
+        int rr = 16 * rb + 4 * i + g;
         if (rr < T) out[(size_t)rr * T + col] = acc[i];
       }
     }

@@ -106,7 +106,8 @@ static int check_desc(const hsa_attn_desc* d, Shape& s, bool need_rank, bool nee
   if (d->force_diag != 0 && d->force_diag != 1) return fail(HSA_ATTN_ERR_SHAPE, "force_diag=%d must be 0 or 1", d->force_diag);
   if (need_rank && d->rank != 16 && d->rank != 32 && d->rank != 64)
     return fail(HSA_ATTN_ERR_SHAPE, "rank=%d: supported ranks are 16, 32, 64", d->rank);
-  if (!(isfinite(d->softmax_scale))) return fail(HSA_ATTN_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
+    return fail(HSA_ATTN_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (need_rank && !(d->rope_base > 0.f && isfinite(d->rope_base))) return fail(HSA_ATTN_ERR_SHAPE, "rope_base must be > 0");
   const bool ok_dt = (d->in_dtype == HSA_ATTN_F32 && d->out_dtype == HSA_ATTN_F32) ||
                      (d->in_dtype == HSA_ATTN_BF16 && d->out_dtype == HSA_ATTN_BF16) ||

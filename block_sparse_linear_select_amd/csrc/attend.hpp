@@ -13,6 +13,8 @@
 // register prefetch overlap the next tile's HBM/L2 reads with the current
 // tile's matrix-core work.
 #pragma once
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -57,6 +59,95 @@ __device__ __forceinline__ void lds_row(float* dst, const Chunk8<float>& c) {
   reinterpret_cast<float4*>(dst)[1] = c.b;
 }
 
+// Readout of the linear branch for the 16 queries of one fragment column:
+// phi_q = elu(q U_q) + 1, q' = rope(phi_q), O_lW = (q' S') / (phi_q . z).
+// qf holds the queries as B fragments; the result lands in the accumulator
+// layout of O^T (lane: query l%16, dims 16 jd + 4 (l/16) + i).
+template <typename T, int D, int R>
+__device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<T>* qf, int qrow, bool qvalid,
+                                        int lane, f32x4* acc_n, float& inv_den) {
+  constexpr int NDB = D / 16;
+  constexpr int NRB = R / 16;
+  constexpr int NRC = (R + 31) / 32;
+  const int g = lane >> 4;
+  const int h = bh % a.H;
+  const T* UQ = reinterpret_cast<const T*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
+  const float* Z = a.z + (size_t)bh * R;
+  f32x4 f[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    f[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      Frag<T> uf;
+      load8(uf, UQ + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+      mma(f[rb], uf, qf[c]);
+    }
+  }
+  // query position
+  int qpos[3];
+  {
+    int tok = qvalid ? qrow : 0, hw = a.gh * a.gw;
+    qpos[0] = tok / hw;
+    int rem = tok - qpos[0] * hw;
+    qpos[1] = rem / a.gw;
+    qpos[2] = rem - qpos[1] * a.gw;
+  }
+  const int ht = 3 * R / 16, hh = 3 * R / 16, hwp = R / 8;
+  float den = 0.f;
+  float qp[NRB][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float phi = elu1(f[rb][i]);
+      f[rb][i] = phi;
+      den += phi * Z[16 * rb + 4 * g + i];
+    }
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      int jp = (16 * rb + 4 * g) / 2 + pr;
+      int axis, m, half, off;
+      if (jp < ht) { axis = 0; m = jp; half = ht; off = 0; }
+      else if (jp < ht + hh) { axis = 1; m = jp - ht; half = hh; off = a.gt * ht; }
+      else { axis = 2; m = jp - ht - hh; half = hwp; off = a.gt * ht + a.gh * hh; }
+      float2 cs = a.rope[off + qpos[axis] * half + m];
+      float x0 = f[rb][2 * pr], x1 = f[rb][2 * pr + 1];
+      qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
+      qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+    }
+  }
+  den = group4_sum(den);
+  inv_den = den > 0.f ? 1.f / den : 0.f;
+  Frag<T> qpf[NRC];
+#pragma unroll
+  for (int rc = 0; rc < NRC; ++rc) {
+    constexpr int kHi = 1;  // second 16-block of the 32-wide chunk
+    const int b0 = 2 * rc, b1 = (2 * rc + kHi < NRB) ? 2 * rc + kHi : 2 * rc;
+    const float keep = (2 * rc + kHi < NRB) ? 1.f : 0.f;  // rank 16: upper half is zero
+    qpf[rc].set_pair(0, qp[b0][0], qp[b0][1]);
+    qpf[rc].set_pair(1, qp[b0][2], qp[b0][3]);
+    qpf[rc].set_pair(2, keep * qp[b1][0], keep * qp[b1][1]);
+    qpf[rc].set_pair(3, keep * qp[b1][2], keep * qp[b1][3]);
+  }
+  constexpr int NFE = NDB * NRC * 512;
+  const T* SP = reinterpret_cast<const T*>(a.sp_frag) + (size_t)bh * (sizeof(T) == 4 ? 1 : 2) * NFE;
+#pragma unroll
+  for (int jd = 0; jd < NDB; ++jd) {
+    acc_n[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rc = 0; rc < NRC; ++rc) {
+      Frag<T> sf;
+      load8(sf, SP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+      mma(acc_n[jd], sf, qpf[rc]);
+      if constexpr (sizeof(T) == 2) {
+        load8(sf, SP + NFE + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        mma(acc_n[jd], sf, qpf[rc]);
+      }
+    }
+  }
+}
+
 template <typename T, int D, int R, bool SPARSE, bool LINEAR>
 __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   constexpr int CPR = D / 8;
@@ -71,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   constexpr int STAGE = SPARSE ? (64 * KSTR + D * VSTR) : 1;
   __shared__ __align__(16) T lds[2 * STAGE];
 
-  const long L = xcd_remap(blockIdx.x, a.nrows);
+  const long L = head_interleaved_row(blockIdx.x, a.T);
   if (L < 0) return;
   const int bh = (int)(L / a.T), qa = (int)(L % a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -198,84 +289,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 
   f32x4 acc_n[NDB];
   float inv_den = 0.f;
-  if constexpr (LINEAR) {
-    const int h = bh % a.H;
-    const T* UQ = reinterpret_cast<const T*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
-    const float* Z = a.z + (size_t)bh * R;
-    f32x4 f[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      f[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        Frag<T> uf;
-        load8(uf, UQ + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
-        mma(f[rb], uf, qf[c]);
-      }
-    }
-    // query position
-    int qpos[3];
-    {
-      int tok = qvalid ? qrow : 0, hw = a.gh * a.gw;
-      qpos[0] = tok / hw;
-      int rem = tok - qpos[0] * hw;
-      qpos[1] = rem / a.gw;
-      qpos[2] = rem - qpos[1] * a.gw;
-    }
-    const int ht = 3 * R / 16, hh = 3 * R / 16, hwp = R / 8;
-    float den = 0.f;
-    float qp[NRB][4];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float phi = elu1(f[rb][i]);
-        f[rb][i] = phi;
-        den += phi * Z[16 * rb + 4 * g + i];
-      }
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        int jp = (16 * rb + 4 * g) / 2 + pr;
-        int axis, m, half, off;
-        if (jp < ht) { axis = 0; m = jp; half = ht; off = 0; }
-        else if (jp < ht + hh) { axis = 1; m = jp - ht; half = hh; off = a.gt * ht; }
-        else { axis = 2; m = jp - ht - hh; half = hwp; off = a.gt * ht + a.gh * hh; }
-        float2 cs = a.rope[off + qpos[axis] * half + m];
-        float x0 = f[rb][2 * pr], x1 = f[rb][2 * pr + 1];
-        qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
-        qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
-      }
-    }
-    den = group4_sum(den);
-    inv_den = den > 0.f ? 1.f / den : 0.f;
-    Frag<T> qpf[NRC];
-#pragma unroll
-    for (int rc = 0; rc < NRC; ++rc) {
-      constexpr int kHi = 1;  // second 16-block of the 32-wide chunk
-      const int b0 = 2 * rc, b1 = (2 * rc + kHi < NRB) ? 2 * rc + kHi : 2 * rc;
-      const float keep = (2 * rc + kHi < NRB) ? 1.f : 0.f;  // rank 16: upper half is zero
-      qpf[rc].set_pair(0, qp[b0][0], qp[b0][1]);
-      qpf[rc].set_pair(1, qp[b0][2], qp[b0][3]);
-      qpf[rc].set_pair(2, keep * qp[b1][0], keep * qp[b1][1]);
-      qpf[rc].set_pair(3, keep * qp[b1][2], keep * qp[b1][3]);
-    }
-    constexpr int NFE = NDB * NRC * 512;
-    const T* SP = reinterpret_cast<const T*>(a.sp_frag) + (size_t)bh * (sizeof(T) == 4 ? 1 : 2) * NFE;
-#pragma unroll
-    for (int jd = 0; jd < NDB; ++jd) {
-      acc_n[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int rc = 0; rc < NRC; ++rc) {
-        Frag<T> sf;
-        load8(sf, SP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-        mma(acc_n[jd], sf, qpf[rc]);
-        if constexpr (sizeof(T) == 2) {
-          load8(sf, SP + NFE + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-          mma(acc_n[jd], sf, qpf[rc]);
-        }
-      }
-    }
-  }
+  if constexpr (LINEAR) readout<T, D, R>(a, bh, qf, qrow, qvalid, lane, acc_n, inv_den);
 
   // epilogue: O = O_s / l + (q' S') / den, pad rows zero
   T* O = reinterpret_cast<T*>(a.o) + base + (size_t)qrow * D;
@@ -295,10 +309,270 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 query-tile kernel.  One block = one (b, h, query tile) = 2 waves of 32
+// queries; each wave keeps its queries as two 16-column B-fragment sets, so
+// every K or V fragment read from LDS feeds two matrix-core steps.
+// K and V tiles sit in LDS row-major, in 16-byte granules XOR-swizzled by row
+// (granule c of row r at c ^ (r mod G)), which keeps both the 16-byte K reads
+// and the transposing V reads free of bank conflicts.  V fragments come
+// straight from the row-major tile through ds_read_b64_tr_b16: within each
+// 16-lane group, output lane i, element t is element (i mod 4) of the 8 bytes
+// addressed by source lane 4t + i/4.  NSTAGE = 1 or 2 LDS tile buffers.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, bounds-checked (gfx9-family dword 3)
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+template <int D>
+__device__ __forceinline__ int swz(int row, int granule) {
+  constexpr int G = D / 8;
+  return row * D + ((granule ^ (row & (G - 1))) << 3);
+}
+
+template <int D, int R, bool SPARSE, bool LINEAR, int NSTAGE>
+__global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(AttendArgs a) {
+  constexpr int G = D / 8;            // 16-byte granules per row
+  constexpr int NQB = 2;              // 16-query blocks per wave
+  constexpr int NDB = D / 16;
+  constexpr int NGT = 64 * G / 128;   // granules per thread per tile
+  constexpr int TILE = 64 * D;        // elements per K (or V) tile
+  __shared__ __align__(16) bf16_t lds[SPARSE ? NSTAGE * 2 * TILE : 8];
+
+  const long L = head_interleaved_row(blockIdx.x, a.T);
+  if (L < 0) return;
+  const int bh = (int)(L / a.T), qa = (int)(L % a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + base;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + base;
+
+  // Bounds-checked buffer views of this head: rows >= N read as zero, and so
+  // does any offset past the slice (an out-of-range tile index included).
+  const int nbytes = a.N * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
+
+  int qrow[NQB];
+  bool qvalid[NQB];
+  Frag<bf16_t> qf[NQB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    qrow[qb] = qa * 64 + 32 * w + 16 * qb + l16;
+    qvalid[qb] = qrow[qb] < a.N;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      qf[qb][c].w = __builtin_amdgcn_raw_buffer_load_b128(qrs, (qrow[qb] * D + 32 * c + 8 * g) * 2, 0, 0);
+  }
+
+  f32x4 acc_o[NQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) acc_o[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float inv_l[NQB] = {0.f, 0.f};
+
+  if constexpr (SPARSE) {
+    const int beg = a.row_ptr[(size_t)bh * a.T + qa];
+    const int end = a.row_ptr[(size_t)bh * a.T + qa + 1];
+    // Running max (log2 units) is only raised when a row's new max exceeds
+    // it by more than 8, so exp2 arguments stay <= 8 and most tiles skip the
+    // rescale of O; the final O / l is the same for any valid max.
+    float m[NQB] = {-INFINITY, -INFINITY};
+    f32x4 acc_l[NQB];  // row sums of P, formed on the matrix cores
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) acc_l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<bf16_t> ones;
+    ones.w = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const float c2 = a.scale_log2;
+    u32x4 kr[NGT], vr[NGT];
+    auto load_tile = [&](int col) {
+#pragma unroll
+      for (int i = 0; i < NGT; ++i) {
+        const int q = tid + 128 * i, row = q / G, gr = q % G;
+        const int off = ((col * 64 + row) * D + gr * 8) * 2;
+        kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+        vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+      }
+    };
+    if (beg < end) load_tile(a.col_idx[beg]);
+    for (int j = beg; j < end; ++j) {
+      bf16_t* Ks = lds + (NSTAGE == 1 ? 0 : ((j - beg) & 1) * 2 * TILE);
+      bf16_t* Vs = Ks + TILE;
+      const int col = a.col_idx[j];
+      if constexpr (NSTAGE == 1) __syncthreads();  // the previous tile's reads are done
+#pragma unroll
+      for (int i = 0; i < NGT; ++i) {
+        const int q = tid + 128 * i, row = q / G, gr = q % G;
+        *reinterpret_cast<u32x4*>(&Ks[swz<D>(row, gr)]) = kr[i];
+        *reinterpret_cast<u32x4*>(&Vs[swz<D>(row, gr)]) = vr[i];
+      }
+      __syncthreads();
+      if (j + 1 < end) load_tile(a.col_idx[j + 1]);
+
+      const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
+      if (kvalid <= 0) continue;  // an out-of-range tile index contributes nothing
+      // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores)
+      f32x4 s[NQB][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          Frag<bf16_t> kf;
+          kf.w = *reinterpret_cast<const u32x4*>(&Ks[swz<D>(16 * kb + l16, 4 * c + g)]);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf, qf[qb][c]);
+        }
+      }
+      if (kvalid < 64) {  // ragged last tile: keys past N do not exist
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * kb + 4 * g + i >= kvalid) s[qb][kb][i] = -INFINITY;
+      }
+      float mt[NQB];
+      bool raise = false;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
+#pragma unroll
+        for (int kb = 1; kb < 4; ++kb)
+          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+        mt[qb] = group4_max(mx) * c2;
+        raise |= mt[qb] > m[qb] + 8.f;
+      }
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float mn = mt[qb] > m[qb] + 8.f ? fmaxf(m[qb], mt[qb]) : m[qb];
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+          m[qb] = mn;
+#pragma unroll
+          for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
+          acc_l[qb] *= alpha;
+        }
+      }
+      Frag<bf16_t> pf[NQB][2];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float nm = -m[qb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[qb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], c2, nm));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pf[qb][c].set_pair(0, s[qb][2 * c][0], s[qb][2 * c][1]);
+          pf[qb][c].set_pair(1, s[qb][2 * c][2], s[qb][2 * c][3]);
+          pf[qb][c].set_pair(2, s[qb][2 * c + 1][0], s[qb][2 * c + 1][1]);
+          pf[qb][c].set_pair(3, s[qb][2 * c + 1][2], s[qb][2 * c + 1][3]);
+          mma(acc_l[qb], ones, pf[qb][c]);
+        }
+      }
+      // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4
+      const int trow = 4 * g + (l16 >> 2);   // source row within a 16-key half
+      const int tcol = 4 * (l16 & 3);        // source column within a 16-dim block
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<bf16_t> vf;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * c + 16 * hh + trow, dcol = 16 * jd + tcol;
+            const bf16_t* src = &Vs[swz<D>(row, dcol >> 3) + (dcol & 7)];
+            s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+            uint2 u = __builtin_bit_cast(uint2, t);
+            vf.w[2 * hh] = u.x;
+            vf.w[2 * hh + 1] = u.y;
+          }
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) mma(acc_o[qb][jd], vf, pf[qb][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = acc_l[qb][0];  // every row of the ones product holds the sum
+      inv_l[qb] = lt > 0.f ? 1.f / lt : 0.f;
+      if (a.lse && g == 0 && qvalid[qb])
+        a.lse[(size_t)bh * a.N_pad + qrow[qb]] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    f32x4 acc_n[NDB];
+    float inv_den = 0.f;
+    if constexpr (LINEAR) readout<bf16_t, D, R>(a, bh, qf[qb], qrow[qb], qvalid[qb], lane, acc_n, inv_den);
+    bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + base + (size_t)qrow[qb] * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float r4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.f;
+        if constexpr (SPARSE) x += acc_o[qb][jd][i] * inv_l[qb];
+        if constexpr (LINEAR) x += acc_n[jd][i] * inv_den;
+        r4[i] = qvalid[qb] ? x : 0.f;
+      }
+      st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+    }
+  }
+}
+
+// LDS stages of the bf16 kernel: 1 (four blocks per CU, two waves per SIMD)
+// by default; HSA_ATTN_NSTAGE=2 selects double buffering (two blocks per CU).
+static inline int attend_nstage() {
+  static const int ns = [] {
+    const char* e = getenv("HSA_ATTN_NSTAGE");
+    return (e && e[0] == '2') ? 2 : 1;
+  }();
+  return ns;
+}
+
+template <int D, int R, int NS>
+static hipError_t attend_launch_bf16(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  if (sparse && linear) k_attend_bf16<D, R, true, true, NS><<<grid, 128, 0, st>>>(a);
+  else if (sparse) k_attend_bf16<D, R, true, false, NS><<<grid, 128, 0, st>>>(a);
+  else k_attend_bf16<D, R, false, true, NS><<<grid, 128, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, int R>
+static hipError_t attend_dispatch_bf16(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
+  return attend_nstage() == 2 ? attend_launch_bf16<D, R, 2>(a, sparse, linear, st)
+                              : attend_launch_bf16<D, R, 1>(a, sparse, linear, st);
+}
+
+static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& a, bool sparse, bool linear,
+                                              hipStream_t st) {
+  if (!linear) return s.d == 64 ? attend_dispatch_bf16<64, 16>(a, sparse, linear, st)
+                                : attend_dispatch_bf16<128, 16>(a, sparse, linear, st);
+  if (s.d == 64) {
+    if (s.rank == 16) return attend_dispatch_bf16<64, 16>(a, sparse, linear, st);
+    if (s.rank == 32) return attend_dispatch_bf16<64, 32>(a, sparse, linear, st);
+    return attend_dispatch_bf16<64, 64>(a, sparse, linear, st);
+  }
+  if (s.rank == 16) return attend_dispatch_bf16<128, 16>(a, sparse, linear, st);
+  if (s.rank == 32) return attend_dispatch_bf16<128, 32>(a, sparse, linear, st);
+  return attend_dispatch_bf16<128, 64>(a, sparse, linear, st);
+}
+
 // Launch helpers shared by the bf16/fp8 translation unit and the float32 one.
 template <typename T, int D, int R>
 static hipError_t attend_dispatch(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
-  const long grid = 8 * ((a.nrows + 7) / 8);
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
   if (sparse && linear) k_attend<T, D, R, true, true><<<grid, 256, 0, st>>>(a);
   else if (sparse) k_attend<T, D, R, true, false><<<grid, 256, 0, st>>>(a);
   else k_attend<T, D, R, false, true><<<grid, 256, 0, st>>>(a);

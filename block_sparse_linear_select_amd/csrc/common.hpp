@@ -30,8 +30,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair with the hardware round-to-nearest-even
+// conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // OCP E4M3FN code -> float (bias 7, subnormals at exponent 0; NaN codes do
@@ -145,13 +150,18 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-// XCD-aware block order: consecutive logical blocks land on the same XCD
-// (hardware hands block i to XCD i % 8), so neighbouring query tiles of one
-// head share that XCD's L2.  Returns -1 for the padding blocks.
-__device__ __forceinline__ long xcd_remap(long i, long n_logical) {
-  long per = (n_logical + 7) / 8;
-  long l = (i % 8) * per + i / 8;
-  return l < n_logical ? l : -1;
+// Block order of the query-tile kernels.  The hardware hands block i to XCD
+// i % 8.  All eight XCDs work on the same head at a time, so the key/value
+// tiles in use stay within one or two heads (~40 MB at 720P) and remain
+// resident in the 256 MB MALL; inside a head, XCD x takes the contiguous x-th
+// eighth of the query tiles, so neighbouring query tiles, which keep many of
+// the same key tiles, share that XCD's L2.  Grid: 8 * heads * ceil(T / 8)
+// blocks; returns the (b*H + h) * T + a row, or -1 for padding blocks.
+__device__ __forceinline__ long head_interleaved_row(long i, int T) {
+  const long per = (T + 7) / 8;
+  const long xcd = i % 8, j = i / 8;
+  const long head = j / per, a = xcd * per + j % per;
+  return a < T ? head * T + a : -1;
 }
 
 }  // namespace hsa

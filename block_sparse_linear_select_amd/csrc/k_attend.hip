@@ -20,7 +20,7 @@ hipError_t launch_attend(const Shape& s, const void* q, const void* k, const voi
   a.nrows = (long)s.B * s.H * s.T;
   switch (s.dt) {
     case Dt::F32: return launch_attend_f32(s, a, sparse, linear, st);
-    case Dt::BF16: return attend_by_shape<bf16_t>(s, a, sparse, linear, st);
+    case Dt::BF16: return attend_bf16_by_shape(s, a, sparse, linear, st);
     default: return hipErrorNotSupported;
   }
 }

@@ -323,9 +323,10 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 }
 
 // ------------------------------------------------------------- finalize
-// Per (b, h): S = sum of the partial states (fixed order), S' = S W_o, and the
-// readout operands: S'^T as A fragments (float, or bf16 hi + lo), z, and
-// U_q^T as A fragments.
+// Per (b, h) and slice of 8 rank rows: S = sum of the partial states (fixed
+// order), S' = S W_o, written as readout A fragments (float, or bf16 hi + lo);
+// the first slice also writes z and zero-fills the fragment slots past r, and
+// the first slice of each head of batch 0 writes U_q^T as A fragments.
 struct FinalArgs {
   int nchunk, H, B;
   const float* part_s;
@@ -337,74 +338,84 @@ struct FinalArgs {
   void* uq_frag;
 };
 
+constexpr int kFinRows = 8;  // rank rows per finalize block
+
+template <typename OT>
+__device__ __forceinline__ float ld_param(const OT* p, size_t i) {
+  if constexpr (sizeof(OT) == 4) return reinterpret_cast<const float*>(p)[i];
+  else return bf16_bits_to_f32(reinterpret_cast<const bf16_t*>(p)[i].bits);
+}
+
+template <typename OT, int D, int R>
+__device__ __forceinline__ void put_sp(void* frag, size_t bh, int rr, int e, float x) {
+  constexpr int NRC = (R + 31) / 32;
+  constexpr int NFE = (D / 16) * NRC * 512;
+  const int rc = rr >> 5, rem = rr & 31;
+  const int s = 4 * (rem >> 4) + (rem & 3), g = (rem >> 2) & 3;
+  const int lane = (e & 15) + 16 * g, db = e >> 4;
+  const size_t idx = ((size_t)(db * NRC + rc) * 64 + lane) * 8 + s;
+  if constexpr (sizeof(OT) == 4) {
+    reinterpret_cast<float*>(frag)[bh * NFE + idx] = x;
+  } else {
+    uint16_t hi = (uint16_t)f32_to_bf16_bits(x);
+    uint16_t lo = (uint16_t)f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+    uint16_t* out = reinterpret_cast<uint16_t*>(frag) + bh * 2 * NFE;
+    out[idx] = hi;
+    out[NFE + idx] = lo;
+  }
+}
+
 template <typename OT, int D, int R>
 __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
-  constexpr int NRC = (R + 31) / 32;
-  constexpr int NDB = D / 16;
   constexpr int NRB = R / 16;
-  __shared__ float S[R * D];
-  __shared__ float Sp[R * D];
+  constexpr int NRC = (R + 31) / 32;
+  __shared__ float S[kFinRows * D];
   const int tid = threadIdx.x, bh = blockIdx.x, h = bh % a.H;
-  const float* ps = a.part_s + (size_t)bh * a.nchunk * R * D;
-  for (int e = tid; e < R * D; e += 256) {
+  const int r0 = blockIdx.y * kFinRows;
+  const float* ps = a.part_s + (size_t)bh * a.nchunk * R * D + (size_t)r0 * D;
+  for (int e = tid; e < kFinRows * D; e += 256) {
     float s = 0.f;
     for (int c = 0; c < a.nchunk; ++c) s += ps[(size_t)c * R * D + e];
     S[e] = s;
   }
-  if (tid < R) {
+  if (blockIdx.y == 0 && tid < R) {
     float s = 0.f;
     for (int c = 0; c < a.nchunk; ++c) s += a.part_z[((size_t)bh * a.nchunk + c) * R + tid];
     a.z[(size_t)bh * R + tid] = s;
   }
   __syncthreads();
   const OT* W = reinterpret_cast<const OT*>(a.wo) + (size_t)h * D * D;
-  for (int e = tid; e < R * D; e += 256) {
-    int rr = e / D, col = e % D;
-    float s = 0.f;
-    for (int d = 0; d < D; ++d) {
-      float wv;
-      if constexpr (sizeof(OT) == 4) wv = reinterpret_cast<const float*>(W)[(size_t)d * D + col];
-      else wv = bf16_bits_to_f32(reinterpret_cast<const bf16_t*>(W)[(size_t)d * D + col].bits);
-      s = fmaf(S[rr * D + d], wv, s);
-    }
-    Sp[e] = s;
+  constexpr int PER = kFinRows * D / 256;  // outputs per thread
+  const int col = tid % D;
+  const int rbase = tid / D;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int d = 0; d < D; ++d) {
+    const float wv = ld_param(W, (size_t)d * D + col);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = fmaf(S[(rbase + j * (256 / D)) * D + d], wv, acc[j]);
   }
-  __syncthreads();
-  // S'^T fragments: frag (db, rc), lane l, slot s -> S'[r][e] with
-  // e = 16 db + l%16, r = 32 rc + 16 (s/4) + 4 (l/16) + s%4 (zero past R).
-  const int nfe = NDB * NRC * 64 * 8;
-  for (int idx = tid; idx < nfe; idx += 256) {
-    int s = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
-    int rc = fr % NRC, db = fr / NRC;
-    int e = 16 * db + (l & 15);
-    int rr = 32 * rc + 16 * (s >> 2) + 4 * (l >> 4) + (s & 3);
-    float x = rr < R ? Sp[rr * D + e] : 0.f;
-    if constexpr (sizeof(OT) == 4) {
-      reinterpret_cast<float*>(a.sp_frag)[(size_t)bh * nfe + idx] = x;
-    } else {
-      uint16_t hi = (uint16_t)f32_to_bf16_bits(x);
-      float rem = x - bf16_bits_to_f32(hi);
-      uint16_t lo = (uint16_t)f32_to_bf16_bits(rem);
-      uint16_t* out = reinterpret_cast<uint16_t*>(a.sp_frag) + (size_t)bh * 2 * nfe;
-      out[idx] = hi;
-      out[nfe + idx] = lo;
-    }
-  }
-  // U_q^T fragments: frag (rb, c), lane l, slot s -> U_q[d][r] with
-  // r = 16 rb + l%16, d = 32 c + 8 (l/16) + s.  Written by the b = 0 blocks.
-  if (bh < a.H) {
-    const int nue = NRB * (D / 32) * 64 * 8;
-    const OT* U = reinterpret_cast<const OT*>(a.uq) + (size_t)h * D * R;
-    OT* out = reinterpret_cast<OT*>(a.uq_frag) + (size_t)h * nue;
-    for (int idx = tid; idx < nue; idx += 256) {
-      int s = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
-      int c = fr % (D / 32), rbk = fr / (D / 32);
-      int rr = 16 * rbk + (l & 15), d = 32 * c + 8 * (l >> 4) + s;
-      out[idx] = U[(size_t)d * R + rr];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) put_sp<OT, D, R>(a.sp_frag, bh, r0 + rbase + j * (256 / D), col, acc[j]);
+  if (blockIdx.y == 0) {
+    // fragment slots of rank rows R .. 32*NRC-1 (rank 16 only) stay zero
+    for (int e = tid; e < (32 * NRC - R) * D; e += 256) put_sp<OT, D, R>(a.sp_frag, bh, R + e / D, e % D, 0.f);
+    // U_q^T fragments: frag (rb, c), lane l, slot s -> U_q[d][r] with
+    // r = 16 rb + l%16, d = 32 c + 8 (l/16) + s.
+    if (bh < a.H) {
+      const int nue = NRB * (D / 32) * 64 * 8;
+      const OT* U = reinterpret_cast<const OT*>(a.uq) + (size_t)h * D * R;
+      OT* out = reinterpret_cast<OT*>(a.uq_frag) + (size_t)h * nue;
+      for (int idx = tid; idx < nue; idx += 256) {
+        int s2 = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
+        int c = fr % (D / 32), rbk = fr / (D / 32);
+        int rr = 16 * rbk + (l & 15), d = 32 * c + 8 * (l >> 4) + s2;
+        out[idx] = U[(size_t)d * R + rr];
+      }
     }
   }
 }
-
 
 // Launch helpers shared by the bf16/fp8 translation unit and the float32 one.
 template <typename T, typename OT, int D, int R>
@@ -434,7 +445,7 @@ static hipError_t stream_by_shape(const Shape& s, const StreamArgs& a, bool pool
 
 template <typename OT, int D, int R>
 static hipError_t finalize_dispatch(const Shape& s, const FinalArgs& a, hipStream_t st) {
-  k_finalize<OT, D, R><<<s.B * s.H, 256, 0, st>>>(a);
+  k_finalize<OT, D, R><<<dim3(s.B * s.H, R / kFinRows), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

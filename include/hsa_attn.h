@@ -97,7 +97,7 @@ typedef struct hsa_attn_desc {
   int32_t topk;             /* tiles kept per row, 1 <= topk <= T */
   int32_t force_diag;       /* 0 or 1: also keep tile a in row a (union) */
   int32_t rank;             /* r: 16, 32 or 64 (multiple of 16) */
-  float softmax_scale;      /* usually 1/sqrt(d) */
+  float softmax_scale;      /* > 0, usually 1/sqrt(d) */
   float rope_base;          /* usually 10000 */
   int32_t in_dtype;         /* HSA_ATTN_F32 | HSA_ATTN_BF16 | HSA_ATTN_FP8_E4M3 */
   int32_t out_dtype;        /* F32 with F32 inputs; BF16 with BF16 or FP8 inputs */

@@ -15,6 +15,9 @@ LIB = os.path.join(PKG, "libhsa_attn.so")
 SOURCES = ["k_stream.hip", "k_stream_f32.hip", "k_select.hip", "k_attend.hip", "k_attend_f32.hip", "api.cpp"]
 # per-file optimisation level (hipcc -O3 crashes on the float32 instantiations)
 OPT = {"k_stream_f32.hip": "-O1", "k_attend_f32.hip": "-O1"}
+# extra flags per file: the attend kernels never see NaNs, so max/min need no
+# signalling-NaN quieting (infinities are still honoured)
+EXTRA = {"k_attend.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 ARCH = "gfx950"
 
 COMMON = [
@@ -35,7 +38,7 @@ def _hipcc():
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), OPT.get(src, "-O3"), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), OPT.get(src, "-O3"), *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -162,9 +162,9 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   constexpr int STAGE = SPARSE ? (64 * KSTR + D * VSTR) : 1;
   __shared__ __align__(16) T lds[2 * STAGE];
 
-  const long L = head_interleaved_row(blockIdx.x, a.T);
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
-  const int bh = (int)(L / a.T), qa = (int)(L % a.T);
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
@@ -314,9 +314,8 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 // bf16 query-tile kernel.  One block = one (b, h, query tile) = 2 waves of 32
 // queries; each wave keeps its queries as two 16-column B-fragment sets, so
 // every K or V fragment read from LDS feeds two matrix-core steps.
-// K and V tiles sit in LDS row-major, in 16-byte granules XOR-swizzled by row
-// (granule c of row r at c ^ (r mod G)), which keeps both the 16-byte K reads
-// and the transposing V reads free of bank conflicts.  V fragments come
+// K and V tiles sit in LDS row-major with padded rows, which keeps both the
+// 16-byte K reads and the transposing V reads free of bank conflicts.  V fragments come
 // straight from the row-major tile through ds_read_b64_tr_b16: within each
 // 16-lane group, output lane i, element t is element (i mod 4) of the 8 bytes
 // addressed by source lane 4t + i/4.  NSTAGE = 1 or 2 LDS tile buffers.
@@ -325,10 +324,14 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, bounds-checked (gfx9-family dword 3)
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
+// LDS row stride of a staged K or V tile: D + 8 elements (16 bytes of
+// padding), so rows start 4 banks apart.  Sixteen rows then cover every bank
+// exactly once for a 16-byte read and twice (the minimum for 512 bytes) for
+// a transposing 8-byte read, and each fragment address is a per-lane base
+// plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ int swz(int row, int granule) {
-  constexpr int G = D / 8;
-  return row * D + ((granule ^ (row & (G - 1))) << 3);
+__device__ __forceinline__ int lds_at(int row, int col) {
+  return row * (D + 8) + col;
 }
 
 template <int D, int R, bool SPARSE, bool LINEAR, int NSTAGE>
@@ -337,12 +340,12 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
   constexpr int NQB = 2;              // 16-query blocks per wave
   constexpr int NDB = D / 16;
   constexpr int NGT = 64 * G / 128;   // granules per thread per tile
-  constexpr int TILE = 64 * D;        // elements per K (or V) tile
+  constexpr int TILE = 64 * (D + 8);  // elements per staged K (or V) tile
   __shared__ __align__(16) bf16_t lds[SPARSE ? NSTAGE * 2 * TILE : 8];
 
-  const long L = head_interleaved_row(blockIdx.x, a.T);
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
-  const int bh = (int)(L / a.T), qa = (int)(L % a.T);
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
@@ -408,8 +411,8 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
 #pragma unroll
       for (int i = 0; i < NGT; ++i) {
         const int q = tid + 128 * i, row = q / G, gr = q % G;
-        *reinterpret_cast<u32x4*>(&Ks[swz<D>(row, gr)]) = kr[i];
-        *reinterpret_cast<u32x4*>(&Vs[swz<D>(row, gr)]) = vr[i];
+        *reinterpret_cast<u32x4*>(&Ks[lds_at<D>(row, 8 * gr)]) = kr[i];
+        *reinterpret_cast<u32x4*>(&Vs[lds_at<D>(row, 8 * gr)]) = vr[i];
       }
       __syncthreads();
       if (j + 1 < end) load_tile(a.col_idx[j + 1]);
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
           Frag<bf16_t> kf;
-          kf.w = *reinterpret_cast<const u32x4*>(&Ks[swz<D>(16 * kb + l16, 4 * c + g)]);
+          kf.w = *reinterpret_cast<const u32x4*>(&Ks[lds_at<D>(16 * kb + l16, 32 * c + 8 * g)]);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf, qf[qb][c]);
         }
@@ -439,7 +442,9 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
             for (int i = 0; i < 4; ++i)
               if (16 * kb + 4 * g + i >= kvalid) s[qb][kb][i] = -INFINITY;
       }
-      float mt[NQB];
+      // The common path needs no cross-lane work: if no lane's own keys exceed
+      // the running max by more than 8, every exp2 argument is <= 8.
+      float mloc[NQB];
       bool raise = false;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
@@ -447,13 +452,14 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
 #pragma unroll
         for (int kb = 1; kb < 4; ++kb)
           mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-        mt[qb] = group4_max(mx) * c2;
-        raise |= mt[qb] > m[qb] + 8.f;
+        mloc[qb] = mx * c2;
+        raise |= mloc[qb] > m[qb] + 8.f;
       }
       if (__ballot(raise)) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const float mn = mt[qb] > m[qb] + 8.f ? fmaxf(m[qb], mt[qb]) : m[qb];
+          const float mt = group4_max(mloc[qb]);  // the row max, the same in all four lane groups
+          const float mn = mt > m[qb] + 8.f ? fmaxf(m[qb], mt) : m[qb];
           const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
           m[qb] = mn;
 #pragma unroll
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int row = 32 * c + 16 * hh + trow, dcol = 16 * jd + tcol;
-            const bf16_t* src = &Vs[swz<D>(row, dcol >> 3) + (dcol & 7)];
+            const bf16_t* src = &Vs[lds_at<D>(row, dcol)];
             s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
             uint2 u = __builtin_bit_cast(uint2, t);
             vf.w[2 * hh] = u.x;

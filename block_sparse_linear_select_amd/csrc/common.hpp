@@ -157,11 +157,15 @@ __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __ex
 // eighth of the query tiles, so neighbouring query tiles, which keep many of
 // the same key tiles, share that XCD's L2.  Grid: 8 * heads * ceil(T / 8)
 // blocks; returns the (b*H + h) * T + a row, or -1 for padding blocks.
-__device__ __forceinline__ long head_interleaved_row(long i, int T) {
-  const long per = (T + 7) / 8;
-  const long xcd = i % 8, j = i / 8;
-  const long head = j / per, a = xcd * per + j % per;
+__device__ __forceinline__ int head_interleaved_row(int i, int T) {
+  const int per = (T + 7) / 8;
+  const int xcd = i & 7, j = i >> 3;
+  const int head = j / per, a = xcd * per + j % per;
   return a < T ? head * T + a : -1;
 }
+
+// Marks a value as wave-uniform (kept in a scalar register), so that buffer
+// descriptors and addresses derived from it need no per-lane handling.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace hsa

@@ -24,7 +24,7 @@ ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_hybrid_attn"]
-KERNEL_KINDS = ["rope", "stream", "finalize", "select", "attend"]
+KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend"]
 
 
 class Desc(ctypes.Structure):

@@ -256,7 +256,9 @@ HSA_API int hsa_block_select(const hsa_attn_desc* desc, const void* q, const voi
                               kbar_out, st);
   });
   if (e != hipSuccess) return hip_fail(e, "tile pooling");
-  e = timed(HSA_ATTN_KERNEL_SELECT, st, [&] { return launch_select(s, w, row_ptr, col_idx, st); });
+  e = timed(HSA_ATTN_KERNEL_SCORES, st, [&] { return launch_scores(s, w, st); });
+  if (e != hipSuccess) return hip_fail(e, "pooled scores");
+  e = timed(HSA_ATTN_KERNEL_TOPK, st, [&] { return launch_topk(s, w, row_ptr, col_idx, st); });
   if (e != hipSuccess) return hip_fail(e, "tile selection");
   return HSA_ATTN_OK;
 }
@@ -350,7 +352,9 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if (!given) {
     int32_t* rpo = internal ? w.row_ptr : row_ptr_out;
     int32_t* cio = internal ? w.col_idx : col_idx_out;
-    hipError_t e = timed(HSA_ATTN_KERNEL_SELECT, st, [&] { return launch_select(s, w, rpo, cio, st); });
+    hipError_t e = timed(HSA_ATTN_KERNEL_SCORES, st, [&] { return launch_scores(s, w, st); });
+    if (e != hipSuccess) return hip_fail(e, "pooled scores");
+    e = timed(HSA_ATTN_KERNEL_TOPK, st, [&] { return launch_topk(s, w, rpo, cio, st); });
     if (e != hipSuccess) return hip_fail(e, "tile selection");
     rp = rpo;
     ci = cio;

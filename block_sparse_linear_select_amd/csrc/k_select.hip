@@ -13,39 +13,72 @@ namespace hsa {
 
 // -------------------------------------------------------------- scores
 // sigma[a][b] = qbar_a . kbar_b for one (b, h), float64 16x16x4 matrix-core
-// steps.  Block: 4 waves, one 16-row block of a; each wave walks the 16-column
-// blocks w, w+4, ...  Means are stored transposed ([d][T]) so that a lane
-// group reads 16 consecutive tiles.
+// steps.  Block: 4 waves x 16 rows = 64 rows of a; the column means are
+// staged 32 columns at a time through double-buffered LDS (row stride 40
+// doubles, which puts the four lane groups of a read on distinct banks), and
+// each wave runs two independent accumulator chains.  Means are stored
+// transposed ([d][T]) so both the A operands and the staging loads read
+// consecutive tiles.
+constexpr int kScoreCols = 32;
+constexpr int kScoreStride = 40;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict__ qbarT,
                                                 const double* __restrict__ kbarT, double* __restrict__ scores) {
-  const int bh = blockIdx.y, rb = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ double kbuf[2][D * kScoreStride];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const double* qb = qbarT + (size_t)bh * D * T;
   const double* kb = kbarT + (size_t)bh * D * T;
   double* out = scores + (size_t)bh * T * T;
-  const int row = 16 * rb + l16;
+  const int rbase = 64 * blockIdx.x + 16 * w;
+  const int row = rbase + l16;
   double af[D / 4];
 #pragma unroll
   for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)(4 * s + g) * T + row] : 0.0;
-  const int ncb = (T + 15) / 16;
-  for (int cb = w; cb < ncb; cb += 4) {
-    const int col = 16 * cb + l16;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+
+  const int nchunks = (T + kScoreCols - 1) / kScoreCols;
+  // each thread stages PER doubles of a chunk: column tid % 32, dims tid / 32 + 8 i
+  constexpr int PER = D * kScoreCols / 256;
+  const int cl = tid % kScoreCols, d0 = tid / kScoreCols;
+  double pre[PER];
+  auto fetch = [&](int cc) {
+    const int col = cc * kScoreCols + cl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pre[i] = col < T ? kb[(size_t)(d0 + 8 * i) * T + col] : 0.0;
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kbuf[buf][(d0 + 8 * i) * kScoreStride + cl] = pre[i];
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int buf = cc & 1;
+    if (cc + 1 < nchunks) fetch(cc + 1);  // in flight while this chunk is multiplied
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+    const double* kt = kbuf[buf];
 #pragma unroll
     for (int s = 0; s < D / 4; ++s) {
-      double bf = col < T ? kb[(size_t)(4 * s + g) * T + col] : 0.0;
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], bf, acc, 0, 0, 0);
+      const double b0 = kt[(4 * s + g) * kScoreStride + l16];
+      const double b1 = kt[(4 * s + g) * kScoreStride + 16 + l16];
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b1, acc1, 0, 0, 0);
     }
-    if (col < T) {
-      // float64 16x16x4 accumulator: register i of lane group g holds row 4i + g
+    // float64 16x16x4 accumulator: register i of lane group g holds row 4i + g
+    const int c0 = cc * kScoreCols + l16, c1 = c0 + 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int rr = 16 * rb + 4 * i + g;
-        if (rr < T) out[(size_t)rr * T + col] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      const int rr = rbase + 4 * i + g;
+      if (rr < T) {
+        if (c0 < T) out[(size_t)rr * T + c0] = acc0[i];
+        if (c1 < T) out[(size_t)rr * T + c1] = acc1[i];
       }
     }
+    if (cc + 1 < nchunks) put(buf ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
   }
 }
 
@@ -84,7 +117,40 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   uint64_t prefix = 0, mask = 0;
   int need = topk;
   uint32_t* hw = hist[w];
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  // First pass (sign and top exponent bits): the scores of a row fall into a
+  // handful of these digits, so LDS atomics would serialise.  Walk the present
+  // digits from the top instead, counting each with ballots, and stop at the
+  // digit that holds the k-th key.
+  {
+    uint32_t pend = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j)
+      if (j < nj && key[j] != 0ull) pend |= 1u << j;
+    int cum = 0, digit = 0;
+    for (;;) {
+      int dl = -1;
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j)
+        if ((pend >> j) & 1u) dl = max(dl, (int)(key[j] >> 56));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) dl = max(dl, __shfl_xor(dl, off, 64));
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        if (j < nj) {
+          const bool hit = ((pend >> j) & 1u) && (int)(key[j] >> 56) == dl;
+          cnt += __popcll(__ballot(hit));
+          if (hit) pend &= ~(1u << j);
+        }
+      }
+      if (cum + cnt >= need || dl < 0) { digit = dl < 0 ? 0 : dl; break; }
+      cum += cnt;
+    }
+    need -= cum;
+    prefix = (uint64_t)digit << 56;
+    mask = 255ull << 56;
+  }
+  for (int shift = 48; shift >= 0; shift -= 8) {
     for (int i = lane; i < 256; i += 64) hw[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -130,13 +196,14 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
-    if (j >= nj) break;
-    bool above = key[j] > kth;
-    bool eq = key[j] == kth && key[j] != 0ull;
-    uint64_t be = __ballot(eq);
-    int before = __popcll(be & lt_mask);
-    if (above || (eq && taken + before < need)) sel |= 1u << j;
-    taken += __popcll(be);
+    if (j < nj) {  // nj is wave-uniform; a guard instead of a break keeps key[] in registers
+      const bool above = key[j] > kth;
+      const bool eq = key[j] == kth && key[j] != 0ull;
+      const uint64_t be = __ballot(eq);
+      const int before = __popcll(be & lt_mask);
+      if (above || (eq && taken + before < need)) sel |= 1u << j;
+      taken += __popcll(be);
+    }
   }
   if (force_diag && lane == (a & 63)) sel |= 1u << (a >> 6);
 
@@ -145,11 +212,12 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   const size_t obase = direct ? (size_t)row * topk : (size_t)row * (topk + 1);
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) {
-    if (j >= nj) break;
-    bool s = (sel >> j) & 1u;
-    uint64_t bs = __ballot(s);
-    if (s && live) out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
-    base_pos += __popcll(bs);
+    if (j < nj) {
+      const bool s = (sel >> j) & 1u;
+      const uint64_t bs = __ballot(s);
+      if (s && live) out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
+      base_pos += __popcll(bs);
+    }
   }
   if (live && lane == 0) {
     if (direct) {
@@ -194,14 +262,16 @@ __global__ void k_compact(int rows, int stride, const int32_t* __restrict__ tmp,
   for (int i = 0; i < n; ++i) col_idx[o + i] = tmp[(size_t)row * stride + i];
 }
 
-hipError_t launch_select(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
-  const int bh = s.B * s.H;
-  dim3 g1((s.T + 15) / 16, bh);
+hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st) {
+  dim3 g1((s.T + 63) / 64, s.B * s.H);
   if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
   else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rows = bh * s.T;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+  const int rows = s.B * s.H * s.T;
+  hipError_t e;
   const int direct = s.force_diag ? 0 : 1;
   k_topk<<<(rows + 3) / 4, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores,
                                          direct ? col_idx : w.sel_tmp, w.sel_cnt, row_ptr);

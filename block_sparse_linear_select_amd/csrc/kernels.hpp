@@ -71,7 +71,8 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
                               const void* uk, bool pool, bool state, const Scratch& w,
                               double* qbar_out, double* kbar_out, hipStream_t st);
 hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const Scratch& w, hipStream_t st);
-hipError_t launch_select(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
+hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st);
+hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const float* qs, const float* ks, const float* vs,
                          const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,

@@ -125,9 +125,10 @@ enum {
   HSA_ATTN_KERNEL_ROPE = 0,      /* RoPE cos/sin table */
   HSA_ATTN_KERNEL_STREAM = 1,    /* tile pooling + linear key/value state pass */
   HSA_ATTN_KERNEL_FINALIZE = 2,  /* state reduction, S W_o, readout operands */
-  HSA_ATTN_KERNEL_SELECT = 3,    /* pooled scores, top-k, CSR */
-  HSA_ATTN_KERNEL_ATTEND = 4,    /* block-sparse flash attention + linear readout */
-  HSA_ATTN_KERNEL_KINDS = 5
+  HSA_ATTN_KERNEL_SCORES = 3,    /* pooled score grid */
+  HSA_ATTN_KERNEL_TOPK = 4,      /* per-row top-k and CSR emission */
+  HSA_ATTN_KERNEL_ATTEND = 5,    /* block-sparse flash attention + linear readout */
+  HSA_ATTN_KERNEL_KINDS = 6
 };
 int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);

@@ -201,10 +201,11 @@ def sparse_attn(cfg: Config, q, k, v, row_ptr, col_idx, q_scale=None, k_scale=No
         raise ValueError("col_idx must be a 1-D int32 device tensor")
     o = torch.empty((cfg.B, cfg.H, cfg.N_pad, cfg.d), dtype=_out_dtype(cfg), device=q.device)
     lse = torch.empty((cfg.B, cfg.H, cfg.N_pad), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = _workspace(cfg, CALL_SPARSE, q.device)
     d = cfg.desc()
     _check(lib().hsa_sparse_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
                                  _ptr(v_scale), _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
-                                 None, 0, _stream()))
+                                 _ptr(ws), ws.numel(), _stream()))
     return (o, lse) if want_lse else o
 
 

@@ -27,9 +27,10 @@ static int fail(int code, const char* fmt, ...) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear) {
+Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt) {
   Plan p;
   p.select = select; p.csr_internal = csr_internal; p.linear = linear;
+  p.vt = vt && s.dt == Dt::FP8;  // the fp8 sparse kernel reads V pre-transposed
   const size_t bh = (size_t)s.B * s.H, rows = bh * s.T;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
@@ -57,6 +58,7 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear) {
     p.off_uq = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
     p.off_rope = take((size_t)rope_entries(s) * sizeof(float2));
   }
+  if (p.vt) p.off_vt = take(bh * (size_t)s.N_pad * s.d * 2);
   p.total = off;
   return p;
 }
@@ -83,6 +85,7 @@ Scratch bind_plan(const Plan& p, void* ws) {
     w.uq_frag = b + p.off_uq;
     w.rope = reinterpret_cast<float2*>(b + p.off_rope);
   }
+  if (p.vt) w.vt = b + p.off_vt;
   return w;
 }
 
@@ -234,7 +237,8 @@ HSA_API int hsa_attn_workspace_size(const hsa_attn_desc* desc, int call, size_t*
   int rc = check_desc(desc, s, lin, sel);
   if (rc) return rc;
   // the hybrid figure covers its largest variant (selection + internal CSR)
-  *bytes = make_plan(s, sel, call == HSA_ATTN_CALL_HYBRID, lin).total;
+  const bool sparse = call == HSA_ATTN_CALL_SPARSE || call == HSA_ATTN_CALL_HYBRID;
+  *bytes = make_plan(s, sel, call == HSA_ATTN_CALL_HYBRID, lin, sparse).total;
   return HSA_ATTN_OK;
 }
 
@@ -247,7 +251,7 @@ HSA_API int hsa_block_select(const hsa_attn_desc* desc, const void* q, const voi
   if (rc) return rc;
   if (!q || !k || !row_ptr || !col_idx) return fail(HSA_ATTN_ERR_NULL, "q, k, row_ptr and col_idx are required");
   if ((rc = check_scales(s, q_scale, k_scale, nullptr, 2))) return rc;
-  Plan p = make_plan(s, true, false, false);
+  Plan p = make_plan(s, true, false, false, false);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -274,10 +278,16 @@ HSA_API int hsa_sparse_attn(const hsa_attn_desc* desc, const void* q, const void
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, row_ptr, col_idx and o_sparse are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
   if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 sparse attention is not built in this version");
-  (void)workspace; (void)workspace_bytes;
-  Scratch w;
+  Plan p = make_plan(s, false, false, false, true);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
+  hipError_t e = hipSuccess;
+  if (p.vt) {
+    e = timed(HSA_ATTN_KERNEL_STREAM, st, [&] { return launch_vtranspose(s, v, w, st); });
+    if (e != hipSuccess) return hip_fail(e, "V transpose");
+  }
+  e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
     return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, row_ptr, col_idx, true, false, w, o_sparse,
                          lse_out, st);
   });
@@ -311,7 +321,7 @@ HSA_API int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o and o_lin are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
   if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 linear attention is not built in this version");
-  Plan p = make_plan(s, false, false, true);
+  Plan p = make_plan(s, false, false, true, false);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -342,7 +352,7 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
   if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 hybrid attention is not built in this version");
   const bool internal = !given && !row_ptr_out;
-  Plan p = make_plan(s, !given, internal, true);
+  Plan p = make_plan(s, !given, internal, true, true);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);

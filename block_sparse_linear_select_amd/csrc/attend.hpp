@@ -33,6 +33,7 @@ struct AttendArgs {
   const float* z;
   const void* uq_frag;
   const float2* rope;
+  const void* vt;  // fp8 path: V tiles transposed ([BH][T][d][64], keys permuted)
   void* o;
   float* lse;
   long nrows;

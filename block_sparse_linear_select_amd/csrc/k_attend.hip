@@ -15,7 +15,7 @@ hipError_t launch_attend(const Shape& s, const void* q, const void* k, const voi
   a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
   a.scale_log2 = s.scale * kLog2e;
   a.q = q; a.k = k; a.v = v; a.row_ptr = row_ptr; a.col_idx = col_idx;
-  a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag; a.rope = w.rope;
+  a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag; a.rope = w.rope; a.vt = w.vt;
   a.o = o; a.lse = lse;
   a.nrows = (long)s.B * s.H * s.T;
   switch (s.dt) {

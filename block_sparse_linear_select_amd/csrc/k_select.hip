@@ -114,8 +114,15 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
     key[j] = (j < nj && b < T && live) ? order_key(src[b]) : 0ull;
   }
 
+  // Radix select of the k-th largest key.  After each pass, `prefix` holds the
+  // bits fixed so far, `need` how many keys of that bucket are still needed.
+  // When a bucket holds exactly the keys still needed, every key >= prefix is
+  // kept and the search stops early (the usual case after two or three passes).
+  // Each wave works on its own row and its own LDS histogram, so the waves of
+  // a block never synchronise with each other.
   uint64_t prefix = 0, mask = 0;
   int need = topk;
+  bool done = false;
   uint32_t* hw = hist[w];
   // First pass (sign and top exponent bits): the scores of a row fall into a
   // handful of these digits, so LDS atomics would serialise.  Walk the present
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
 #pragma unroll
     for (int j = 0; j < kMaxJ; ++j)
       if (j < nj && key[j] != 0ull) pend |= 1u << j;
-    int cum = 0, digit = 0;
+    int cum = 0, digit = 0, dcnt = 0;
     for (;;) {
       int dl = -1;
 #pragma unroll
@@ -143,52 +150,61 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
           if (hit) pend &= ~(1u << j);
         }
       }
-      if (cum + cnt >= need || dl < 0) { digit = dl < 0 ? 0 : dl; break; }
+      if (cum + cnt >= need || dl < 0) { digit = dl < 0 ? 0 : dl; dcnt = cnt; break; }
       cum += cnt;
     }
     need -= cum;
     prefix = (uint64_t)digit << 56;
     mask = 255ull << 56;
+    done = dcnt == need;
   }
-  for (int shift = 48; shift >= 0; shift -= 8) {
+  for (int shift = 48; shift >= 0 && !done; shift -= 8) {
     for (int i = lane; i < 256; i += 64) hw[i] = 0;
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < kMaxJ; ++j)
       if (j < nj && (key[j] & mask) == prefix && key[j] != 0ull)
         atomicAdd(&hw[(key[j] >> shift) & 255u], 1u);
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
     // lane l owns digits 4l .. 4l+3; count from the top digit down
-    uint32_t h0 = hw[4 * lane], h1 = hw[4 * lane + 1], h2 = hw[4 * lane + 2], h3 = hw[4 * lane + 3];
-    uint32_t mine = h0 + h1 + h2 + h3;
+    const uint32_t h0 = hw[4 * lane], h1 = hw[4 * lane + 1], h2 = hw[4 * lane + 2], h3 = hw[4 * lane + 3];
+    const uint32_t mine = h0 + h1 + h2 + h3;
     // inclusive suffix sum over lanes (lanes above hold larger digits)
     uint32_t suf = mine;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      uint32_t o = __shfl_down(suf, off, 64);
+      const uint32_t o = __shfl_down(suf, off, 64);
       if (lane + off < 64) suf += o;
     }
-    uint32_t above = suf - mine;  // count in digits > 4l+3
-    int found = -1, rest = 0;
-    uint32_t hh[4] = {h0, h1, h2, h3};
-    uint32_t cum = above;
+    uint32_t cum = suf - mine;  // count in digits > 4l+3
+    int found = -1, rest = 0, fcnt = 0;
+    const uint32_t hh[4] = {h0, h1, h2, h3};
 #pragma unroll
     for (int dd = 3; dd >= 0; --dd) {
       if (found < 0 && cum < (uint32_t)need && cum + hh[dd] >= (uint32_t)need) {
         found = 4 * lane + dd;
         rest = need - (int)cum;
+        fcnt = (int)hh[dd];
       }
       cum += hh[dd];
     }
-    uint64_t bal = __ballot(found >= 0);
-    int src_lane = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
-    int digit = __shfl(found, src_lane, 64);
+    const uint64_t bal = __ballot(found >= 0);
+    const int src_lane = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
+    const int digit = __shfl(found, src_lane, 64);
     need = __shfl(rest, src_lane, 64);
+    const int bcnt = __shfl(fcnt, src_lane, 64);
     prefix |= ((uint64_t)(digit < 0 ? 0 : digit)) << shift;
     mask |= 255ull << shift;
-    __syncthreads();
+    done = bcnt == need;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
   }
-  const uint64_t kth = prefix;
+  // keep key > kth, plus the `need` lowest-index keys equal to kth; an early
+  // exit keeps every key >= prefix (kth = prefix - 1, no ties to break)
+  const uint64_t kth = done ? prefix - 1 : prefix;
+  if (done) need = 0;
 
   // selection flags: strictly above the threshold, then ties by lowest index
   uint32_t sel = 0;  // bit j: element j of this lane is kept

@@ -22,7 +22,7 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
   a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
   a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
   a.qbarT = w.qbarT; a.kbarT = w.kbarT; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
-  a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope;
+  a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope; a.vt = w.vt;
   switch (s.dt) {
     case Dt::F32: return launch_stream_f32(s, a, pool, state, st);
     case Dt::BF16: return stream_by_shape<bf16_t, bf16_t>(s, a, pool, state, st);
@@ -37,6 +37,15 @@ hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const
   a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag;
   if (s.dt == Dt::F32) return launch_finalize_f32(s, a, st);
   return finalize_by_shape<bf16_t>(s, a, st);
+}
+
+hipError_t launch_vtranspose(const Shape& s, const void* v, const Scratch& w, hipStream_t st) {
+  dim3 grid(s.T, s.B * s.H);
+  const bf16_t* vv = reinterpret_cast<const bf16_t*>(v);
+  bf16_t* out = reinterpret_cast<bf16_t*>(w.vt);
+  if (s.d == 64) k_vtranspose<64><<<grid, 256, 0, st>>>(s.N, s.N_pad, s.T, vv, out);
+  else k_vtranspose<128><<<grid, 256, 0, st>>>(s.N, s.N_pad, s.T, vv, out);
+  return hipGetLastError();
 }
 
 }  // namespace hsa

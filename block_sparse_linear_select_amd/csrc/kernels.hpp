@@ -49,6 +49,7 @@ struct Scratch {
   float* z = nullptr;          // [BH][r]
   void* uq_frag = nullptr;     // [H] U_q^T as readout fragments
   float2* rope = nullptr;      // RoPE table
+  void* vt = nullptr;          // [BH][T][d][64] V tiles transposed, keys permuted (bf16 sparse path)
 };
 
 // Workspace planning: byte offsets of each region for a given call.
@@ -56,11 +57,11 @@ struct Plan {
   size_t total = 0;
   size_t off_qbarT = 0, off_kbarT = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
-  size_t off_z = 0, off_uq = 0, off_rope = 0;
-  bool select = false, csr_internal = false, linear = false;
+  size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
+  bool select = false, csr_internal = false, linear = false, vt = false;
 };
 
-Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear);
+Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt);
 Scratch bind_plan(const Plan& p, void* ws);
 
 // Launchers: each enqueues its kernels on `st` and returns hipSuccess or the
@@ -70,6 +71,7 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
                               const float* qs, const float* ks, const float* vs,
                               const void* uk, bool pool, bool state, const Scratch& w,
                               double* qbar_out, double* kbar_out, hipStream_t st);
+hipError_t launch_vtranspose(const Shape& s, const void* v, const Scratch& w, hipStream_t st);
 hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const Scratch& w, hipStream_t st);
 hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st);
 hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);

@@ -121,6 +121,7 @@ struct StreamArgs {
   float* part_s;
   float* part_z;
   const float2* rope;
+  void* vt;  // optional: V tiles transposed, [BH][T][d][64] with keys permuted as in LDS
 };
 
 template <typename T, typename OT, int D, int R, bool POOL, bool STATE>
@@ -243,6 +244,17 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
     }
     __syncthreads();
     if (t + 1 < t1) load_tile(t + 1);
+    if constexpr (STATE && sizeof(T) == 1) {
+      // hand the transposed tile to the sparse kernel: D rows of 64 keys
+      if (a.vt) {
+        bf16_t* dst = reinterpret_cast<bf16_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64;
+        for (int q = tid; q < D * 8; q += 256) {
+          const int row = q >> 3, gr = q & 7;
+          *reinterpret_cast<u32x4*>(dst + row * 64 + gr * 8) =
+              *reinterpret_cast<const u32x4*>(&Vt[row * VSTR + gr * 8]);
+        }
+      }
+    }
 
     if constexpr (STATE) {
       const float sk = a.ks ? a.ks[(size_t)bh * a.T + t] : 1.f;
@@ -319,6 +331,40 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
     }
     float zt = group4_sum(zacc);
     if (dg == 0 && g == 0) a.part_z[pbase * R + r] = zt;
+  }
+}
+
+// ------------------------------------------------------------- V transpose
+// V tiles transposed for the sparse kernel when no streaming pass runs:
+// vt[bh][t][d][p] = V[bh][64 t + key(p)][d], keys permuted as vt_pos, rows
+// past N zero.  One block per (tile, b*H + h).
+template <int D>
+__global__ __launch_bounds__(256) void k_vtranspose(int N, int N_pad, int T, const bf16_t* __restrict__ v,
+                                                    bf16_t* __restrict__ vt) {
+  constexpr int VSTR = 64 + 8;
+  constexpr int NVU = 16 * (D / 8);
+  __shared__ __align__(16) bf16_t Vt[D * VSTR];
+  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const bf16_t* V = v + (size_t)bh * N_pad * D;
+  if (tid < NVU) {
+    const int kg = tid % 16, c8 = tid / 16;
+    Chunk8<bf16_t> c[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int gr = t * 64 + 4 * kg + ii;
+      if (gr < N) gload8(c[ii], V + (size_t)gr * D + c8 * 8);
+      else zero8(c[ii]);
+    }
+    const int p0 = vt_pos(4 * kg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(c[0], e), elem(c[1], e), elem(c[2], e), elem(c[3], e));
+  }
+  __syncthreads();
+  bf16_t* dst = vt + ((size_t)bh * T + t) * D * 64;
+  for (int q = tid; q < D * 8; q += 256) {
+    const int row = q >> 3, gr = q & 7;
+    *reinterpret_cast<u32x4*>(dst + row * 64 + gr * 8) = *reinterpret_cast<const u32x4*>(&Vt[row * VSTR + gr * 8]);
   }
 }
 

@@ -149,7 +149,9 @@ int hsa_block_select(const hsa_attn_desc* desc, const void* q, const void* k,
 
 /*
  * Block-sparse softmax branch on a given CSR: for each query tile, flash
- * attention over the kept key tiles with float32 softmax statistics.
+ * attention over the kept key tiles with float32 softmax statistics.  With
+ * FP8 inputs the workspace holds V transposed per tile (B*H*N_pad*d bytes);
+ * the other dtypes need none.
  *   o_sparse: [B, H, N_pad, d] in out_dtype (rows >= N zero).
  *   lse_out: optional float [B, H, N_pad] natural-log sum of exp(scale*q.k)
  *   over the kept valid keys (NULL to skip; rows >= N undefined).

@@ -66,7 +66,8 @@ def test_workspace_grows_with_the_problem():
         assert rc == 0
         sizes.append(n)
         rc2, n2 = _ws(cfg, B.CALL_SPARSE)
-        assert rc2 == 0 and n2 == 0  # the sparse branch needs no scratch
+        assert rc2 == 0 and n2 == 0  # bf16 sparse attention needs no scratch
+        assert _ws(_cfg(dtype="f32", grid=grid, N=cfg.N, N_pad=npad), B.CALL_SPARSE) == (0, 0)
         assert _ws(cfg, B.CALL_LINEAR)[1] < n
     assert sizes == sorted(sizes) and len(set(sizes)) == 3
 

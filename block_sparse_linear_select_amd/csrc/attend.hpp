@@ -60,13 +60,15 @@ __device__ __forceinline__ void lds_row(float* dst, const Chunk8<float>& c) {
   reinterpret_cast<float4*>(dst)[1] = c.b;
 }
 
-// Readout of the linear branch for the 16 queries of one fragment column:
-// phi_q = elu(q U_q) + 1, q' = rope(phi_q), O_lW = (q' S') / (phi_q . z).
-// qf holds the queries as B fragments; the result lands in the accumulator
-// layout of O^T (lane: query l%16, dims 16 jd + 4 (l/16) + i).
-template <typename T, int D, int R>
-__device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<T>* qf, int qrow, bool qvalid,
-                                        int lane, f32x4* acc_n, float& inv_den) {
+// Readout of the linear branch for NQ blocks of 16 queries (one fragment
+// column each): phi_q = elu(q U_q) + 1, q' = rope(phi_q),
+// O_lW = (q' S') / (phi_q . z).  Every U_q^T and S' fragment is fetched once
+// and used for all NQ blocks.  qf[b] holds block b's queries as B fragments;
+// results land in the accumulator layout of O^T (lane: query l%16, dims
+// 16 jd + 4 (l/16) + i).
+template <typename T, int D, int R, int NQ>
+__device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<T> (*qf)[D / 32], const int* qrow,
+                                        const bool* qvalid, int lane, f32x4 (*acc_n)[D / 16], float* inv_den) {
   constexpr int NDB = D / 16;
   constexpr int NRB = R / 16;
   constexpr int NRC = (R + 31) / 32;
@@ -74,76 +76,83 @@ __device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<
   const int h = bh % a.H;
   const T* UQ = reinterpret_cast<const T*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
   const float* Z = a.z + (size_t)bh * R;
-  f32x4 f[NRB];
+  f32x4 f[NQ][NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    f[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NQ; ++b) f[b][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       Frag<T> uf;
       load8(uf, UQ + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
-      mma(f[rb], uf, qf[c]);
+#pragma unroll
+      for (int b = 0; b < NQ; ++b) mma(f[b][rb], uf, qf[b][c]);
     }
-  }
-  // query position
-  int qpos[3];
-  {
-    int tok = qvalid ? qrow : 0, hw = a.gh * a.gw;
-    qpos[0] = tok / hw;
-    int rem = tok - qpos[0] * hw;
-    qpos[1] = rem / a.gw;
-    qpos[2] = rem - qpos[1] * a.gw;
   }
   const int ht = 3 * R / 16, hh = 3 * R / 16, hwp = R / 8;
-  float den = 0.f;
-  float qp[NRB][4];
+  Frag<T> qpf[NQ][NRC];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float phi = elu1(f[rb][i]);
-      f[rb][i] = phi;
-      den += phi * Z[16 * rb + 4 * g + i];
+  for (int b = 0; b < NQ; ++b) {
+    int qpos[3];
+    {
+      const int tok = qvalid[b] ? qrow[b] : 0, hw = a.gh * a.gw;
+      qpos[0] = tok / hw;
+      const int rem = tok - qpos[0] * hw;
+      qpos[1] = rem / a.gw;
+      qpos[2] = rem - qpos[1] * a.gw;
     }
+    float den = 0.f;
+    float qp[NRB][4];
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      int jp = (16 * rb + 4 * g) / 2 + pr;
-      int axis, m, half, off;
-      if (jp < ht) { axis = 0; m = jp; half = ht; off = 0; }
-      else if (jp < ht + hh) { axis = 1; m = jp - ht; half = hh; off = a.gt * ht; }
-      else { axis = 2; m = jp - ht - hh; half = hwp; off = a.gt * ht + a.gh * hh; }
-      float2 cs = a.rope[off + qpos[axis] * half + m];
-      float x0 = f[rb][2 * pr], x1 = f[rb][2 * pr + 1];
-      qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
-      qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float phi = elu1(f[b][rb][i]);
+        f[b][rb][i] = phi;
+        den += phi * Z[16 * rb + 4 * g + i];
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int jp = (16 * rb + 4 * g) / 2 + pr;
+        int axis, m, half, off;
+        if (jp < ht) { axis = 0; m = jp; half = ht; off = 0; }
+        else if (jp < ht + hh) { axis = 1; m = jp - ht; half = hh; off = a.gt * ht; }
+        else { axis = 2; m = jp - ht - hh; half = hwp; off = a.gt * ht + a.gh * hh; }
+        const float2 cs = a.rope[off + qpos[axis] * half + m];
+        const float x0 = f[b][rb][2 * pr], x1 = f[b][rb][2 * pr + 1];
+        qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
+        qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+      }
     }
-  }
-  den = group4_sum(den);
-  inv_den = den > 0.f ? 1.f / den : 0.f;
-  Frag<T> qpf[NRC];
+    den = group4_sum(den);
+    inv_den[b] = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-  for (int rc = 0; rc < NRC; ++rc) {
-    constexpr int kHi = 1;  // second 16-block of the 32-wide chunk
-    const int b0 = 2 * rc, b1 = (2 * rc + kHi < NRB) ? 2 * rc + kHi : 2 * rc;
-    const float keep = (2 * rc + kHi < NRB) ? 1.f : 0.f;  // rank 16: upper half is zero
-    qpf[rc].set_pair(0, qp[b0][0], qp[b0][1]);
-    qpf[rc].set_pair(1, qp[b0][2], qp[b0][3]);
-    qpf[rc].set_pair(2, keep * qp[b1][0], keep * qp[b1][1]);
-    qpf[rc].set_pair(3, keep * qp[b1][2], keep * qp[b1][3]);
+    for (int rc = 0; rc < NRC; ++rc) {
+      constexpr int kHi = 1;  // second 16-block of the 32-wide chunk
+      const int b0 = 2 * rc, b1 = (2 * rc + kHi < NRB) ? 2 * rc + kHi : 2 * rc;
+      const float keep = (2 * rc + kHi < NRB) ? 1.f : 0.f;  // rank 16: upper half is zero
+      qpf[b][rc].set_pair(0, qp[b0][0], qp[b0][1]);
+      qpf[b][rc].set_pair(1, qp[b0][2], qp[b0][3]);
+      qpf[b][rc].set_pair(2, keep * qp[b1][0], keep * qp[b1][1]);
+      qpf[b][rc].set_pair(3, keep * qp[b1][2], keep * qp[b1][3]);
+    }
   }
   constexpr int NFE = NDB * NRC * 512;
   const T* SP = reinterpret_cast<const T*>(a.sp_frag) + (size_t)bh * (sizeof(T) == 4 ? 1 : 2) * NFE;
 #pragma unroll
   for (int jd = 0; jd < NDB; ++jd) {
-    acc_n[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NQ; ++b) acc_n[b][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rc = 0; rc < NRC; ++rc) {
       Frag<T> sf;
       load8(sf, SP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-      mma(acc_n[jd], sf, qpf[rc]);
+#pragma unroll
+      for (int b = 0; b < NQ; ++b) mma(acc_n[b][jd], sf, qpf[b][rc]);
       if constexpr (sizeof(T) == 2) {
         load8(sf, SP + NFE + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-        mma(acc_n[jd], sf, qpf[rc]);
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) mma(acc_n[b][jd], sf, qpf[b][rc]);
       }
     }
   }
@@ -288,9 +297,13 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     if (a.lse && g == 0 && qvalid) a.lse[(size_t)bh * a.N_pad + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
 
-  f32x4 acc_n[NDB];
-  float inv_den = 0.f;
-  if constexpr (LINEAR) readout<T, D, R>(a, bh, qf, qrow, qvalid, lane, acc_n, inv_den);
+  f32x4 acc_n[1][NDB];
+  float inv_den[1] = {0.f};
+  if constexpr (LINEAR) {
+    const int qr[1] = {qrow};
+    const bool qv[1] = {qvalid};
+    readout<T, D, R, 1>(a, bh, &qf, qr, qv, lane, acc_n, inv_den);
+  }
 
   // epilogue: O = O_s / l + (q' S') / den, pad rows zero
   T* O = reinterpret_cast<T*>(a.o) + base + (size_t)qrow * D;
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
       for (int i = 0; i < 4; ++i) {
         float x = 0.f;
         if constexpr (SPARSE) x += acc_o[jd][i] * inv_l;
-        if constexpr (LINEAR) x += acc_n[jd][i] * inv_den;
+        if constexpr (LINEAR) x += acc_n[0][jd][i] * inv_den[0];
         r4[i] = qvalid ? x : 0.f;
       }
       st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
@@ -516,11 +529,11 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
     }
   }
 
+  f32x4 acc_n[NQB][NDB];
+  float inv_den[NQB] = {0.f, 0.f};
+  if constexpr (LINEAR) readout<bf16_t, D, R, NQB>(a, bh, qf, qrow, qvalid, lane, acc_n, inv_den);
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    f32x4 acc_n[NDB];
-    float inv_den = 0.f;
-    if constexpr (LINEAR) readout<bf16_t, D, R>(a, bh, qf[qb], qrow[qb], qvalid[qb], lane, acc_n, inv_den);
     bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + base + (size_t)qrow[qb] * D;
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
@@ -529,7 +542,7 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
       for (int i = 0; i < 4; ++i) {
         float x = 0.f;
         if constexpr (SPARSE) x += acc_o[qb][jd][i] * inv_l[qb];
-        if constexpr (LINEAR) x += acc_n[jd][i] * inv_den;
+        if constexpr (LINEAR) x += acc_n[qb][jd][i] * inv_den[qb];
         r4[i] = qvalid[qb] ? x : 0.f;
       }
       st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);

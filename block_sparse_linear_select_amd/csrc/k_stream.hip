@@ -41,10 +41,8 @@ hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const
 
 hipError_t launch_vtranspose(const Shape& s, const void* v, const Scratch& w, hipStream_t st) {
   dim3 grid(s.T, s.B * s.H);
-  const bf16_t* vv = reinterpret_cast<const bf16_t*>(v);
-  bf16_t* out = reinterpret_cast<bf16_t*>(w.vt);
-  if (s.d == 64) k_vtranspose<64><<<grid, 256, 0, st>>>(s.N, s.N_pad, s.T, vv, out);
-  else k_vtranspose<128><<<grid, 256, 0, st>>>(s.N, s.N_pad, s.T, vv, out);
+  k_vtranspose_fp8<<<grid, 256, 0, st>>>(s.N, s.N_pad, s.T, reinterpret_cast<const fp8_t*>(v),
+                                          reinterpret_cast<uint8_t*>(w.vt));
   return hipGetLastError();
 }
 

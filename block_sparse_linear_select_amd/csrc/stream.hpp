@@ -102,6 +102,41 @@ __device__ __forceinline__ int vt_pos(int key) {
   return 32 * c + 8 * g + 4 * h + i;
 }
 
+// fp8 V^T tiles for the sparse kernel: vt8[d][p] = code of V[key][d] with
+// key = 16 kb + 4 g + i stored at p = 16 g + 4 kb + i, so that lane group g of
+// a 16x16x128 operand reads its 16 keys of a tile as one 16-byte run.
+inline __device__ __forceinline__ int vt8_pos(int key) {
+  const int kb = key >> 4, g = (key >> 2) & 3, i = key & 3;
+  return 16 * g + 4 * kb + i;
+}
+
+// Thread `u` (< 16 * D / 8) holds codes of keys 4(u%16) .. +3 for dims
+// 8(u/16) .. +7 and writes them, transposed, into an LDS tile of D rows x 80 B.
+inline __device__ __forceinline__ void stage_vt8(uint8_t* Vt8, int u, const Chunk8<fp8_t>* vc) {
+  const int kg = u % 16, c8 = u / 16;
+  const int p0 = vt8_pos(4 * kg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = 8 * (e & 3);
+    uint32_t w = 0;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const uint32_t word = (e < 4) ? vc[ii].w.x : vc[ii].w.y;
+      w |= ((word >> sh) & 0xFFu) << (8 * ii);
+    }
+    *reinterpret_cast<uint32_t*>(&Vt8[(c8 * 8 + e) * 80 + p0]) = w;
+  }
+}
+
+// Copy a staged fp8 V^T tile (D rows x 64 codes) to global memory.
+template <int D = 128>
+__device__ __forceinline__ void write_vt8(uint8_t* dst, const uint8_t* Vt8, int tid) {
+  for (int q = tid; q < D * 4; q += 256) {
+    const int row = q >> 2, part = q & 3;
+    *reinterpret_cast<u32x4*>(dst + row * 64 + part * 16) = *reinterpret_cast<const u32x4*>(&Vt8[row * 80 + part * 16]);
+  }
+}
+
 // --------------------------------------------------------- streaming pass
 struct StreamArgs {
   int N, N_pad, T, nchunk, tpc;
@@ -140,6 +175,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 
   __shared__ __align__(16) OT Ks[STATE ? 64 * KSTR : 1];
   __shared__ __align__(16) OT Vt[STATE ? D * VSTR : 1];
+  __shared__ __align__(16) uint8_t Vt8[(STATE && sizeof(T) == 1) ? D * 80 : 16];  // fp8 V^T tile for the sparse kernel
   __shared__ double redq[POOL ? NCONT * D : 1];
   __shared__ double redk[POOL ? NCONT * D : 1];
   __shared__ int spos[64];
@@ -241,19 +277,15 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(vc[0], e), elem(vc[1], e), elem(vc[2], e), elem(vc[3], e));
       }
       if (tid < 64) spos[tid] = pack_pos(min(t * 64 + tid, a.N - 1), a.gh, a.gw);
+      if constexpr (sizeof(T) == 1) {
+        if (a.vt && tid < NVU) stage_vt8(Vt8, tid, vc);
+      }
     }
     __syncthreads();
     if (t + 1 < t1) load_tile(t + 1);
     if constexpr (STATE && sizeof(T) == 1) {
-      // hand the transposed tile to the sparse kernel: D rows of 64 keys
-      if (a.vt) {
-        bf16_t* dst = reinterpret_cast<bf16_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64;
-        for (int q = tid; q < D * 8; q += 256) {
-          const int row = q >> 3, gr = q & 7;
-          *reinterpret_cast<u32x4*>(dst + row * 64 + gr * 8) =
-              *reinterpret_cast<const u32x4*>(&Vt[row * VSTR + gr * 8]);
-        }
-      }
+      // hand the transposed fp8 tile to the sparse kernel
+      if (a.vt) write_vt8(reinterpret_cast<uint8_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64, Vt8, tid);
     }
 
     if constexpr (STATE) {
@@ -335,37 +367,26 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 }
 
 // ------------------------------------------------------------- V transpose
-// V tiles transposed for the sparse kernel when no streaming pass runs:
-// vt[bh][t][d][p] = V[bh][64 t + key(p)][d], keys permuted as vt_pos, rows
-// past N zero.  One block per (tile, b*H + h).
-template <int D>
-__global__ __launch_bounds__(256) void k_vtranspose(int N, int N_pad, int T, const bf16_t* __restrict__ v,
-                                                    bf16_t* __restrict__ vt) {
-  constexpr int VSTR = 64 + 8;
-  constexpr int NVU = 16 * (D / 8);
-  __shared__ __align__(16) bf16_t Vt[D * VSTR];
+// fp8 V^T tiles for the sparse kernel when no streaming pass runs (sparse
+// attention on a given CSR).  One block per (tile, b*H + h); rows past N are
+// zero codes.
+static __global__ __launch_bounds__(256) void k_vtranspose_fp8(int N, int N_pad, int T, const fp8_t* __restrict__ v,
+                                                        uint8_t* __restrict__ vt) {
+  constexpr int D = 128;
+  __shared__ __align__(16) uint8_t Vt8[D * 80];
   const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const bf16_t* V = v + (size_t)bh * N_pad * D;
-  if (tid < NVU) {
-    const int kg = tid % 16, c8 = tid / 16;
-    Chunk8<bf16_t> c[4];
+  const fp8_t* V = v + (size_t)bh * N_pad * D;
+  Chunk8<fp8_t> c[4];
+  const int kg = tid % 16, c8 = tid / 16;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int gr = t * 64 + 4 * kg + ii;
-      if (gr < N) gload8(c[ii], V + (size_t)gr * D + c8 * 8);
-      else zero8(c[ii]);
-    }
-    const int p0 = vt_pos(4 * kg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(c[0], e), elem(c[1], e), elem(c[2], e), elem(c[3], e));
+  for (int ii = 0; ii < 4; ++ii) {
+    const int gr = t * 64 + 4 * kg + ii;
+    if (gr < N) gload8(c[ii], V + (size_t)gr * D + c8 * 8);
+    else zero8(c[ii]);
   }
+  stage_vt8(Vt8, tid, c);
   __syncthreads();
-  bf16_t* dst = vt + ((size_t)bh * T + t) * D * 64;
-  for (int q = tid; q < D * 8; q += 256) {
-    const int row = q >> 3, gr = q & 7;
-    *reinterpret_cast<u32x4*>(dst + row * 64 + gr * 8) = *reinterpret_cast<const u32x4*>(&Vt[row * VSTR + gr * 8]);
-  }
+  write_vt8(vt + ((size_t)bh * T + t) * D * 64, Vt8, tid);
 }
 
 // ------------------------------------------------------------- finalize

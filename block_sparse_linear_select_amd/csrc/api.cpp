@@ -58,7 +58,7 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     p.off_uq = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
     p.off_rope = take((size_t)rope_entries(s) * sizeof(float2));
   }
-  if (p.vt) p.off_vt = take(bh * (size_t)s.N_pad * s.d * 2);
+  if (p.vt) p.off_vt = take(bh * (size_t)s.N_pad * s.d);  // one byte per code
   p.total = off;
   return p;
 }
@@ -277,7 +277,7 @@ HSA_API int hsa_sparse_attn(const hsa_attn_desc* desc, const void* q, const void
   if (!q || !k || !v || !row_ptr || !col_idx || !o_sparse)
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, row_ptr, col_idx and o_sparse are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
-  if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 sparse attention is not built in this version");
+  if (s.dt == Dt::FP8 && s.d != 128) return fail(HSA_ATTN_ERR_SHAPE, "FP8 attention needs head dim 128 (d=%d)", s.d);
   Plan p = make_plan(s, false, false, false, true);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
@@ -320,7 +320,7 @@ HSA_API int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void
   if (!q || !k || !v || !U_q || !U_k || !W_o || !o_lin)
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o and o_lin are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
-  if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 linear attention is not built in this version");
+  if (s.dt == Dt::FP8 && s.d != 128) return fail(HSA_ATTN_ERR_SHAPE, "FP8 attention needs head dim 128 (d=%d)", s.d);
   Plan p = make_plan(s, false, false, true, false);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
@@ -350,7 +350,7 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if (!q || !k || !v || !U_q || !U_k || !W_o || !o)
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o and o are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
-  if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "FP8 hybrid attention is not built in this version");
+  if (s.dt == Dt::FP8 && s.d != 128) return fail(HSA_ATTN_ERR_SHAPE, "FP8 attention needs head dim 128 (d=%d)", s.d);
   const bool internal = !given && !row_ptr_out;
   Plan p = make_plan(s, !given, internal, true, true);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;

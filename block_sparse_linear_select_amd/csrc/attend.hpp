@@ -33,7 +33,10 @@ struct AttendArgs {
   const float* z;
   const void* uq_frag;
   const float2* rope;
-  const void* vt;  // fp8 path: V tiles transposed ([BH][T][d][64], keys permuted)
+  const void* vt;  // fp8 path: V tiles transposed ([BH][T][d][64] codes, keys permuted)
+  const float* qs;  // fp8 path: per-(b, h, tile) scales of Q, K, V
+  const float* ks;
+  const float* vs;
   void* o;
   float* lse;
   long nrows;
@@ -68,7 +71,8 @@ __device__ __forceinline__ void lds_row(float* dst, const Chunk8<float>& c) {
 // 16 jd + 4 (l/16) + i).
 template <typename T, int D, int R, int NQ>
 __device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<T> (*qf)[D / 32], const int* qrow,
-                                        const bool* qvalid, int lane, f32x4 (*acc_n)[D / 16], float* inv_den) {
+                                        const bool* qvalid, int lane, f32x4 (*acc_n)[D / 16], float* inv_den,
+                                        float qscale = 1.f) {
   constexpr int NDB = D / 16;
   constexpr int NRB = R / 16;
   constexpr int NRC = (R + 31) / 32;
@@ -107,7 +111,7 @@ __device__ __forceinline__ void readout(const AttendArgs& a, int bh, const Frag<
     for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float phi = elu1(f[b][rb][i]);
+        const float phi = elu1(f[b][rb][i] * qscale);  // qscale: fp8 tile scale of the queries
         f[b][rb][i] = phi;
         den += phi * Z[16 * rb + 4 * g + i];
       }
@@ -587,6 +591,279 @@ static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& 
   if (s.rank == 16) return attend_dispatch_bf16<128, 16>(a, sparse, linear, st);
   if (s.rank == 32) return attend_dispatch_bf16<128, 32>(a, sparse, linear, st);
   return attend_dispatch_bf16<128, 64>(a, sparse, linear, st);
+}
+
+
+// ---------------------------------------------------------------------------
+// fp8 query-tile kernel (OCP E4M3FN codes with one fp32 scale per
+// (b, h, 64-token tile, tensor)).  One block = one query tile = 2 waves of 32
+// queries, d = 128.  Kept key tiles are taken in pairs so that one
+// 16x16x128 fp8 matrix-core step contracts over 128 keys:
+//   S = (q8 . k8) * s_q * s_k      (the scales enter the exp2 multiplier)
+//   P' = P * s_v,tile / s_v,ref    (P quantised to fp8 per tile; the ratio
+//                                   enters the exp2 argument, s_v,ref is the
+//                                   largest V scale of the row, so P' <= 256)
+//   O  = s_v,ref * sum P' v8 / sum P
+// V tiles arrive transposed (from the streaming pass) with keys ordered so
+// that lane group g reads its 16 keys of a tile as one 16-byte run.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma_fp8(const i32x8_t& a, const i32x8_t& b, const f32x4& c) {
+  // formats 0/0 = E4M3 for both operands, unit (2^0) block scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8_t cat8(const u32x4& lo, const u32x4& hi) {
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// 8 fp8 codes (two dwords) -> bf16 fragment with the exact code values
+__device__ __forceinline__ void codes_to_bf16(Frag<bf16_t>& f, uint32_t lo, uint32_t hi) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = j < 2 ? lo : hi;
+    const int sh = 16 * (j & 1);
+    f.set_pair(j, e4m3_to_f32((w >> sh) & 0xFFu), e4m3_to_f32((w >> (sh + 8)) & 0xFFu));
+  }
+}
+
+template <int R, bool SPARSE, bool LINEAR>
+__global__ __launch_bounds__(128, 1) void k_attend_fp8(AttendArgs a) {
+  constexpr int D = 128;
+  constexpr int NQB = 2;
+  constexpr int NDB = D / 16;
+  constexpr int KSTR = D + 16;     // bytes per staged K row
+  constexpr int VSTR = 64 + 16;    // bytes per staged V^T row
+  constexpr int KT = 64 * KSTR;    // bytes per staged K tile
+  constexpr int VTB = D * VSTR;    // bytes per staged V^T tile
+  __shared__ __align__(16) uint8_t lds[SPARSE ? 2 * (KT + VTB) : 16];
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.q) + base;
+  const uint8_t* K = reinterpret_cast<const uint8_t*>(a.k) + base;
+  const uint8_t* VT = reinterpret_cast<const uint8_t*>(a.vt) + base;  // T*64*D codes per head
+  const int nbytes = a.N * D;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)VT, 0, a.T * 64 * D, kBufferFlags);
+  const float* SQ = a.qs + (size_t)bh * a.T;
+  const float* SK = a.ks + (size_t)bh * a.T;
+  const float* SV = a.vs + (size_t)bh * a.T;
+  const float sq = SQ[qa];
+
+  int qrow[NQB];
+  bool qvalid[NQB];
+  i32x8_t qf8[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    qrow[qb] = qa * 64 + 32 * w + 16 * qb + l16;
+    qvalid[qb] = qrow[qb] < a.N;
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(qrs, qrow[qb] * D + 32 * g, 0, 0);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qrs, qrow[qb] * D + 32 * g + 16, 0, 0);
+    qf8[qb] = cat8(lo, hi);
+  }
+
+  f32x4 acc_o[NQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) acc_o[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float os[NQB] = {0.f, 0.f};  // final factor s_v,ref / l per query
+
+  if constexpr (SPARSE) {
+    const int beg = a.row_ptr[(size_t)bh * a.T + qa];
+    const int end = a.row_ptr[(size_t)bh * a.T + qa + 1];
+    float svref = 0.f;
+    for (int j = beg; j < end; ++j) {
+      const int col = a.col_idx[j];
+      if (col >= 0 && col < a.T) svref = fmaxf(svref, SV[col]);
+    }
+    svref = uniform_f(svref);
+    const float c0 = sq * a.scale_log2;
+    float m[NQB] = {-INFINITY, -INFINITY};
+    float lsum[NQB] = {0.f, 0.f};  // per-lane partial sums of P
+    // prefetch registers for a pair of tiles: 4 K granules + 4 V^T granules per tile
+    u32x4 kr[8], vr[8];
+    auto load_pair = [&](int c0i, int c1i) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = t == 0 ? c0i : c1i;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = tid + 128 * i;
+          const int krow = q >> 3, kgr = q & 7;   // 64 rows x 8 granules
+          const int vrow = q >> 2, vgr = q & 3;   // 128 rows x 4 granules
+          kr[4 * t + i] = __builtin_amdgcn_raw_buffer_load_b128(krs, (col * 64 + krow) * D + 16 * kgr, 0, 0);
+          vr[4 * t + i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (col * D + vrow) * 64 + 16 * vgr, 0, 0);
+        }
+      }
+    };
+    auto col_at = [&](int j) { return j < end ? a.col_idx[j] : -1; };
+    if (beg < end) load_pair(col_at(beg), col_at(beg + 1));
+    for (int j = beg; j < end; j += 2) {
+      const int col0 = col_at(j), col1 = col_at(j + 1);
+      __syncthreads();  // the previous pair's reads are done
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = tid + 128 * i;
+          *reinterpret_cast<u32x4*>(&lds[t * KT + (q >> 3) * KSTR + 16 * (q & 7)]) = kr[4 * t + i];
+          *reinterpret_cast<u32x4*>(&lds[2 * KT + t * VTB + (q >> 2) * VSTR + 16 * (q & 3)]) = vr[4 * t + i];
+        }
+      __syncthreads();
+      if (j + 2 < end) load_pair(col_at(j + 2), col_at(j + 3));
+
+      int kv[2];
+      float ck[2], lr[2], ir[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = t == 0 ? col0 : col1;
+        const bool ok = col >= 0 && col < a.T;
+        kv[t] = ok ? min(64, a.N - col * 64) : 0;
+        const float sv = ok ? SV[col] : 1.f;
+        ck[t] = ok ? c0 * SK[col] : 0.f;
+        lr[t] = ok ? __log2f(sv / svref) : 0.f;   // P' = P * s_v / s_v,ref
+        ir[t] = ok ? svref / sv : 0.f;
+      }
+      if (kv[0] + kv[1] == 0) continue;  // out-of-range tile indices contribute nothing
+      // S^T = K Q^T over both tiles: key blocks 0..3 from tile 0, 4..7 from tile 1
+      f32x4 s[NQB][8];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const int t = kb >> 2;
+        const uint8_t* kp = &lds[t * KT + (16 * (kb & 3) + l16) * KSTR + 32 * g];
+        const i32x8_t kf = cat8(*reinterpret_cast<const u32x4*>(kp), *reinterpret_cast<const u32x4*>(kp + 16));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mma_fp8(kf, qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+      // scores in log2 units; keys past N or of a missing tile do not exist
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = kb >> 2;
+            const float x = s[qb][kb][i] * ck[t];
+            s[qb][kb][i] = (16 * (kb & 3) + 4 * g + i < kv[t]) ? x : -INFINITY;
+          }
+      bool raise = false;
+      float mloc[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+        mloc[qb] = mx;
+        raise |= mx > m[qb] + 8.f;
+      }
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float mt = group4_max(mloc[qb]);
+          const float mn = mt > m[qb] + 8.f ? fmaxf(m[qb], mt) : m[qb];
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+          m[qb] = mn;
+#pragma unroll
+          for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
+          lsum[qb] *= alpha;
+        }
+      }
+      // P' -> fp8, B operand of the PV step: byte 4 kb + i of lane group g is
+      // key 16 (kb%4) + 4g + i of tile kb/4
+      i32x8_t pf[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          const int t = kb >> 2;
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m[qb] + lr[t]);
+            part[t] += pv[i];
+          }
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+          pf[qb][kb] = wd;
+        }
+        lsum[qb] += part[0] * ir[0] + part[1] * ir[1];
+      }
+      // O^T += V^T P'^T: lane (dim row, g) reads 16 codes of each tile
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd) {
+        const int row = 16 * jd + l16;
+        const i32x8_t vf = cat8(*reinterpret_cast<const u32x4*>(&lds[2 * KT + row * VSTR + 16 * g]),
+                                *reinterpret_cast<const u32x4*>(&lds[2 * KT + VTB + row * VSTR + 16 * g]));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc_o[qb][jd] = mma_fp8(vf, pf[qb], acc_o[qb][jd]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = group4_sum(lsum[qb]);
+      os[qb] = lt > 0.f ? svref / lt : 0.f;
+      if (a.lse && g == 0 && qvalid[qb])
+        a.lse[(size_t)bh * a.N_pad + qrow[qb]] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+
+  f32x4 acc_n[NQB][NDB];
+  float inv_den[NQB] = {0.f, 0.f};
+  if constexpr (LINEAR) {
+    // the readout runs on bf16 operands holding the exact code values
+    Frag<bf16_t> qfb[NQB][D / 32];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const uint2 u = *reinterpret_cast<const uint2*>(
+            Q + (size_t)(qvalid[qb] ? qrow[qb] : 0) * D + 32 * c + 8 * g);
+        codes_to_bf16(qfb[qb][c], qvalid[qb] ? u.x : 0u, qvalid[qb] ? u.y : 0u);
+      }
+    readout<bf16_t, D, R, NQB>(a, bh, qfb, qrow, qvalid, lane, acc_n, inv_den, sq);
+  }
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + base + (size_t)qrow[qb] * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float r4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.f;
+        if constexpr (SPARSE) x += acc_o[qb][jd][i] * os[qb];
+        if constexpr (LINEAR) x += acc_n[qb][jd][i] * inv_den[qb];
+        r4[i] = qvalid[qb] ? x : 0.f;
+      }
+      st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+    }
+  }
+}
+
+template <int R>
+static hipError_t attend_dispatch_fp8(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  if (sparse && linear) k_attend_fp8<R, true, true><<<grid, 128, 0, st>>>(a);
+  else if (sparse) k_attend_fp8<R, true, false><<<grid, 128, 0, st>>>(a);
+  else k_attend_fp8<R, false, true><<<grid, 128, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+static inline hipError_t attend_fp8_by_shape(const Shape& s, const AttendArgs& a, bool sparse, bool linear,
+                                             hipStream_t st) {
+  if (!linear || s.rank == 16) return attend_dispatch_fp8<16>(a, sparse, linear, st);
+  if (s.rank == 32) return attend_dispatch_fp8<32>(a, sparse, linear, st);
+  return attend_dispatch_fp8<64>(a, sparse, linear, st);
 }
 
 // Launch helpers shared by the bf16/fp8 translation unit and the float32 one.

@@ -167,5 +167,8 @@ __device__ __forceinline__ int head_interleaved_row(int i, int T) {
 // Marks a value as wave-uniform (kept in a scalar register), so that buffer
 // descriptors and addresses derived from it need no per-lane handling.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 }  // namespace hsa

@@ -36,7 +36,13 @@
  *     otherwise (also for FP8 inputs).
  *   - FP8 inputs: OCP E4M3FN byte codes; *_scale are float [B, H, T], the
  *     value of a code is code * scale of its (b, h, tile).  Scales must be
- *     NULL for the other dtypes.
+ *     positive and finite (other values give unspecified outputs) and NULL
+ *     for the other dtypes.  The attention calls take FP8 inputs with d = 128
+ *     only (HSA_ATTN_ERR_SHAPE otherwise); selection takes any d.  With FP8
+ *     inputs both products of the softmax branch run on fp8 operands: the
+ *     probabilities of each key tile are rounded to E4M3 after scaling by
+ *     that tile's V scale over the largest V scale among the row's kept
+ *     tiles, while the softmax statistics stay float32 and unrounded.
  *   - CSR: row_ptr int32 [B*H*T + 1] over the flattened (b, h, a) rows,
  *     starting at 0 and non-decreasing; col_idx int32, each row sorted
  *     ascending.  Output CSR capacity is B*H*T*(topk + force_diag) entries.

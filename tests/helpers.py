@@ -23,6 +23,10 @@ CASES = {
                                        rank=32, seed=9),
     "f32_d128_r64": make_workload("tiny_f32", H=2, d=128, grid=(3, 7, 11), topk=2, rank=64, seed=11),
     "bf16_dense_all_tiles": make_workload("wan14b_480p_bf16", H=1, grid=(2, 9, 14), topk=4, rank=32, seed=13),
+    # fp8 attention takes the kept tiles in pairs: odd and even kept counts
+    "fp8_ragged": make_workload("wan14b_720p_fp8", B=2, H=3, grid=(3, 10, 13), topk=3, rank=32, seed=21),
+    "fp8_r64_diag": make_workload("wan14b_720p_fp8", H=2, grid=(5, 12, 20), topk=4, force_diag=True,
+                                  rank=64, seed=23),
 }
 
 

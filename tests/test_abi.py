@@ -103,3 +103,8 @@ def test_null_and_workspace_errors_enqueue_nothing():
     rc = L.hsa_block_select(ctypes.byref(d8), fake, fake, None, None, fake, fake, None, None, fake, need, None)
     assert rc == -3
     assert b"scale" in L.hsa_attn_last_error()
+    # fp8 attention needs d = 128 (selection does not)
+    d8 = _cfg(dtype="fp8", d=64).desc()
+    rc = L.hsa_sparse_attn(ctypes.byref(d8), fake, fake, fake, fake, fake, fake, fake, fake, fake, None,
+                           fake, need, None)
+    assert rc == -2 and b"128" in L.hsa_attn_last_error()

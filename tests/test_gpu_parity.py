@@ -136,31 +136,37 @@ def test_runs_are_bitwise_reproducible(case):
 
 
 # ---------------------------------------------------------------- edge cases
-def test_given_csr_with_empty_row_and_out_of_range_columns():
-    w = Hp.CASES["bf16_ragged"]
+@pytest.mark.parametrize("name", ["bf16_ragged", "fp8_ragged"])
+def test_given_csr_with_empty_row_and_out_of_range_columns(name):
+    w = Hp.CASES[name]
     inp = Hp.gen(w)
     d = Hp.to_device(inp, DEV)
     T = w.T
     rows_h = []
     for b in range(w.B):
         for h in range(w.H):
-            rows = [np.array([a, (a + 2) % T]) for a in range(T)]
+            rows = [np.array([a, (a + 2) % T, (a + 5) % T]) for a in range(T)]
             rows_h.append(rows)
     rows_h[0][1] = np.array([], dtype=np.int64)          # empty row -> O_s = 0
     rp, ci = Hp.csr_tensors(rows_h, DEV)
     ci_bad = ci.clone()
-    r = 3  # row (b=0, h=0, a=3): add entries outside [0, T) that must be skipped
-    lo, hi = int(rp[r]), int(rp[r + 1])
-    ci_bad[lo] = T + 5
-    o = B.sparse_attn(B.Config.from_workload(w), d["q"], d["k"], d["v"], rp, ci_bad)
+    # row (b=0, h=0, a=3): its first entry lies outside [0, T) and is skipped;
+    # row a=4: its first two entries (one kept pair) are both out of range
+    r3, r4 = (int(rp[3]), int(rp[4])), (int(rp[4]), int(rp[5]))
+    ci_bad[r3[0]] = T + 5
+    ci_bad[r4[0]] = -1
+    ci_bad[r4[0] + 1] = T
+    o = B.sparse_attn(B.Config.from_workload(w), d["q"], d["k"], d["v"], rp, ci_bad,
+                      d["q_scale"], d["k_scale"], d["v_scale"])
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     assert np.all(o[0, 0, 64:128] == 0)
     qh, kh, vh = Hp.head_arrays(inp, 0, 0)
-    kept = [int(c) for c in ci[lo + 1:hi].cpu().numpy()]
-    ref = R.sparse_tile(qh, kh, vh, w.N, 3, kept, w.softmax_scale)
-    err = np.linalg.norm(o[0, 0, 192:192 + len(ref)] - ref) / np.linalg.norm(ref)
-    assert err <= 1e-2
+    for a, (lo, hi), skip in ((3, r3, 1), (4, r4, 2)):
+        kept = [int(c) for c in ci[lo + skip:hi].cpu().numpy()]
+        ref = R.sparse_tile(qh, kh, vh, w.N, a, kept, w.softmax_scale)
+        err = np.linalg.norm(o[0, 0, 64 * a:64 * a + len(ref)] - ref) / np.linalg.norm(ref)
+        assert err <= Hp.TOL[w.dtype]
 
 
 def test_topk_one_keeps_the_argmax():

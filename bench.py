@@ -11,7 +11,7 @@ are seeded synthetic tensors of that shape, resident in HBM before timing.
 Prints one JSON line with the whole-call throughput in dense-equivalent
 TFLOP/s (4 N^2 d H per call), the per-kernel split from HIP events recorded
 on the launch stream, the roofline of the dominant kernel (the sparse flash
-kernel against the bf16 matrix-core peak) and the fp64 oracle timed on this
+kernel against the dense matrix-core peak of the input type) and the fp64 oracle timed on this
 host's cores over a bounded sample.
 """
 import argparse
@@ -33,9 +33,49 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+ATTEND_SOURCES = ("common.hpp", "attend.hpp", "k_attend.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attend_hbm_traffic.md")
+
+
+def attend_source_digest():
+    """sha256 over the sources the attend kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_linear_select_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attend launch from the committed counter summary, or None
+    when there is none for this workload or the kernel sources changed since.
+    The summary carries lines `traffic <workload> <bytes per launch> <digest>`."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    digest = attend_source_digest()
+    for ln in lines:
+        f = ln.strip().strip("`").split()
+        if len(f) == 4 and f[0] == "traffic" and f[1] == workload and f[3] == digest:
+            return float(f[2])
+    return None
+
+
+def head_fp64(w, inp, h):
+    """(q, k, v) of head (0, h) in fp64 exactly as the kernels read them."""
+    from oracle import rola as R
+    from workloads.gen import fp8_codes, to_fp64
+    if w.dtype == "fp8":
+        return tuple(R.dequantize_tiles(fp8_codes(getattr(inp, n)[0, h]), getattr(inp, n + "_scale")[0, h].numpy())
+                     for n in ("q", "k", "v"))
+    return to_fp64(inp.q[0, h]), to_fp64(inp.k[0, h]), to_fp64(inp.v[0, h])
+
+
 def cpu_baseline(w, inp, heads):
     """The fp64 oracle on `heads` whole heads of the workload, in the metric's unit."""
-    import numpy as np
     from oracle import rola as R
     from workloads.gen import to_fp64
     try:
@@ -45,8 +85,7 @@ def cpu_baseline(w, inp, heads):
         threads = 1
     t_total = 0.0
     for h in heads:
-        args = (to_fp64(inp.q[0, h]), to_fp64(inp.k[0, h]), to_fp64(inp.v[0, h]), w.N, w.grid,
-                to_fp64(inp.uq[h]), to_fp64(inp.uk[h]), to_fp64(inp.wo[h]))
+        args = (*head_fp64(w, inp, h), w.N, w.grid, to_fp64(inp.uq[h]), to_fp64(inp.uk[h]), to_fp64(inp.wo[h]))
         t0 = time.perf_counter()
         R.hybrid_head(*args, topk=w.topk, force_diag=w.force_diag, scale=w.softmax_scale, base=w.rope_base)
         t_total += time.perf_counter() - t0
@@ -66,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b_720p_bf16")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads the oracle baseline runs (0 skips it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
+                         "MiB each (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by head, "
@@ -90,6 +132,15 @@ def main():
     run = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
                            sc["v_scale"], check=False)
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        log(f"  calibration: 3 x neg over {args.calibrate_copy} MiB float32 (read and write {n * 4} bytes each)")
+        del x, y
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -133,7 +184,7 @@ def main():
         "executed_tflops": exec_flops / (ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": "k_attend (block-sparse flash + linear readout)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "kernels_ms": kern,
         "linear_state": {"kernel": "k_stream (pooling + key/value state)", "ms": stream_ms,
                          "kv_bytes": kv_bytes, "kv_GBps": kv_bytes / (stream_ms * 1e-3) / 1e9,

@@ -332,39 +332,75 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 // bf16 query-tile kernel.  One block = one (b, h, query tile) = 2 waves of 32
 // queries; each wave keeps its queries as two 16-column B-fragment sets, so
 // every K or V fragment read from LDS feeds two matrix-core steps.
-// K and V tiles sit in LDS row-major with padded rows, which keeps both the
-// 16-byte K reads and the transposing V reads free of bank conflicts.  V fragments come
-// straight from the row-major tile through ds_read_b64_tr_b16: within each
-// 16-lane group, output lane i, element t is element (i mod 4) of the 8 bytes
-// addressed by source lane 4t + i/4.  NSTAGE = 1 or 2 LDS tile buffers.
+//
+// Staging.  Key tiles travel global -> LDS by buffer loads that write LDS
+// directly (no registers in between): one such load moves 64 lanes x 16 bytes
+// into 1 KB of contiguous LDS, lane l at byte 16 l.  K and V have one LDS
+// buffer each; the loads of the next K tile are issued once both waves are
+// done with the current one (after the scores), those of the next V tile once
+// both are done with the PV step, so each load has about half an iteration to
+// land.  A tile index outside [0, T) reads as zeros and is skipped.
+//
+// Layout.  Rows are stored unpadded, their 16-byte granules permuted by an
+// XOR swizzle (position = granule ^ f(row)) so that fragment reads are free
+// of bank conflicts: for K, the 16 rows of a 16-byte fragment read land on 16
+// distinct granule positions of the 64 banks; for V, each half wave of a
+// transposing 8-byte read touches 8 rows x 32 bytes, 8 distinct granule pairs.
+// V fragments come straight from the row-major tile through
+// ds_read_b64_tr_b16: within each 16-lane group, output lane i, element t is
+// element (i mod 4) of the 8 bytes addressed by source lane 4t + i/4.
 // ---------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, bounds-checked (gfx9-family dword 3)
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void* lds_void_t;
 
-// LDS row stride of a staged K or V tile: D + 8 elements (16 bytes of
-// padding), so rows start 4 banks apart.  Sixteen rows then cover every bank
-// exactly once for a 16-byte read and twice (the minimum for 512 bytes) for
-// a transposing 8-byte read, and each fragment address is a per-lane base
-// plus a compile-time offset.
-template <int D>
-__device__ __forceinline__ int lds_at(int row, int col) {
-  return row * (D + 8) + col;
+// s_waitcnt immediate that waits for all but n vector-memory operations
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Swizzles of a staged tile with RG 16-byte granules per row (RB = 16 RG
+// bytes): rows sharing a 256-byte bank set get distinct granule positions
+// (K) or distinct granule pairs (V).
+template <int RG> __device__ __forceinline__ int swz_k(int row) { return (row / (16 / RG)) & (RG - 1); }
+template <int RG> __device__ __forceinline__ int swz_v(int row) { return 2 * ((row / (16 / RG)) & (RG / 2 - 1)); }
+
+// One wave's share of the LDS-direct loads of a 64-row tile (RB bytes per
+// row): load i of wave w fills LDS bytes [1024 (NI w + i), +1024).
+// off[i] = the lane's byte offset within the tile of the granule it moves.
+template <int RB, bool V>
+__device__ __forceinline__ void dma_offsets(int w, int lane, int* off) {
+  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int lin = 1024 * (NI * w + i) + 16 * lane;
+    const int row = lin / RB, pos = (lin % RB) / 16;
+    const int gr = pos ^ (V ? swz_v<RG>(row) : swz_k<RG>(row));
+    off[i] = row * RB + 16 * gr;
+  }
+}
+template <int RB>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int col, const int* off, uint8_t* dst, int w) {
+  constexpr int NI = 64 * RB / 1024 / 2;
+  const int base = col * 64 * RB;  // out-of-range columns fall outside the buffer and load zeros
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)(dst + 1024 * (NI * w + i)), 16, base + off[i], 0, 0, 0);
 }
 
-template <int D, int R, bool SPARSE, bool LINEAR, int NSTAGE>
-__global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(AttendArgs a) {
-  constexpr int G = D / 8;            // 16-byte granules per row
-  constexpr int NQB = 2;              // 16-query blocks per wave
+template <int D, int R, bool SPARSE, bool LINEAR>
+__global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
+  constexpr int RB = 2 * D, RG = RB / 16;  // bytes and granules per row
+  constexpr int NQB = 2;                   // 16-query blocks per wave
   constexpr int NDB = D / 16;
-  constexpr int NGT = 64 * G / 128;   // granules per thread per tile
-  constexpr int TILE = 64 * (D + 8);  // elements per staged K (or V) tile
-  __shared__ __align__(16) bf16_t lds[SPARSE ? NSTAGE * 2 * TILE : 8];
+  constexpr int NI = 64 * RB / 1024 / 2;   // LDS-direct loads per wave per tile
+  __shared__ __align__(16) uint8_t Ks[SPARSE ? 64 * RB : 16];
+  __shared__ __align__(16) uint8_t Vs[SPARSE ? 64 * RB : 16];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
   const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + base;
@@ -373,7 +409,7 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
 
   // Bounds-checked buffer views of this head: rows >= N read as zero, and so
   // does any offset past the slice (an out-of-range tile index included).
-  const int nbytes = a.N * D * 2;
+  const int nbytes = a.N * RB;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
@@ -398,6 +434,9 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
   float inv_l[NQB] = {0.f, 0.f};
 
   if constexpr (SPARSE) {
+    // The LDS tiles are only written by the LDS-direct loads; this store,
+    // never executed, keeps the compiler from treating them as unwritten.
+    if (a.N < 0) { Ks[tid] = 0; Vs[tid] = 0; }
     const int beg = a.row_ptr[(size_t)bh * a.T + qa];
     const int end = a.row_ptr[(size_t)bh * a.T + qa + 1];
     // Running max (log2 units) is only raised when a row's new max exceeds
@@ -410,119 +449,124 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
     Frag<bf16_t> ones;
     ones.w = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const float c2 = a.scale_log2;
-    u32x4 kr[NGT], vr[NGT];
-    auto load_tile = [&](int col) {
-#pragma unroll
-      for (int i = 0; i < NGT; ++i) {
-        const int q = tid + 128 * i, row = q / G, gr = q % G;
-        const int off = ((col * 64 + row) * D + gr * 8) * 2;
-        kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-        vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-      }
-    };
-    if (beg < end) load_tile(a.col_idx[beg]);
-    for (int j = beg; j < end; ++j) {
-      bf16_t* Ks = lds + (NSTAGE == 1 ? 0 : ((j - beg) & 1) * 2 * TILE);
-      bf16_t* Vs = Ks + TILE;
-      const int col = a.col_idx[j];
-      if constexpr (NSTAGE == 1) __syncthreads();  // the previous tile's reads are done
-#pragma unroll
-      for (int i = 0; i < NGT; ++i) {
-        const int q = tid + 128 * i, row = q / G, gr = q % G;
-        *reinterpret_cast<u32x4*>(&Ks[lds_at<D>(row, 8 * gr)]) = kr[i];
-        *reinterpret_cast<u32x4*>(&Vs[lds_at<D>(row, 8 * gr)]) = vr[i];
-      }
+    int koff[NI], voff[NI];
+    dma_offsets<RB, false>(w, lane, koff);
+    dma_offsets<RB, true>(w, lane, voff);
+    // fragment read addresses: K (16 B) per 32-wide d chunk cc; V (8 B, transposing) per 16-wide d block jd
+    const int fk = swz_k<RG>(l16);
+    const int kaddr = l16 * RB + 16 * (g ^ fk);                   // ^ 64 cc, + 16 RB kb
+    const int rowl = 4 * g + (l16 >> 2);
+    const int vaddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);  // ^ 32 jd
+    // The row's tile indices, 64 at a time, one per lane: the loop reads them
+    // with readlane and issues no memory load of its own besides the tiles.
+    int colv = beg + lane < end ? a.col_idx[beg + lane] : 0;
+    if (beg < end) {
+      const int c0 = __builtin_amdgcn_readfirstlane(colv);
+      dma_tile<RB>(krs, c0, koff, Ks, w);
+      dma_tile<RB>(vrs, c0, voff, Vs, w);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's K share has landed
       __syncthreads();
-      if (j + 1 < end) load_tile(a.col_idx[j + 1]);
-
+    }
+    for (int j = beg; j < end; ++j) {
+      const int col = __builtin_amdgcn_readlane(colv, (j - beg) & 63);
       const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
-      if (kvalid <= 0) continue;  // an out-of-range tile index contributes nothing
-      // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores)
-      f32x4 s[NQB][4];
+      Frag<bf16_t> pf[NQB][2];
+      if (kvalid > 0) {
+        // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores)
+        f32x4 s[NQB][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          Frag<bf16_t> kf;
-          kf.w = *reinterpret_cast<const u32x4*>(&Ks[lds_at<D>(16 * kb + l16, 32 * c + 8 * g)]);
+          for (int c = 0; c < D / 32; ++c) {
+            Frag<bf16_t> kf;
+            kf.w = *reinterpret_cast<const u32x4*>(&Ks[(kaddr ^ (64 * c)) + 16 * RB * kb]);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf, qf[qb][c]);
+            for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf, qf[qb][c]);
+          }
         }
-      }
-      if (kvalid < 64) {  // ragged last tile: keys past N do not exist
+        if (__builtin_expect(kvalid < 64, 0)) {  // ragged last tile: keys past N do not exist
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+          for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * kb + 4 * g + i >= kvalid) s[qb][kb][i] = -INFINITY;
+        }
+        // The common path needs no cross-lane work: if no lane's own keys exceed
+        // the running max by more than 8, every exp2 argument is <= 8.
+        float mloc[NQB];
+        bool raise = false;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
+#pragma unroll
+          for (int kb = 1; kb < 4; ++kb)
+            mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+          mloc[qb] = mx * c2;
+          raise |= mloc[qb] > m[qb] + 8.f;
+        }
+        if (__ballot(raise)) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float mt = group4_max(mloc[qb]);  // the row max, the same in all four lane groups
+            const float mn = mt > m[qb] + 8.f ? fmaxf(m[qb], mt) : m[qb];
+            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+            m[qb] = mn;
+#pragma unroll
+            for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
+            acc_l[qb] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float nm = -m[qb];
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * kb + 4 * g + i >= kvalid) s[qb][kb][i] = -INFINITY;
-      }
-      // The common path needs no cross-lane work: if no lane's own keys exceed
-      // the running max by more than 8, every exp2 argument is <= 8.
-      float mloc[NQB];
-      bool raise = false;
+            for (int i = 0; i < 4; ++i) s[qb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], c2, nm));
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
-#pragma unroll
-        for (int kb = 1; kb < 4; ++kb)
-          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-        mloc[qb] = mx * c2;
-        raise |= mloc[qb] > m[qb] + 8.f;
-      }
-      if (__ballot(raise)) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const float mt = group4_max(mloc[qb]);  // the row max, the same in all four lane groups
-          const float mn = mt > m[qb] + 8.f ? fmaxf(m[qb], mt) : m[qb];
-          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-          m[qb] = mn;
-#pragma unroll
-          for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
-          acc_l[qb] *= alpha;
-        }
-      }
-      Frag<bf16_t> pf[NQB][2];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float nm = -m[qb];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[qb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], c2, nm));
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          pf[qb][c].set_pair(0, s[qb][2 * c][0], s[qb][2 * c][1]);
-          pf[qb][c].set_pair(1, s[qb][2 * c][2], s[qb][2 * c][3]);
-          pf[qb][c].set_pair(2, s[qb][2 * c + 1][0], s[qb][2 * c + 1][1]);
-          pf[qb][c].set_pair(3, s[qb][2 * c + 1][2], s[qb][2 * c + 1][3]);
-          mma(acc_l[qb], ones, pf[qb][c]);
-        }
-      }
-      // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4
-      const int trow = 4 * g + (l16 >> 2);   // source row within a 16-key half
-      const int tcol = 4 * (l16 & 3);        // source column within a 16-dim block
-#pragma unroll
-      for (int jd = 0; jd < NDB; ++jd) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          Frag<bf16_t> vf;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row = 32 * c + 16 * hh + trow, dcol = 16 * jd + tcol;
-            const bf16_t* src = &Vs[lds_at<D>(row, dcol)];
-            s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-            uint2 u = __builtin_bit_cast(uint2, t);
-            vf.w[2 * hh] = u.x;
-            vf.w[2 * hh + 1] = u.y;
+          for (int c = 0; c < 2; ++c) {
+            pf[qb][c].set_pair(0, s[qb][2 * c][0], s[qb][2 * c][1]);
+            pf[qb][c].set_pair(1, s[qb][2 * c][2], s[qb][2 * c][3]);
+            pf[qb][c].set_pair(2, s[qb][2 * c + 1][0], s[qb][2 * c + 1][1]);
+            pf[qb][c].set_pair(3, s[qb][2 * c + 1][2], s[qb][2 * c + 1][3]);
+            mma(acc_l[qb], ones, pf[qb][c]);
           }
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) mma(acc_o[qb][jd], vf, pf[qb][c]);
         }
       }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's V share has landed
+      __syncthreads();                            // V visible; both waves are done with K
+      if (((j + 1 - beg) & 63) == 0 && j + 1 < end)  // the next 64 indices (nothing else is in flight here)
+        colv = j + 1 + lane < end ? a.col_idx[j + 1 + lane] : 0;
+      const int ncol = __builtin_amdgcn_readlane(colv, (j + 1 - beg) & 63);
+      if (j + 1 < end) dma_tile<RB>(krs, ncol, koff, Ks, w);
+      if (kvalid > 0) {
+        // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4
+#pragma unroll
+        for (int jd = 0; jd < NDB; ++jd) {
+          const int va = vaddr ^ (32 * jd);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            Frag<bf16_t> vf;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint8_t* src = &Vs[va + (32 * c + 16 * hh) * RB];
+              s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+              uint2 u = __builtin_bit_cast(uint2, t);
+              vf.w[2 * hh] = u.x;
+              vf.w[2 * hh + 1] = u.y;
+            }
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) mma(acc_o[qb][jd], vf, pf[qb][c]);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K has landed
+      __syncthreads();                            // next K visible; both waves are done with V
+      if (j + 1 < end) dma_tile<RB>(vrs, ncol, voff, Vs, w);
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -554,29 +598,13 @@ __global__ __launch_bounds__(128, NSTAGE == 1 ? 2 : 1) void k_attend_bf16(Attend
   }
 }
 
-// LDS stages of the bf16 kernel: 1 (four blocks per CU, two waves per SIMD)
-// by default; HSA_ATTN_NSTAGE=2 selects double buffering (two blocks per CU).
-static inline int attend_nstage() {
-  static const int ns = [] {
-    const char* e = getenv("HSA_ATTN_NSTAGE");
-    return (e && e[0] == '2') ? 2 : 1;
-  }();
-  return ns;
-}
-
-template <int D, int R, int NS>
-static hipError_t attend_launch_bf16(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
-  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
-  if (sparse && linear) k_attend_bf16<D, R, true, true, NS><<<grid, 128, 0, st>>>(a);
-  else if (sparse) k_attend_bf16<D, R, true, false, NS><<<grid, 128, 0, st>>>(a);
-  else k_attend_bf16<D, R, false, true, NS><<<grid, 128, 0, st>>>(a);
-  return hipGetLastError();
-}
-
 template <int D, int R>
 static hipError_t attend_dispatch_bf16(const AttendArgs& a, bool sparse, bool linear, hipStream_t st) {
-  return attend_nstage() == 2 ? attend_launch_bf16<D, R, 2>(a, sparse, linear, st)
-                              : attend_launch_bf16<D, R, 1>(a, sparse, linear, st);
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  if (sparse && linear) k_attend_bf16<D, R, true, true><<<grid, 128, 0, st>>>(a);
+  else if (sparse) k_attend_bf16<D, R, true, false><<<grid, 128, 0, st>>>(a);
+  else k_attend_bf16<D, R, false, true><<<grid, 128, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& a, bool sparse, bool linear,
@@ -592,7 +620,6 @@ static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& 
   if (s.rank == 32) return attend_dispatch_bf16<128, 32>(a, sparse, linear, st);
   return attend_dispatch_bf16<128, 64>(a, sparse, linear, st);
 }
-
 
 // ---------------------------------------------------------------------------
 // fp8 query-tile kernel (OCP E4M3FN codes with one fp32 scale per
@@ -743,17 +770,22 @@ __global__ __launch_bounds__(128, 1) void k_attend_fp8(AttendArgs a) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mma_fp8(kf, qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
       }
-      // scores in log2 units; keys past N or of a missing tile do not exist
+      // scores in log2 units
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = kb >> 2;
-            const float x = s[qb][kb][i] * ck[t];
-            s[qb][kb][i] = (16 * (kb & 3) + 4 * g + i < kv[t]) ? x : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) s[qb][kb][i] *= ck[kb >> 2];
+      if (__builtin_expect(kv[0] < 64 || kv[1] < 64, 0)) {  // keys past N or of a missing tile do not exist
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * (kb & 3) + 4 * g + i >= kv[kb >> 2]) s[qb][kb][i] = -INFINITY;
+      }
       bool raise = false;
       float mloc[NQB];
 #pragma unroll

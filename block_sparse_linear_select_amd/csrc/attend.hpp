@@ -472,19 +472,26 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
       const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
       Frag<bf16_t> pf[NQB][2];
       if (kvalid > 0) {
-        // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores)
+        // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores); the K
+        // fragments of key block kb + 1 are read while kb's steps run
         f32x4 s[NQB][4];
+        Frag<bf16_t> kf[2][D / 32];
+        auto ldk = [&](int kb, Frag<bf16_t>* dst) {
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+            dst[c].w = *reinterpret_cast<const u32x4*>(&Ks[(kaddr ^ (64 * c)) + 16 * RB * kb]);
+        };
+        ldk(0, kf[0]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+          if (kb + 1 < 4) ldk(kb + 1, kf[(kb + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            Frag<bf16_t> kf;
-            kf.w = *reinterpret_cast<const u32x4*>(&Ks[(kaddr ^ (64 * c)) + 16 * RB * kb]);
+          for (int c = 0; c < D / 32; ++c)
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf, qf[qb][c]);
-          }
+            for (int qb = 0; qb < NQB; ++qb) mma(s[qb][kb], kf[kb & 1][c], qf[qb][c]);
         }
         if (__builtin_expect(kvalid < 64, 0)) {  // ragged last tile: keys past N do not exist
 #pragma unroll
@@ -544,24 +551,31 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
       const int ncol = __builtin_amdgcn_readlane(colv, (j + 1 - beg) & 63);
       if (j + 1 < end) dma_tile<RB>(krs, ncol, koff, Ks, w);
       if (kvalid > 0) {
-        // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4
-#pragma unroll
-        for (int jd = 0; jd < NDB; ++jd) {
+        // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4.
+        // The V fragments of d block jd + 1 are read while jd's steps run.
+        Frag<bf16_t> vf[2][2];
+        auto ldv = [&](int jd, Frag<bf16_t>* dst) {
           const int va = vaddr ^ (32 * jd);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            Frag<bf16_t> vf;
+          for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const uint8_t* src = &Vs[va + (32 * c + 16 * hh) * RB];
               s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
               uint2 u = __builtin_bit_cast(uint2, t);
-              vf.w[2 * hh] = u.x;
-              vf.w[2 * hh + 1] = u.y;
+              dst[c].w[2 * hh] = u.x;
+              dst[c].w[2 * hh + 1] = u.y;
             }
+        };
+        ldv(0, vf[0]);
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) mma(acc_o[qb][jd], vf, pf[qb][c]);
-          }
+        for (int jd = 0; jd < NDB; ++jd) {
+          if (jd + 1 < NDB) ldv(jd + 1, vf[(jd + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the steps that do not need them
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) mma(acc_o[qb][jd], vf[jd & 1][c], pf[qb][c]);
         }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K has landed

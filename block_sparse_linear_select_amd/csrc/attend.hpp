@@ -359,6 +359,19 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// Workgroup barrier for the LDS-direct pipeline.  __syncthreads() also
+// orders memory, which makes the compiler wait for every load still writing
+// LDS, including the one just issued for the other buffer.  Here each wave
+// waits for its own loads of the buffer it is about to publish (s_waitcnt
+// before the call), finishes its own LDS reads, and the asm statement keeps
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are complete
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Swizzles of a staged tile with RG 16-byte granules per row (RB = 16 RG
 // bytes): rows sharing a 256-byte bank set get distinct granule positions
 // (K) or distinct granule pairs (V).
@@ -379,13 +392,33 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, int* off) {
     off[i] = row * RB + 16 * gr;
   }
 }
+// Buffer descriptor as four scalar registers (base, stride 0, num_records,
+// flags) for the LDS-direct loads below.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc_regs(const void* base, int nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)(uint32_t)p, (int)((p >> 32) & 0xFFFF), nbytes, kBufferFlags};
+}
+
+// One 16-byte-per-lane LDS-direct load: M0 = LDS destination of lane 0 (lane
+// l writes 16 bytes at M0 + 16 l), voff = the lane's byte offset in the
+// buffer.  Written as an asm statement so that the compiler, which does not
+// see its LDS write, inserts no waits for it before unrelated LDS reads (it
+// would wait for every such load before a transposing read, whose memory
+// operand carries no alias information); the kernels wait on vmcnt
+// themselves before publishing a buffer.  s_nop covers the M0 hazard.
+__device__ __forceinline__ void lds_dma16(const i32x4_t& rs, const uint8_t* lds_dst, int voff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t)(lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(m0v), "s"(rs) : "memory", "m0");
+}
+
 template <int RB>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int col, const int* off, uint8_t* dst, int w) {
+__device__ __forceinline__ void dma_tile(const i32x4_t& rs, int col, const int* off, uint8_t* dst, int w) {
   constexpr int NI = 64 * RB / 1024 / 2;
   const int base = col * 64 * RB;  // out-of-range columns fall outside the buffer and load zeros
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)(dst + 1024 * (NI * w + i)), 16, base + off[i], 0, 0, 0);
+  for (int i = 0; i < NI; ++i) lds_dma16(rs, dst + 1024 * (NI * w + i), base + off[i]);
 }
 
 template <int D, int R, bool SPARSE, bool LINEAR>
@@ -411,8 +444,8 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
   // does any offset past the slice (an out-of-range tile index included).
   const int nbytes = a.N * RB;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
+  const i32x4_t krs = make_rsrc_regs(K, nbytes);
+  const i32x4_t vrs = make_rsrc_regs(V, nbytes);
 
   int qrow[NQB];
   bool qvalid[NQB];
@@ -434,8 +467,9 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
   float inv_l[NQB] = {0.f, 0.f};
 
   if constexpr (SPARSE) {
-    // The LDS tiles are only written by the LDS-direct loads; this store,
-    // never executed, keeps the compiler from treating them as unwritten.
+    // The LDS tiles are only written by the LDS-direct loads, which the
+    // compiler does not see; this store, never executed, keeps it from
+    // treating them as unwritten.
     if (a.N < 0) { Ks[tid] = 0; Vs[tid] = 0; }
     const int beg = a.row_ptr[(size_t)bh * a.T + qa];
     const int end = a.row_ptr[(size_t)bh * a.T + qa + 1];
@@ -458,23 +492,24 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
     const int rowl = 4 * g + (l16 >> 2);
     const int vaddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);  // ^ 32 jd
     // The row's tile indices, 64 at a time, one per lane: the loop reads them
-    // with readlane and issues no memory load of its own besides the tiles.
+    // with readlane; col / ncol are the indices of tiles j and j + 1.
     int colv = beg + lane < end ? a.col_idx[beg + lane] : 0;
+    int col = __builtin_amdgcn_readlane(colv, 0);
+    int ncol = __builtin_amdgcn_readlane(colv, 1);
     if (beg < end) {
-      const int c0 = __builtin_amdgcn_readfirstlane(colv);
-      dma_tile<RB>(krs, c0, koff, Ks, w);
-      dma_tile<RB>(vrs, c0, voff, Vs, w);
+      dma_tile<RB>(krs, col, koff, Ks, w);
+      dma_tile<RB>(vrs, col, voff, Vs, w);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's K share has landed
       __syncthreads();
     }
     for (int j = beg; j < end; ++j) {
-      const int col = __builtin_amdgcn_readlane(colv, (j - beg) & 63);
+      const bool more = j + 1 < end;
       const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
       Frag<bf16_t> pf[NQB][2];
+      f32x4 s[NQB][4];
       if (kvalid > 0) {
         // S^T = K Q^T: 4 key blocks x 2 query blocks (raw scores); the K
         // fragments of key block kb + 1 are read while kb's steps run
-        f32x4 s[NQB][4];
         Frag<bf16_t> kf[2][D / 32];
         auto ldk = [&](int kb, Frag<bf16_t>* dst) {
 #pragma unroll
@@ -545,11 +580,8 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
         }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's V share has landed
-      __syncthreads();                            // V visible; both waves are done with K
-      if (((j + 1 - beg) & 63) == 0 && j + 1 < end)  // the next 64 indices (nothing else is in flight here)
-        colv = j + 1 + lane < end ? a.col_idx[j + 1 + lane] : 0;
-      const int ncol = __builtin_amdgcn_readlane(colv, (j + 1 - beg) & 63);
-      if (j + 1 < end) dma_tile<RB>(krs, ncol, koff, Ks, w);
+      lds_barrier();                              // V visible; both waves are done with K
+      if (more) dma_tile<RB>(krs, ncol, koff, Ks, w);  // the next K tile loads during the PV step
       if (kvalid > 0) {
         // O^T += V^T P^T; slot s of lane group g holds key 32c + 16(s/4) + 4g + s%4.
         // The V fragments of d block jd + 1 are read while jd's steps run.
@@ -579,8 +611,15 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
         }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K has landed
-      __syncthreads();                            // next K visible; both waves are done with V
-      if (j + 1 < end) dma_tile<RB>(vrs, ncol, voff, Vs, w);
+      lds_barrier();                              // next K visible; both waves are done with V
+      if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
+        // the next 64 indices; nothing else is in flight at this point
+        colv = j + 2 + lane < end ? a.col_idx[j + 2 + lane] : 0;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      if (more) dma_tile<RB>(vrs, ncol, voff, Vs, w);
+      col = ncol;
+      ncol = __builtin_amdgcn_readlane(colv, (j + 2 - beg) & 63);
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {

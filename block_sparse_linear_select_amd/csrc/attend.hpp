@@ -13,6 +13,8 @@
 // register prefetch overlap the next tile's HBM/L2 reads with the current
 // tile's matrix-core work.
 #pragma once
+
+#include <type_traits>
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -407,18 +409,34 @@ __device__ __forceinline__ i32x4_t make_rsrc_regs(const void* base, int nbytes) 
 // would wait for every such load before a transposing read, whose memory
 // operand carries no alias information); the kernels wait on vmcnt
 // themselves before publishing a buffer.  s_nop covers the M0 hazard.
+// M0 is saved and restored around the load (the compiler keeps no value of
+// its own there across the statement); `imm` is a compile-time byte offset
+// added to the LDS destination.
+template <int IMM = 0>
 __device__ __forceinline__ void lds_dma16(const i32x4_t& rs, const uint8_t* lds_dst, int voff) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t)(lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-               :: "v"(voff), "s"(m0v), "s"(rs) : "memory", "m0");
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(voff), "s"(m0v), "s"(rs), "n"(IMM) : "memory", "scc");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <int RB>
 __device__ __forceinline__ void dma_tile(const i32x4_t& rs, int col, const int* off, uint8_t* dst, int w) {
   constexpr int NI = 64 * RB / 1024 / 2;
   const int base = col * 64 * RB;  // out-of-range columns fall outside the buffer and load zeros
-#pragma unroll
-  for (int i = 0; i < NI; ++i) lds_dma16(rs, dst + 1024 * (NI * w + i), base + off[i]);
+  static_for<0, NI>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    lds_dma16<1024 * i>(rs, dst + 1024 * NI * w, base + off[i]);
+  });
 }
 
 template <int D, int R, bool SPARSE, bool LINEAR>
@@ -679,13 +697,18 @@ static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& 
 // (b, h, 64-token tile, tensor)).  One block = one query tile = 2 waves of 32
 // queries, d = 128.  Kept key tiles are taken in pairs so that one
 // 16x16x128 fp8 matrix-core step contracts over 128 keys:
-//   S = (q8 . k8) * s_q * s_k      (the scales enter the exp2 multiplier)
-//   P' = P * s_v,tile / s_v,ref    (P quantised to fp8 per tile; the ratio
-//                                   enters the exp2 argument, s_v,ref is the
-//                                   largest V scale of the row, so P' <= 256)
-//   O  = s_v,ref * sum P' v8 / sum P
-// V tiles arrive transposed (from the streaming pass) with keys ordered so
-// that lane group g reads its 16 keys of a tile as one 16-byte run.
+//   S = (q8 . k8) * s_q * s_k       (the scales enter the exp2 multiplier)
+//   P'_k = fp8(P_k * s_v,t / s_v,ref)   (s_v,ref: largest V scale of the
+//                                    row's kept tiles, so P' <= 256)
+//   O = s_v,ref * sum_k P'_k v8_k / sum_k P'_k s_v,ref / s_v,t
+// The denominator uses the same rounded P' as the numerator (its per-tile
+// sums come from a matrix-core step against a ones operand), so O is an
+// exact convex combination of the V rows with weights P'_k s_v,ref / s_v,t.
+// V tiles arrive transposed from the streaming pass (d rows of 64 key codes,
+// keys ordered so that lane group g reads its 16 keys of a tile as one
+// 16-byte granule).  Staging, buffers and barriers follow the bf16 kernel:
+// LDS-direct loads into XOR-swizzled unpadded tiles, the next K pair loading
+// during the PV step and the next V pair during the score step.
 // ---------------------------------------------------------------------------
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -708,30 +731,36 @@ __device__ __forceinline__ void codes_to_bf16(Frag<bf16_t>& f, uint32_t lo, uint
   }
 }
 
+// Swizzles of the fp8 tiles: K rows of 128 bytes (two rows per 256-byte bank
+// set), V^T rows of 64 bytes (four rows per bank set); the 16 rows of one
+// 16-byte fragment read land on distinct banks.
+__device__ __forceinline__ int swz_k8(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_v8(int row) { return (row >> 2) & 3; }
+
 template <int R, bool SPARSE, bool LINEAR>
-__global__ __launch_bounds__(128, 1) void k_attend_fp8(AttendArgs a) {
+__global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
   constexpr int D = 128;
   constexpr int NQB = 2;
   constexpr int NDB = D / 16;
-  constexpr int KSTR = D + 16;     // bytes per staged K row
-  constexpr int VSTR = 64 + 16;    // bytes per staged V^T row
-  constexpr int KT = 64 * KSTR;    // bytes per staged K tile
-  constexpr int VTB = D * VSTR;    // bytes per staged V^T tile
-  __shared__ __align__(16) uint8_t lds[SPARSE ? 2 * (KT + VTB) : 16];
+  constexpr int KT = 64 * D;       // bytes of one K tile (64 rows x 128 codes)
+  constexpr int VT = D * 64;       // bytes of one V^T tile (128 rows x 64 codes)
+  constexpr int NI = 2 * KT / 1024 / 2;  // LDS-direct loads per wave per pair (K; the same for V)
+  __shared__ __align__(16) uint8_t Ks[SPARSE ? 2 * KT : 16];
+  __shared__ __align__(16) uint8_t Vs[SPARSE ? 2 * VT : 16];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
   const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.q) + base;
   const uint8_t* K = reinterpret_cast<const uint8_t*>(a.k) + base;
-  const uint8_t* VT = reinterpret_cast<const uint8_t*>(a.vt) + base;  // T*64*D codes per head
+  const uint8_t* VT8 = reinterpret_cast<const uint8_t*>(a.vt) + base;  // T*64*D codes per head
   const int nbytes = a.N * D;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)VT, 0, a.T * 64 * D, kBufferFlags);
+  const i32x4_t krs = make_rsrc_regs(K, nbytes);
+  const i32x4_t vrs = make_rsrc_regs(VT8, a.T * VT);
   const float* SQ = a.qs + (size_t)bh * a.T;
   const float* SK = a.ks + (size_t)bh * a.T;
   const float* SV = a.vs + (size_t)bh * a.T;
@@ -757,148 +786,197 @@ __global__ __launch_bounds__(128, 1) void k_attend_fp8(AttendArgs a) {
   float os[NQB] = {0.f, 0.f};  // final factor s_v,ref / l per query
 
   if constexpr (SPARSE) {
+    if (a.N < 0) { Ks[tid] = 0; Vs[tid] = 0; }  // see the bf16 kernel
     const int beg = a.row_ptr[(size_t)bh * a.T + qa];
     const int end = a.row_ptr[(size_t)bh * a.T + qa + 1];
-    float svref = 0.f;
-    for (int j = beg; j < end; ++j) {
-      const int col = a.col_idx[j];
-      if (col >= 0 && col < a.T) svref = fmaxf(svref, SV[col]);
+    // tile indices and their K and V scales, 64 at a time, one per lane
+    int colv = beg + lane < end ? a.col_idx[beg + lane] : -1;
+    float svv = (colv >= 0 && colv < a.T) ? SV[colv] : 0.f;
+    float skv = (colv >= 0 && colv < a.T) ? SK[colv] : 0.f;
+    float svref = svv;
+    for (int j = beg + 64; j < end; ++j) {  // rows longer than 64 entries
+      const int c = a.col_idx[j];
+      if (c >= 0 && c < a.T) svref = fmaxf(svref, SV[c]);
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) svref = fmaxf(svref, __shfl_xor(svref, o, 64));
     svref = uniform_f(svref);
     const float c0 = sq * a.scale_log2;
     float m[NQB] = {-INFINITY, -INFINITY};
-    float lsum[NQB] = {0.f, 0.f};  // per-lane partial sums of P
-    // prefetch registers for a pair of tiles: 4 K granules + 4 V^T granules per tile
-    u32x4 kr[8], vr[8];
-    auto load_pair = [&](int c0i, int c1i) {
+    f32x4 acc_l[NQB];  // rows 0 and 1 (lane group 0): sums of P' over tile 0 and tile 1 of each pair
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int col = t == 0 ? c0i : c1i;
+    for (int qb = 0; qb < NQB; ++qb) acc_l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum[NQB] = {0.f, 0.f};
+    // exact sums of the unrounded P, kept only for the log-sum-exp output
+    const bool want_lse = a.lse != nullptr;
+    float lex[NQB] = {0.f, 0.f};
+    // ones operand for those sums: row 0 holds 1.0 on tile-0 keys, row 1 on tile-1 keys
+    const uint32_t one4 = 0x38383838u;  // four E4M3 codes of 1.0
+    const i32x8_t onesf = (l16 == 0) ? i32x8_t{(int)one4, (int)one4, (int)one4, (int)one4, 0, 0, 0, 0}
+                        : (l16 == 1) ? i32x8_t{0, 0, 0, 0, (int)one4, (int)one4, (int)one4, (int)one4}
+                                     : i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    // wave w loads tile w of each pair: its K tile and its V^T tile (8 KB each)
+    static_assert(NI * 1024 == KT && KT == VT, "one tile per wave");
+    int koff[NI], voff[NI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = tid + 128 * i;
-          const int krow = q >> 3, kgr = q & 7;   // 64 rows x 8 granules
-          const int vrow = q >> 2, vgr = q & 3;   // 128 rows x 4 granules
-          kr[4 * t + i] = __builtin_amdgcn_raw_buffer_load_b128(krs, (col * 64 + krow) * D + 16 * kgr, 0, 0);
-          vr[4 * t + i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (col * D + vrow) * 64 + 16 * vgr, 0, 0);
-        }
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int lin = 1024 * i + 16 * lane;
+      const int rk = lin / D, pk = (lin % D) / 16;
+      koff[i] = rk * D + 16 * (pk ^ swz_k8(rk));
+      const int rv = lin / 64, pv = (lin % 64) / 16;
+      voff[i] = rv * 64 + 16 * (pv ^ swz_v8(rv));
+    }
+    // col0, col1: the pair's tile indices (-1 for none); out-of-range columns load zeros
+    auto issue_k = [&](int col0, int col1) {
+      const int cb = (w ? col1 : col0) * KT;
+      static_for<0, NI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_dma16<1024 * i>(krs, Ks + KT * w, cb + koff[i]);
+      });
     };
-    auto col_at = [&](int j) { return j < end ? a.col_idx[j] : -1; };
-    if (beg < end) load_pair(col_at(beg), col_at(beg + 1));
+    auto issue_v = [&](int col0, int col1) {
+      const int cb = (w ? col1 : col0) * VT;
+      static_for<0, NI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_dma16<1024 * i>(vrs, Vs + VT * w, cb + voff[i]);
+      });
+    };
+    auto col_at = [&](int j) { return j < end ? __builtin_amdgcn_readlane(colv, (j - beg) & 63) : -1; };
+    // fragment read addresses: K row 16 (kb % 4) + l16 of tile kb / 4, granules 2g and 2g + 1;
+    // V^T row 16 jd + l16 of each tile, granule g
+    const int fk = swz_k8(l16);
+    const int ka0 = l16 * D + 16 * ((2 * g) ^ fk), ka1 = l16 * D + 16 * ((2 * g + 1) ^ fk);
+    const int va = l16 * 64 + 16 * (g ^ swz_v8(l16));
+    int c0i = col_at(beg), c1i = col_at(beg + 1);
+    if (beg < end) {
+      issue_k(c0i, c1i);
+      issue_v(c0i, c1i);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's K share has landed
+      lds_barrier();
+    }
     for (int j = beg; j < end; j += 2) {
-      const int col0 = col_at(j), col1 = col_at(j + 1);
-      __syncthreads();  // the previous pair's reads are done
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = tid + 128 * i;
-          *reinterpret_cast<u32x4*>(&lds[t * KT + (q >> 3) * KSTR + 16 * (q & 7)]) = kr[4 * t + i];
-          *reinterpret_cast<u32x4*>(&lds[2 * KT + t * VTB + (q >> 2) * VSTR + 16 * (q & 3)]) = vr[4 * t + i];
-        }
-      __syncthreads();
-      if (j + 2 < end) load_pair(col_at(j + 2), col_at(j + 3));
-
+      const bool more = j + 2 < end;
       int kv[2];
       float ck[2], lr[2], ir[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int col = t == 0 ? col0 : col1;
+      for (int t = 0; t < 2; ++t) {  // a pair never straddles a block of 64 indices
+        const int col = t == 0 ? c0i : c1i;
         const bool ok = col >= 0 && col < a.T;
         kv[t] = ok ? min(64, a.N - col * 64) : 0;
-        const float sv = ok ? SV[col] : 1.f;
-        ck[t] = ok ? c0 * SK[col] : 0.f;
-        lr[t] = ok ? __log2f(sv / svref) : 0.f;   // P' = P * s_v / s_v,ref
-        ir[t] = ok ? svref / sv : 0.f;
+        const float svf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svv), (j + t - beg) & 63));
+        const float skf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(skv), (j + t - beg) & 63));
+        ck[t] = ok ? c0 * skf : 1.f;  // a missing tile's scores are all -inf: any positive multiplier
+        lr[t] = ok ? __log2f(svf / svref) : 0.f;   // P' = P * s_v / s_v,ref
+        ir[t] = ok ? svref / svf : 0.f;
       }
-      if (kv[0] + kv[1] == 0) continue;  // out-of-range tile indices contribute nothing
-      // S^T = K Q^T over both tiles: key blocks 0..3 from tile 0, 4..7 from tile 1
-      f32x4 s[NQB][8];
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const int t = kb >> 2;
-        const uint8_t* kp = &lds[t * KT + (16 * (kb & 3) + l16) * KSTR + 32 * g];
-        const i32x8_t kf = cat8(*reinterpret_cast<const u32x4*>(kp), *reinterpret_cast<const u32x4*>(kp + 16));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mma_fp8(kf, qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+      if (((j - beg) & 63) == 62 && more) {  // the next pair starts a new block of 64 indices
+        // (only rows longer than 64 entries get here; waits for the loads in flight)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        colv = j + 2 + lane < end ? a.col_idx[j + 2 + lane] : -1;
+        svv = (colv >= 0 && colv < a.T) ? SV[colv] : 0.f;
+        skv = (colv >= 0 && colv < a.T) ? SK[colv] : 0.f;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
-      // scores in log2 units
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[qb][kb][i] *= ck[kb >> 2];
-      if (__builtin_expect(kv[0] < 64 || kv[1] < 64, 0)) {  // keys past N or of a missing tile do not exist
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * (kb & 3) + 4 * g + i >= kv[kb >> 2]) s[qb][kb][i] = -INFINITY;
-      }
-      bool raise = false;
-      float mloc[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-        mloc[qb] = mx;
-        raise |= mx > m[qb] + 8.f;
-      }
-      if (__ballot(raise)) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const float mt = group4_max(mloc[qb]);
-          const float mn = mt > m[qb] + 8.f ? fmaxf(m[qb], mt) : m[qb];
-          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-          m[qb] = mn;
-#pragma unroll
-          for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
-          lsum[qb] *= alpha;
-        }
-      }
-      // P' -> fp8, B operand of the PV step: byte 4 kb + i of lane group g is
-      // key 16 (kb%4) + 4g + i of tile kb/4
+      const int n0 = more ? col_at(j + 2) : -1, n1 = more ? col_at(j + 3) : -1;
+      const bool work = kv[0] + kv[1] > 0;
       i32x8_t pf[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float part[2] = {0.f, 0.f};
+      if (work) {
+        // S^T = K Q^T over both tiles: key blocks 0..3 from tile 0, 4..7 from tile 1
+        f32x4 s[NQB][8];
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-          const int t = kb >> 2;
-          float pv[4];
+          const uint8_t* kp = Ks + (kb >> 2) * KT + 16 * (kb & 3) * D;
+          const i32x8_t kf = cat8(*reinterpret_cast<const u32x4*>(kp + ka0), *reinterpret_cast<const u32x4*>(kp + ka1));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m[qb] + lr[t]);
-            part[t] += pv[i];
-          }
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
-          pf[qb][kb] = wd;
+          for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mma_fp8(kf, qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
         }
-        lsum[qb] += part[0] * ir[0] + part[1] * ir[1];
-      }
-      // O^T += V^T P'^T: lane (dim row, g) reads 16 codes of each tile
+        if (__builtin_expect(kv[0] < 64 || kv[1] < 64, 0)) {  // keys past N or of a missing tile do not exist
 #pragma unroll
-      for (int jd = 0; jd < NDB; ++jd) {
-        const int row = 16 * jd + l16;
-        const i32x8_t vf = cat8(*reinterpret_cast<const u32x4*>(&lds[2 * KT + row * VSTR + 16 * g]),
-                                *reinterpret_cast<const u32x4*>(&lds[2 * KT + VTB + row * VSTR + 16 * g]));
+          for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc_o[qb][jd] = mma_fp8(vf, pf[qb], acc_o[qb][jd]);
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * (kb & 3) + 4 * g + i >= kv[kb >> 2]) s[qb][kb][i] = -INFINITY;
+        }
+        // row max in log2 units from each tile's raw max (the multipliers are positive)
+        bool raise = false;
+        float mloc[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float mt[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 4 * t; kb < 4 * t + 4; ++kb)
+              mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+            mt[t] = kv[t] > 0 ? mx * ck[t] : -INFINITY;
+          }
+          mloc[qb] = fmaxf(mt[0], mt[1]);
+          raise |= mloc[qb] > m[qb] + 8.f;
+        }
+        if (__ballot(raise)) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float mtt = group4_max(mloc[qb]);
+            const float mn = mtt > m[qb] + 8.f ? fmaxf(m[qb], mtt) : m[qb];
+            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+            m[qb] = mn;
+#pragma unroll
+            for (int jd = 0; jd < NDB; ++jd) acc_o[qb][jd] *= alpha;
+            lsum[qb] *= alpha;
+            lex[qb] *= alpha;
+          }
+        }
+        // P' -> fp8, B operand of the PV step: byte 4 kb + i of lane group g is
+        // key 16 (kb % 4) + 4g + i of tile kb / 4
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float b0 = lr[0] - m[qb], b1 = lr[1] - m[qb];
+          float part[2] = {0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const float mul = kb < 4 ? ck[0] : ck[1], add = kb < 4 ? b0 : b1;
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], mul, add));
+            if (__builtin_expect(want_lse, 0)) part[kb >> 2] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+            pf[qb][kb] = wd;
+          }
+          lex[qb] += part[0] * ir[0] + part[1] * ir[1];  // per-lane partial sums of P'; ir undoes the V-scale ratio
+          const f32x4 r = mma_fp8(onesf, pf[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+          lsum[qb] += r[0] * ir[0] + r[1] * ir[1];  // meaningful in lane group 0
+        }
       }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's V share has landed
+      lds_barrier();                              // V visible; both waves are done with K
+      if (more) issue_k(n0, n1);                  // the next K pair loads during the PV step
+      if (work) {
+        // O^T += V^T P'^T: lane (d row, g) reads 16 codes of each tile
+#pragma unroll
+        for (int jd = 0; jd < NDB; ++jd) {
+          const uint8_t* vp = Vs + 16 * jd * 64 + va;
+          const i32x8_t vf = cat8(*reinterpret_cast<const u32x4*>(vp), *reinterpret_cast<const u32x4*>(vp + VT));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) acc_o[qb][jd] = mma_fp8(vf, pf[qb], acc_o[qb][jd]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K pair has landed
+      lds_barrier();                              // next K visible; both waves are done with V
+      if (more) issue_v(n0, n1);
+      c0i = n0;
+      c1i = n1;
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      const float lt = group4_sum(lsum[qb]);
+      const float lt = __shfl(lsum[qb], l16, 64);  // from lane group 0
       os[qb] = lt > 0.f ? svref / lt : 0.f;
-      if (a.lse && g == 0 && qvalid[qb])
-        a.lse[(size_t)bh * a.N_pad + qrow[qb]] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+      const float le = group4_sum(lex[qb]);
+      if (want_lse && g == 0 && qvalid[qb])
+        a.lse[(size_t)bh * a.N_pad + qrow[qb]] = le > 0.f ? (m[qb] + __log2f(le)) * kLn2 : -INFINITY;
     }
   }
 

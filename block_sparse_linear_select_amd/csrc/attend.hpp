@@ -723,12 +723,10 @@ __device__ __forceinline__ i32x8_t cat8(const u32x4& lo, const u32x4& hi) {
 
 // 8 fp8 codes (two dwords) -> bf16 fragment with the exact code values
 __device__ __forceinline__ void codes_to_bf16(Frag<bf16_t>& f, uint32_t lo, uint32_t hi) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = j < 2 ? lo : hi;
-    const int sh = 16 * (j & 1);
-    f.set_pair(j, e4m3_to_f32((w >> sh) & 0xFFu), e4m3_to_f32((w >> (sh + 8)) & 0xFFu));
-  }
+  f.set_pair(0, e4m3_byte<0>(lo), e4m3_byte<1>(lo));
+  f.set_pair(1, e4m3_byte<2>(lo), e4m3_byte<3>(lo));
+  f.set_pair(2, e4m3_byte<0>(hi), e4m3_byte<1>(hi));
+  f.set_pair(3, e4m3_byte<2>(hi), e4m3_byte<3>(hi));
 }
 
 // Swizzles of the fp8 tiles: K rows of 128 bytes (two rows per 256-byte bank

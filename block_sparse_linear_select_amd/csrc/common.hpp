@@ -39,20 +39,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// OCP E4M3FN code -> float (bias 7, subnormals at exponent 0; NaN codes do
-// not occur in valid inputs and decode to a large finite value here).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 24;
-  uint32_t e = (c >> 3) & 0xFu;
-  uint32_t m = c & 0x7u;
-  float mag;
-  if (e == 0) {
-    mag = (float)m * 0.001953125f;  // m/8 * 2^-6
-  } else {
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
-  }
-  return __uint_as_float(__float_as_uint(mag) | s);
-}
+// OCP E4M3FN code -> float with the gfx950 conversion instruction (exact
+// for every finite code; the two NaN codes do not occur in valid inputs).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+// byte `sel` (0..3) of a word of four codes
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL); }
 
 // ---------------------------------------------------------------------------
 // Fragments.  A fragment is what one lane holds of a 16 x 32 operand of a
@@ -129,8 +121,13 @@ __device__ __forceinline__ float elem(const Chunk8<float>& c, int e) {
   }
 }
 __device__ __forceinline__ float elem(const Chunk8<fp8_t>& c, int e) {
-  uint32_t w = (e < 4) ? c.w.x : c.w.y;
-  return e4m3_to_f32((w >> (8 * (e & 3))) & 0xFFu);
+  const uint32_t w = (e < 4) ? c.w.x : c.w.y;
+  switch (e & 3) {
+    case 0: return e4m3_byte<0>(w);
+    case 1: return e4m3_byte<1>(w);
+    case 2: return e4m3_byte<2>(w);
+    default: return e4m3_byte<3>(w);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -27,9 +27,14 @@ inline int rope_entries(const Shape& s) {
   return s.gt * rope_dims(s.rank, 0) / 2 + s.gh * rope_dims(s.rank, 1) / 2 + s.gw * rope_dims(s.rank, 2) / 2;
 }
 
-// Number of token chunks per (b, h) in the streaming pass over K/V.
+// Number of tile chunks per (b, h) in the streaming pass.  The pass runs two
+// 256-thread blocks per CU (512 on the 256 CUs); the chunk count makes the
+// B*H*chunks blocks fill those slots in one round, so that no round runs
+// half empty.
 inline int stream_chunks(const Shape& s) {
-  int c = 32;
+  constexpr int kSlots = 512;
+  int c = kSlots / (s.B * s.H);
+  if (c < 1) c = 1;
   if (c > s.T) c = s.T;
   return c;
 }

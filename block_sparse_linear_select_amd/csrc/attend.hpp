@@ -353,7 +353,6 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 // element (i mod 4) of the 8 bytes addressed by source lane 4t + i/4.
 // ---------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, bounds-checked (gfx9-family dword 3)
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void* lds_void_t;
 

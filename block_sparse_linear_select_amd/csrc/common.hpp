@@ -105,6 +105,27 @@ __device__ __forceinline__ void gload8(Chunk8<float>& c, const float* p) {
   c.a = q[0]; c.b = q[1];
 }
 __device__ __forceinline__ void gload8(Chunk8<fp8_t>& c, const fp8_t* p) { c.w = *reinterpret_cast<const uint2*>(p); }
+// Bounds-checked buffer loads of one chunk: a buffer view covers the valid
+// part of a tensor, and any element offset past it reads as zero.
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, bounds-checked (gfx9-family dword 3)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, nbytes, kBufferFlags);
+}
+__device__ __forceinline__ void bload8(Chunk8<bf16_t>& c, __amdgpu_buffer_rsrc_t r, int elem) {
+  c.w = __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0);
+}
+__device__ __forceinline__ void bload8(Chunk8<fp8_t>& c, __amdgpu_buffer_rsrc_t r, int elem) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, elem, 0, 0);
+  c.w = make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void bload8(Chunk8<float>& c, __amdgpu_buffer_rsrc_t r, int elem) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4, 0, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4 + 16, 0, 0);
+  c.a = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]));
+  c.b = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
+}
+
 __device__ __forceinline__ void zero8(Chunk8<bf16_t>& c) { c.w = u32x4{0, 0, 0, 0}; }
 __device__ __forceinline__ void zero8(Chunk8<float>& c) { c.a = make_float4(0, 0, 0, 0); c.b = c.a; }
 __device__ __forceinline__ void zero8(Chunk8<fp8_t>& c) { c.w = make_uint2(0, 0); }
@@ -145,7 +166,12 @@ __device__ __forceinline__ float group4_sum(float x) {
   return x + wave_xor(x, 32);
 }
 
-__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// elu(x) + 1, without a branch: the exponential of min(x, 0) is always
+// formed (one transcendental op) and selected for x <= 0.
+__device__ __forceinline__ float elu1(float x) {
+  const float e = __expf(fminf(x, 0.f));
+  return x > 0.f ? x + 1.f : e;
+}
 
 // Block order of the query-tile kernels.  The hardware hands block i to XCD
 // i % 8.  All eight XCDs work on the same head at a time, so the key/value

@@ -57,8 +57,10 @@ __device__ __forceinline__ int pack_pos(int tok, int gh, int gw) {
   int h = rem / gw, w = rem - h * gw;
   return (t << 20) | (h << 10) | w;
 }
-__device__ __forceinline__ int pos_axis(int packed, int axis) {
-  return axis == 0 ? (packed >> 20) : (axis == 1 ? ((packed >> 10) & 1023) : (packed & 1023));
+// Value of the neighbouring lane in the pair (2m, 2m + 1): a DPP quad
+// permutation (1, 0, 3, 2), no LDS traffic.
+__device__ __forceinline__ float quad_swap1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
 // ------------------------------------------------------ operand conversions
@@ -200,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   const int r = 16 * rb + l16;
   Frag<OT> uf[D / 32];
   RopeSlot rs;
+  int psh = 0, pmask = 0;
   float zacc = 0.f;
   f32x4 accS[DBW];
   if constexpr (STATE) {
@@ -217,34 +220,28 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
       for (int j = 0; j < 4; ++j) uf[c].set_pair(j, tmp[2 * j], tmp[2 * j + 1]);
     }
     rs = rope_slot(r >> 1, R, a.gt, a.gh);
+    psh = rs.axis == 0 ? 20 : (rs.axis == 1 ? 10 : 0);  // field of the packed position on this axis
+    pmask = rs.axis == 0 ? 0xFFF : 1023;
 #pragma unroll
     for (int j = 0; j < DBW; ++j) accS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // buffer views of this head's valid rows: rows >= N read as zeros
+  const int nbytes = a.N * D * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, nbytes), krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
   Chunk8<T> qc[KCH], kc[KCH], vc[4];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      int row = row0 + i * NCONT;
-      int gr = t * 64 + row;
-      size_t off = (size_t)gr * D + col8 * 8;
-      if (gr < a.N) {
-        gload8(kc[i], K + off);
-        if constexpr (POOL) gload8(qc[i], Q + off);
-      } else {
-        zero8(kc[i]);
-        if constexpr (POOL) zero8(qc[i]);
-      }
+      const int e = (t * 64 + row0 + i * NCONT) * D + col8 * 8;
+      bload8(kc[i], krs, e);
+      if constexpr (POOL) bload8(qc[i], qrs, e);
     }
     if constexpr (STATE) {
       if (tid < NVU) {
-        int kg = tid % 16, c8 = tid / 16;
+        const int kg = tid % 16, c8 = tid / 16;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          int gr = t * 64 + 4 * kg + ii;
-          if (gr < a.N) gload8(vc[ii], V + (size_t)gr * D + c8 * 8);
-          else zero8(vc[ii]);
-        }
+        for (int ii = 0; ii < 4; ++ii) bload8(vc[ii], vrs, (t * 64 + 4 * kg + ii) * D + c8 * 8);
       }
     }
   };
@@ -307,12 +304,13 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
       for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int tok = 16 * tb + 4 * g + i;
-          float phi = (t * 64 + tok < a.N) ? elu1(accF[tb][i] * sk) : 0.f;
+          const int tok = 16 * tb + 4 * g + i;
+          const float e1 = elu1(accF[tb][i] * sk);
+          const float phi = (t * 64 + tok < a.N) ? e1 : 0.f;
           zacc += phi;
-          float other = __shfl_xor(phi, 1, 64);
-          int pa = pos_axis(spos[tok], rs.axis);
-          float2 cs = a.rope[rs.off + pa * rs.half + rs.m];
+          const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
+          const int pa = (spos[tok] >> psh) & pmask;
+          const float2 cs = a.rope[rs.off + pa * rs.half + rs.m];
           float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
           kp[tb][i] = rot * sv;
         }

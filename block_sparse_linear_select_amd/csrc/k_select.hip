@@ -91,11 +91,12 @@ __device__ __forceinline__ uint64_t order_key(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row
+constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row (keys per lane: MJ <= kMaxJ)
 
 // One wave per row: radix-select the k-th largest key (8 passes of 8 bits),
 // keep every key above it and the lowest-index keys equal to it, add the
 // diagonal if forced, and write the kept tiles in ascending order.
+template <int MJ>  // keys per lane held in registers: T <= 64 * MJ
 __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int force_diag, int direct,
                                               const double* __restrict__ scores, int32_t* __restrict__ out_cols,
                                               int32_t* __restrict__ out_cnt, int32_t* __restrict__ row_ptr) {
@@ -107,9 +108,9 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   const double* src = scores + (size_t)(live ? row : 0) * T;
   const int nj = (T + 63) / 64;
 
-  uint64_t key[kMaxJ];
+  uint64_t key[MJ];
 #pragma unroll
-  for (int j = 0; j < kMaxJ; ++j) {
+  for (int j = 0; j < MJ; ++j) {
     int b = lane + 64 * j;
     key[j] = (j < nj && b < T && live) ? order_key(src[b]) : 0ull;
   }
@@ -131,19 +132,19 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   {
     uint32_t pend = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxJ; ++j)
+    for (int j = 0; j < MJ; ++j)
       if (j < nj && key[j] != 0ull) pend |= 1u << j;
     int cum = 0, digit = 0, dcnt = 0;
     for (;;) {
       int dl = -1;
 #pragma unroll
-      for (int j = 0; j < kMaxJ; ++j)
+      for (int j = 0; j < MJ; ++j)
         if ((pend >> j) & 1u) dl = max(dl, (int)(key[j] >> 56));
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) dl = max(dl, __shfl_xor(dl, off, 64));
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < kMaxJ; ++j) {
+      for (int j = 0; j < MJ; ++j) {
         if (j < nj) {
           const bool hit = ((pend >> j) & 1u) && (int)(key[j] >> 56) == dl;
           cnt += __popcll(__ballot(hit));
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < kMaxJ; ++j)
+    for (int j = 0; j < MJ; ++j)
       if (j < nj && (key[j] & mask) == prefix && key[j] != 0ull)
         atomicAdd(&hw[(key[j] >> shift) & 255u], 1u);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   int taken = 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int j = 0; j < kMaxJ; ++j) {
+  for (int j = 0; j < MJ; ++j) {
     if (j < nj) {  // nj is wave-uniform; a guard instead of a break keeps key[] in registers
       const bool above = key[j] > kth;
       const bool eq = key[j] == kth && key[j] != 0ull;
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
   int base_pos = 0;
   const size_t obase = direct ? (size_t)row * topk : (size_t)row * (topk + 1);
 #pragma unroll
-  for (int j = 0; j < kMaxJ; ++j) {
+  for (int j = 0; j < MJ; ++j) {
     if (j < nj) {
       const bool s = (sel >> j) & 1u;
       const uint64_t bs = __ballot(s);
@@ -289,8 +290,12 @@ hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32
   const int rows = s.B * s.H * s.T;
   hipError_t e;
   const int direct = s.force_diag ? 0 : 1;
-  k_topk<<<(rows + 3) / 4, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores,
-                                         direct ? col_idx : w.sel_tmp, w.sel_cnt, row_ptr);
+  int32_t* cols = direct ? col_idx : w.sel_tmp;
+  const int nj = (s.T + 63) / 64, grid = (rows + 3) / 4;
+  if (nj <= 8) k_topk<8><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
+  else if (nj <= 16) k_topk<16><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
+  else if (nj <= 20) k_topk<20><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
+  else k_topk<kMaxJ><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
   e = hipGetLastError();
   if (e != hipSuccess || direct) return e;
   k_scan<<<1, 1024, 0, st>>>(rows, w.sel_cnt, row_ptr);

@@ -1,17 +1,19 @@
-// Query-tile kernel: block-sparse flash attention over the kept key tiles,
+// Query-tile kernels: block-sparse flash attention over the kept key tiles,
 // followed by the readout of the rotary low-rank linear branch, both summed in
 // one epilogue (SparkDiffusion news article, section 05: the sparse branch
 // keeps the high-energy tile interactions, the linear branch restores the
 // global context).
 //
-// One block = one (b, h, query tile) = 64 queries, 4 waves of 16 queries.
-// Scores are formed transposed, S^T = K Q^T, so that each lane owns one query
-// column: the softmax max/sum run mostly in-lane, and the score accumulator
-// already sits in the operand layout of P^T for O^T += V^T P^T.  K tiles are
-// staged row-major in LDS; V tiles transposed, with keys permuted inside
-// every 32-key chunk to match that operand layout.  Two LDS stages and a
-// register prefetch overlap the next tile's HBM/L2 reads with the current
-// tile's matrix-core work.
+// Common to all three kernels: scores are formed transposed, S^T = K Q^T, so
+// that each lane owns one query column (the softmax max and sum run mostly
+// in-lane) and the score accumulator already sits in the operand layout of P^T
+// for O^T += V^T P^T.
+//  * k_attend<float>: the float32 kernel (4 waves of 16 queries, K staged
+//    row-major and V transposed in LDS, two stages).
+//  * k_attend_bf16: 2 waves of 32 queries, K/V tiles moved global -> LDS by
+//    LDS-direct loads into XOR-swizzled tiles, V operands by transposing reads.
+//  * k_attend_fp8: the same staging over pairs of kept tiles, 16x16x128 fp8
+//    matrix-core steps, per-tile scales folded into the exp2 argument.
 #pragma once
 
 #include <type_traits>

@@ -15,6 +15,7 @@
 // loads, the next tile is prefetched into registers while the current one is
 // processed, and all arithmetic runs from LDS and registers.
 #pragma once
+#include <type_traits>
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -57,6 +58,8 @@ __device__ __forceinline__ int pack_pos(int tok, int gh, int gw) {
   int h = rem / gw, w = rem - h * gw;
   return (t << 20) | (h << 10) | w;
 }
+typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
+
 // Value of the neighbouring lane in the pair (2m, 2m + 1): a DPP quad
 // permutation (1, 0, 3, 2), no LDS traffic.
 __device__ __forceinline__ float quad_swap1(float x) {
@@ -169,6 +172,10 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   constexpr int NVU = 16 * CPR;           // V units (4 keys x 8 dims)
   constexpr int KSTR = D + 8;             // LDS row stride of K (elements)
   constexpr int VSTR = 64 + 8;            // LDS row stride of V^T
+  // bf16 inputs keep V row-major in LDS and read V^T operands with
+  // transposing reads; the other types stage V transposed
+  constexpr bool VROW = std::is_same<T, bf16_t>::value;
+  constexpr int VRS = D + 16;             // LDS row stride of row-major V (rows 8 banks apart)
   constexpr int NRB = R / 16;             // 16-wide blocks of the rank
   constexpr int NDG = 4 / NRB;            // waves sharing an r block
   constexpr int DBW = (D / 16) / NDG;     // 16-wide d blocks per wave
@@ -176,7 +183,8 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
 
   __shared__ __align__(16) OT Ks[STATE ? 64 * KSTR : 1];
-  __shared__ __align__(16) OT Vt[STATE ? D * VSTR : 1];
+  __shared__ __align__(16) OT Vt[(STATE && !VROW) ? D * VSTR : 1];
+  __shared__ __align__(16) OT Vr[(STATE && VROW) ? 64 * VRS : 1];
   __shared__ __align__(16) uint8_t Vt8[(STATE && sizeof(T) == 1) ? D * 80 : 16];  // fp8 V^T tile for the sparse kernel
   __shared__ double redq[POOL ? NCONT * D : 1];
   __shared__ double redk[POOL ? NCONT * D : 1];
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   // buffer views of this head's valid rows: rows >= N read as zeros
   const int nbytes = a.N * D * (int)sizeof(T);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, nbytes), krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
-  Chunk8<T> qc[KCH], kc[KCH], vc[4];
+  Chunk8<T> qc[KCH], kc[KCH], vc[VROW ? KCH : 4];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
@@ -237,7 +245,10 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
       bload8(kc[i], krs, e);
       if constexpr (POOL) bload8(qc[i], qrs, e);
     }
-    if constexpr (STATE) {
+    if constexpr (STATE && VROW) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) bload8(vc[i], vrs, (t * 64 + row0 + i * NCONT) * D + col8 * 8);
+    } else if constexpr (STATE) {
       if (tid < NVU) {
         const int kg = tid % 16, c8 = tid / 16;
 #pragma unroll
@@ -266,7 +277,10 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
     if constexpr (STATE) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Ks[(row0 + i * NCONT) * KSTR + col8 * 8], kc[i]);
-      if (tid < NVU) {
+      if constexpr (VROW) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Vr[(row0 + i * NCONT) * VRS + col8 * 8], vc[i]);
+      } else if (tid < NVU) {
         int kg = tid % 16, c8 = tid / 16;
         int p0 = vt_pos(4 * kg);
 #pragma unroll
@@ -329,7 +343,20 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           Frag<OT> vf;
-          load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
+          if constexpr (VROW) {
+            // slot s of lane group g holds token 32c + 16(s/4) + 4g + s%4 (as kf2)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = 32 * c + 16 * hh + 4 * g + (l16 >> 2), col = 16 * db + 4 * (l16 & 3);
+              typedef __attribute__((address_space(3))) s16x4_lds_t s16x4_as3;
+              const s16x4_lds_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_as3*)(&Vr[row * VRS + col]));
+              const uint2 u = __builtin_bit_cast(uint2, t4);
+              vf.w[2 * hh] = u.x;
+              vf.w[2 * hh + 1] = u.y;
+            }
+          } else {
+            load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
+          }
           mma(accS[j], vf, kf2[c]);
         }
       }

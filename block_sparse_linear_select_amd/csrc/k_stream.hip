@@ -23,6 +23,7 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
   a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
   a.qbarT = w.qbarT; a.kbarT = w.kbarT; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
   a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope; a.vt = w.vt;
+  a.nrope = rope_entries(s);
   switch (s.dt) {
     case Dt::F32: return launch_stream_f32(s, a, pool, state, st);
     case Dt::BF16: return stream_by_shape<bf16_t, bf16_t>(s, a, pool, state, st);

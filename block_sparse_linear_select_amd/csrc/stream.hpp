@@ -161,10 +161,16 @@ struct StreamArgs {
   float* part_s;
   float* part_z;
   const float2* rope;
+  int nrope;  // RoPE table entries
   void* vt;  // optional: V tiles transposed, [BH][T][d][64] with keys permuted as in LDS
 };
 
-template <typename T, typename OT, int D, int R, bool POOL, bool STATE>
+// RoPE tables up to this many entries (11.5 KB at 720P, rank 64) are staged
+// in LDS once per block, so the per-token lookups are LDS reads (bf16 inputs;
+// two blocks per CU still fit).
+constexpr int kRopeLdsMax = 1536;
+
+template <typename T, typename OT, int D, int R, bool POOL, bool STATE, bool RLDS = false>
 __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   constexpr int CPR = D / 8;              // 8-element chunks per row
   constexpr int NCONT = 256 / CPR;        // threads sharing a column chunk
@@ -189,6 +195,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   __shared__ double redq[POOL ? NCONT * D : 1];
   __shared__ double redk[POOL ? NCONT * D : 1];
   __shared__ int spos[64];
+  __shared__ float2 rtab[RLDS ? kRopeLdsMax : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -228,6 +235,9 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
       for (int j = 0; j < 4; ++j) uf[c].set_pair(j, tmp[2 * j], tmp[2 * j + 1]);
     }
     rs = rope_slot(r >> 1, R, a.gt, a.gh);
+    if constexpr (RLDS) {
+      for (int i = tid; i < a.nrope; i += 256) rtab[i] = a.rope[i];  // published by the loop's first barrier
+    }
     psh = rs.axis == 0 ? 20 : (rs.axis == 1 ? 10 : 0);  // field of the packed position on this axis
     pmask = rs.axis == 0 ? 0xFFF : 1023;
 #pragma unroll
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           zacc += phi;
           const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
           const int pa = (spos[tok] >> psh) & pmask;
-          const float2 cs = a.rope[rs.off + pa * rs.half + rs.m];
+          const float2 cs = RLDS ? rtab[rs.off + pa * rs.half + rs.m] : a.rope[rs.off + pa * rs.half + rs.m];
           float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
           kp[tb][i] = rot * sv;
         }
@@ -513,8 +523,12 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
 template <typename T, typename OT, int D, int R>
 static hipError_t stream_dispatch(const Shape& s, const StreamArgs& a, bool pool, bool state, hipStream_t st) {
   dim3 grid(a.nchunk, s.B * s.H);
-  if (pool && state) k_stream<T, OT, D, R, true, true><<<grid, 256, 0, st>>>(a);
+  // (the fp8 variant's LDS is already full with its two V^T tiles)
+  const bool rlds = a.nrope <= kRopeLdsMax && std::is_same<T, bf16_t>::value;
+  if (pool && state && rlds) k_stream<T, OT, D, R, true, true, true><<<grid, 256, 0, st>>>(a);
+  else if (pool && state) k_stream<T, OT, D, R, true, true><<<grid, 256, 0, st>>>(a);
   else if (pool) k_stream<T, OT, D, R, true, false><<<grid, 256, 0, st>>>(a);
+  else if (rlds) k_stream<T, OT, D, R, false, true, true><<<grid, 256, 0, st>>>(a);
   else k_stream<T, OT, D, R, false, true><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -247,145 +247,155 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   // buffer views of this head's valid rows: rows >= N read as zeros
   const int nbytes = a.N * D * (int)sizeof(T);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, nbytes), krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
-  Chunk8<T> qc[KCH], kc[KCH], vc[VROW ? KCH : 4];
-  auto load_tile = [&](int t) {
+  // Two tiles in flight per block: while tile t is processed from one
+  // register set, tile t + 1 is already loading into the other, and tile t + 2
+  // is issued into the first set once tile t sits in LDS.
+  struct TileRegs { Chunk8<T> q[KCH], k[KCH], v[VROW ? KCH : 4]; };
+  TileRegs tra, trb;
+  auto load_tile = [&](int t, TileRegs& c) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int e = (t * 64 + row0 + i * NCONT) * D + col8 * 8;
-      bload8(kc[i], krs, e);
-      if constexpr (POOL) bload8(qc[i], qrs, e);
+      bload8(c.k[i], krs, e);
+      if constexpr (POOL) bload8(c.q[i], qrs, e);
     }
     if constexpr (STATE && VROW) {
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) bload8(vc[i], vrs, (t * 64 + row0 + i * NCONT) * D + col8 * 8);
+      for (int i = 0; i < KCH; ++i) bload8(c.v[i], vrs, (t * 64 + row0 + i * NCONT) * D + col8 * 8);
     } else if constexpr (STATE) {
       if (tid < NVU) {
         const int kg = tid % 16, c8 = tid / 16;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) bload8(vc[ii], vrs, (t * 64 + 4 * kg + ii) * D + c8 * 8);
+        for (int ii = 0; ii < 4; ++ii) bload8(c.v[ii], vrs, (t * 64 + 4 * kg + ii) * D + c8 * 8);
       }
     }
   };
 
-  load_tile(t0);
-  for (int t = t0; t < t1; ++t) {
-    // ---- registers -> LDS
-    if constexpr (POOL) {
-      double pq[8], pk[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { pq[e] = 0.0; pk[e] = 0.0; }
-#pragma unroll
-      for (int i = 0; i < KCH; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pq[e] += (double)elem(qc[i], e); pk[e] += (double)elem(kc[i], e); }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        redq[row0 * D + col8 * 8 + e] = pq[e];
-        redk[row0 * D + col8 * 8 + e] = pk[e];
+  auto process = [&](int t, TileRegs& c) {
+      // ---- registers -> LDS
+      if constexpr (POOL) {
+        double pq[8], pk[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) { pq[e] = 0.0; pk[e] = 0.0; }
+  #pragma unroll
+        for (int i = 0; i < KCH; ++i)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) { pq[e] += (double)elem(c.q[i], e); pk[e] += (double)elem(c.k[i], e); }
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          redq[row0 * D + col8 * 8 + e] = pq[e];
+          redk[row0 * D + col8 * 8 + e] = pk[e];
+        }
       }
-    }
-    if constexpr (STATE) {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Ks[(row0 + i * NCONT) * KSTR + col8 * 8], kc[i]);
-      if constexpr (VROW) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Vr[(row0 + i * NCONT) * VRS + col8 * 8], vc[i]);
-      } else if (tid < NVU) {
-        int kg = tid % 16, c8 = tid / 16;
-        int p0 = vt_pos(4 * kg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(vc[0], e), elem(vc[1], e), elem(vc[2], e), elem(vc[3], e));
+      if constexpr (STATE) {
+  #pragma unroll
+        for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Ks[(row0 + i * NCONT) * KSTR + col8 * 8], c.k[i]);
+        if constexpr (VROW) {
+  #pragma unroll
+          for (int i = 0; i < KCH; ++i) Conv<T, OT>::row(&Vr[(row0 + i * NCONT) * VRS + col8 * 8], c.v[i]);
+        } else if (tid < NVU) {
+          int kg = tid % 16, c8 = tid / 16;
+          int p0 = vt_pos(4 * kg);
+  #pragma unroll
+          for (int e = 0; e < 8; ++e)
+            st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(c.v[0], e), elem(c.v[1], e), elem(c.v[2], e), elem(c.v[3], e));
+        }
+        if (tid < 64) spos[tid] = pack_pos(min(t * 64 + tid, a.N - 1), a.gh, a.gw);
+        if constexpr (sizeof(T) == 1) {
+          if (a.vt && tid < NVU) stage_vt8(Vt8, tid, c.v);
+        }
       }
-      if (tid < 64) spos[tid] = pack_pos(min(t * 64 + tid, a.N - 1), a.gh, a.gw);
-      if constexpr (sizeof(T) == 1) {
-        if (a.vt && tid < NVU) stage_vt8(Vt8, tid, vc);
+      __syncthreads();
+      if (t + 2 < t1) load_tile(t + 2, c);
+      if constexpr (STATE && sizeof(T) == 1) {
+        // hand the transposed fp8 tile to the sparse kernel
+        if (a.vt) write_vt8(reinterpret_cast<uint8_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64, Vt8, tid);
       }
-    }
-    __syncthreads();
-    if (t + 1 < t1) load_tile(t + 1);
-    if constexpr (STATE && sizeof(T) == 1) {
-      // hand the transposed fp8 tile to the sparse kernel
-      if (a.vt) write_vt8(reinterpret_cast<uint8_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64, Vt8, tid);
-    }
 
-    if constexpr (STATE) {
-      const float sk = a.ks ? a.ks[(size_t)bh * a.T + t] : 1.f;
-      const float sv = a.vs ? a.vs[(size_t)bh * a.T + t] : 1.f;
-      f32x4 accF[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        accF[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          Frag<OT> kf;
-          load8(kf, &Ks[(16 * tb + l16) * KSTR + 32 * c + 8 * g]);
-          mma(accF[tb], kf, uf[c]);
-        }
-      }
-      float kp[4][4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * tb + 4 * g + i;
-          const float e1 = elu1(accF[tb][i] * sk);
-          const float phi = (t * 64 + tok < a.N) ? e1 : 0.f;
-          zacc += phi;
-          const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
-          const int pa = (spos[tok] >> psh) & pmask;
-          const float2 cs = RLDS ? rtab[rs.off + pa * rs.half + rs.m] : a.rope[rs.off + pa * rs.half + rs.m];
-          float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
-          kp[tb][i] = rot * sv;
-        }
-      }
-      Frag<OT> kf2[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        kf2[c].set_pair(0, kp[2 * c][0], kp[2 * c][1]);
-        kf2[c].set_pair(1, kp[2 * c][2], kp[2 * c][3]);
-        kf2[c].set_pair(2, kp[2 * c + 1][0], kp[2 * c + 1][1]);
-        kf2[c].set_pair(3, kp[2 * c + 1][2], kp[2 * c + 1][3]);
-      }
-#pragma unroll
-      for (int j = 0; j < DBW; ++j) {
-        int db = dg * DBW + j;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          Frag<OT> vf;
-          if constexpr (VROW) {
-            // slot s of lane group g holds token 32c + 16(s/4) + 4g + s%4 (as kf2)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int row = 32 * c + 16 * hh + 4 * g + (l16 >> 2), col = 16 * db + 4 * (l16 & 3);
-              typedef __attribute__((address_space(3))) s16x4_lds_t s16x4_as3;
-              const s16x4_lds_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_as3*)(&Vr[row * VRS + col]));
-              const uint2 u = __builtin_bit_cast(uint2, t4);
-              vf.w[2 * hh] = u.x;
-              vf.w[2 * hh + 1] = u.y;
-            }
-          } else {
-            load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
+      if constexpr (STATE) {
+        const float sk = a.ks ? a.ks[(size_t)bh * a.T + t] : 1.f;
+        const float sv = a.vs ? a.vs[(size_t)bh * a.T + t] : 1.f;
+        f32x4 accF[4];
+  #pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          accF[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            Frag<OT> kf;
+            load8(kf, &Ks[(16 * tb + l16) * KSTR + 32 * c + 8 * g]);
+            mma(accF[tb], kf, uf[c]);
           }
-          mma(accS[j], vf, kf2[c]);
+        }
+        float kp[4][4];
+  #pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * tb + 4 * g + i;
+            const float e1 = elu1(accF[tb][i] * sk);
+            const float phi = (t * 64 + tok < a.N) ? e1 : 0.f;
+            zacc += phi;
+            const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
+            const int pa = (spos[tok] >> psh) & pmask;
+            const float2 cs = RLDS ? rtab[rs.off + pa * rs.half + rs.m] : a.rope[rs.off + pa * rs.half + rs.m];
+            float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
+            kp[tb][i] = rot * sv;
+          }
+        }
+        Frag<OT> kf2[2];
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          kf2[c].set_pair(0, kp[2 * c][0], kp[2 * c][1]);
+          kf2[c].set_pair(1, kp[2 * c][2], kp[2 * c][3]);
+          kf2[c].set_pair(2, kp[2 * c + 1][0], kp[2 * c + 1][1]);
+          kf2[c].set_pair(3, kp[2 * c + 1][2], kp[2 * c + 1][3]);
+        }
+  #pragma unroll
+        for (int j = 0; j < DBW; ++j) {
+          int db = dg * DBW + j;
+  #pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            Frag<OT> vf;
+            if constexpr (VROW) {
+              // slot s of lane group g holds token 32c + 16(s/4) + 4g + s%4 (as kf2)
+  #pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const int row = 32 * c + 16 * hh + 4 * g + (l16 >> 2), col = 16 * db + 4 * (l16 & 3);
+                typedef __attribute__((address_space(3))) s16x4_lds_t s16x4_as3;
+                const s16x4_lds_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_as3*)(&Vr[row * VRS + col]));
+                const uint2 u = __builtin_bit_cast(uint2, t4);
+                vf.w[2 * hh] = u.x;
+                vf.w[2 * hh + 1] = u.y;
+              }
+            } else {
+              load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
+            }
+            mma(accS[j], vf, kf2[c]);
+          }
         }
       }
-    }
-    if constexpr (POOL) {
-      if (tid < D) {
-        double sq = 0.0, sk2 = 0.0;
-        for (int c = 0; c < NCONT; ++c) { sq += redq[c * D + tid]; sk2 += redk[c * D + tid]; }
-        const double cnt = (double)min(64, a.N - t * 64);
-        if (a.qs) sq *= (double)a.qs[(size_t)bh * a.T + t];
-        if (a.ks) sk2 *= (double)a.ks[(size_t)bh * a.T + t];
-        const double mq = sq / cnt, mk = sk2 / cnt;
-        a.qbarT[((size_t)bh * D + tid) * a.T + t] = mq;
-        a.kbarT[((size_t)bh * D + tid) * a.T + t] = mk;
-        if (a.qbar_out) a.qbar_out[((size_t)bh * a.T + t) * D + tid] = mq;
-        if (a.kbar_out) a.kbar_out[((size_t)bh * a.T + t) * D + tid] = mk;
+      if constexpr (POOL) {
+        if (tid < D) {
+          double sq = 0.0, sk2 = 0.0;
+          for (int c = 0; c < NCONT; ++c) { sq += redq[c * D + tid]; sk2 += redk[c * D + tid]; }
+          const double cnt = (double)min(64, a.N - t * 64);
+          if (a.qs) sq *= (double)a.qs[(size_t)bh * a.T + t];
+          if (a.ks) sk2 *= (double)a.ks[(size_t)bh * a.T + t];
+          const double mq = sq / cnt, mk = sk2 / cnt;
+          a.qbarT[((size_t)bh * D + tid) * a.T + t] = mq;
+          a.kbarT[((size_t)bh * D + tid) * a.T + t] = mk;
+          if (a.qbar_out) a.qbar_out[((size_t)bh * a.T + t) * D + tid] = mq;
+          if (a.kbar_out) a.kbar_out[((size_t)bh * a.T + t) * D + tid] = mk;
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
+  };
+
+  load_tile(t0, tra);
+  if (t0 + 1 < t1) load_tile(t0 + 1, trb);
+  for (int t = t0; t < t1; t += 2) {
+    process(t, tra);
+    if (t + 1 < t1) process(t + 1, trb);
   }
 
   if constexpr (STATE) {

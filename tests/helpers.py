@@ -27,6 +27,10 @@ CASES = {
     "fp8_ragged": make_workload("wan14b_720p_fp8", B=2, H=3, grid=(3, 10, 13), topk=3, rank=32, seed=21),
     "fp8_r64_diag": make_workload("wan14b_720p_fp8", H=2, grid=(5, 12, 20), topk=4, force_diag=True,
                                   rank=64, seed=23),
+    # rows of more than 64 (and 128) kept tiles: the kernels hold a row's tile
+    # indices 64 at a time and reload them mid-row
+    "bf16_long_rows": make_workload("wan14b_480p_bf16", H=1, grid=(3, 40, 70), topk=130, rank=32, seed=31),
+    "fp8_long_rows": make_workload("wan14b_720p_fp8", H=1, grid=(3, 40, 70), topk=129, rank=32, seed=33),
 }
 
 

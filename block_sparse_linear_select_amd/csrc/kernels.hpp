@@ -30,13 +30,16 @@ inline int rope_entries(const Shape& s) {
 // Number of tile chunks per (b, h) in the streaming pass.  The pass runs two
 // 256-thread blocks per CU (512 on the 256 CUs); the chunk count makes the
 // B*H*chunks blocks fill those slots in one round, so that no round runs
-// half empty.
+// half empty.  Chunks hold ceil(T / c) tiles each, and the count is then cut
+// to the chunks that hold any tile: every chunk writes its partial state,
+// which the finalize step sums over all of them.
 inline int stream_chunks(const Shape& s) {
   constexpr int kSlots = 512;
   int c = kSlots / (s.B * s.H);
   if (c < 1) c = 1;
   if (c > s.T) c = s.T;
-  return c;
+  const int per = (s.T + c - 1) / c;
+  return (s.T + per - 1) / per;
 }
 
 // Device scratch of one call, carved out of the caller's workspace.

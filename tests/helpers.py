@@ -31,6 +31,11 @@ CASES = {
     # indices 64 at a time and reload them mid-row
     "bf16_long_rows": make_workload("wan14b_480p_bf16", H=1, grid=(3, 40, 70), topk=130, rank=32, seed=31),
     "fp8_long_rows": make_workload("wan14b_720p_fp8", H=1, grid=(3, 40, 70), topk=129, rank=32, seed=33),
+    # 16 heads of 36 tiles: the streaming pass gives each block two tiles
+    # (chunks of several tiles, some chunk counts not dividing T)
+    "bf16_many_heads": make_workload("wan14b_480p_bf16", B=2, H=8, grid=(2, 6, 190), topk=3, force_diag=True,
+                                     rank=32, seed=41),
+    "fp8_many_heads": make_workload("wan14b_720p_fp8", B=2, H=8, grid=(2, 6, 190), topk=4, rank=64, seed=43),
 }
 
 

@@ -135,6 +135,36 @@ def test_runs_are_bitwise_reproducible(case):
     assert torch.equal(ci1[:n], ci2[:n])
 
 
+def test_workspace_contents_do_not_matter(case, monkeypatch):
+    """Every call gives bitwise the same result whether its workspace starts
+    as zeros or as all-ones bytes (NaN as floats): no kernel reads scratch
+    memory that an earlier step of the same call has not written."""
+    name, inp, d, ref, heads = case
+    w = inp.w
+    cfg = _cfg(w)
+    rp, ci = Hp.csr_tensors([ref[bh]["rows"] for bh in heads], DEV)
+    args = (d["q_scale"], d["k_scale"], d["v_scale"])
+
+    def run(fill):
+        monkeypatch.setattr(B, "_workspace", lambda c, call, dev: torch.full(
+            (max(B.workspace_size(c, call), 256),), fill, dtype=torch.uint8, device=dev))
+        out = [B.hybrid_attn(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], *args, export_mask=True),
+               B.hybrid_attn(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], *args, row_ptr=rp, col_idx=ci),
+               B.sparse_attn(cfg, d["q"], d["k"], d["v"], rp, ci, *args, want_lse=True),
+               B.linear_attn(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], *args),
+               B.block_select(cfg, d["q"], d["k"], args[0], args[1], want_means=True)]
+        torch.cuda.synchronize()
+        (o, rpo, cio), bs = out[0], out[4]
+        n, nb = int(rpo[-1]), int(bs[0][-1])  # entries past the last row are unused capacity
+        lse = out[2][1][..., :w.N]  # rows past N are left unwritten
+        flat = [o, rpo, cio[:n], out[1], out[2][0], lse, out[3], bs[0], bs[1][:nb], bs[2], bs[3]]
+        return [t.clone() for t in flat]
+
+    zeros, ones = run(0), run(255)
+    for i, (x, y) in enumerate(zip(zeros, ones)):
+        assert torch.equal(x, y), f"output {i} depends on the workspace contents"
+
+
 # ---------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("name", ["bf16_ragged", "fp8_ragged"])
 def test_given_csr_with_empty_row_and_out_of_range_columns(name):

@@ -35,8 +35,8 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   if (select) {
-    p.off_qbarT = take(bh * s.d * s.T * sizeof(double));
-    p.off_kbarT = take(bh * s.d * s.T * sizeof(double));
+    p.off_qmean = take(bh * s.d * s.T * sizeof(double));
+    p.off_kmean = take(bh * s.d * s.T * sizeof(double));
     p.off_scores = take(bh * (size_t)s.T * s.T * sizeof(double));
     if (s.force_diag) {
       p.off_sel_tmp = take(rows * (s.topk + 1) * sizeof(int32_t));
@@ -67,8 +67,8 @@ Scratch bind_plan(const Plan& p, void* ws) {
   Scratch w;
   char* b = static_cast<char*>(ws);
   if (p.select) {
-    w.qbarT = reinterpret_cast<double*>(b + p.off_qbarT);
-    w.kbarT = reinterpret_cast<double*>(b + p.off_kbarT);
+    w.qmean = reinterpret_cast<double*>(b + p.off_qmean);
+    w.kmean = reinterpret_cast<double*>(b + p.off_kmean);
     w.scores = reinterpret_cast<double*>(b + p.off_scores);
     w.sel_tmp = reinterpret_cast<int32_t*>(b + p.off_sel_tmp);
     w.sel_cnt = reinterpret_cast<int32_t*>(b + p.off_sel_cnt);

@@ -14,43 +14,49 @@ namespace hsa {
 // -------------------------------------------------------------- scores
 // sigma[a][b] = qbar_a . kbar_b for one (b, h), float64 16x16x4 matrix-core
 // steps.  Block: 4 waves x 16 rows = 64 rows of a; the column means are
-// staged 32 columns at a time through double-buffered LDS (row stride 40
-// doubles, which puts the four lane groups of a read on distinct banks), and
-// each wave runs two independent accumulator chains.  Means are stored
-// transposed ([d][T]) so both the A operands and the staging loads read
-// consecutive tiles.
+// staged 32 columns at a time through double-buffered LDS, and each wave runs
+// two independent accumulator chains.  Means are stored one row per tile
+// ([T][d]): a chunk of 32 column means is one contiguous block, loaded
+// coalesced and kept in LDS with row stride d + 4 doubles (the 16 rows x 4
+// dims of an operand read then spread over all banks).
 constexpr int kScoreCols = 32;
-constexpr int kScoreStride = 40;
 
 template <int D>
-__global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict__ qbarT,
-                                                const double* __restrict__ kbarT, double* __restrict__ scores) {
-  __shared__ double kbuf[2][D * kScoreStride];
+__global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict__ qmean,
+                                                const double* __restrict__ kmean, double* __restrict__ scores) {
+  constexpr int CS = D + 4;  // LDS row stride (doubles) of a staged column mean
+  __shared__ double kbuf[2][kScoreCols * CS];
   const int bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const double* qb = qbarT + (size_t)bh * D * T;
-  const double* kb = kbarT + (size_t)bh * D * T;
+  const double* qb = qmean + (size_t)bh * T * D;
+  const double* kb = kmean + (size_t)bh * T * D;
   double* out = scores + (size_t)bh * T * T;
   const int rbase = 64 * blockIdx.x + 16 * w;
   const int row = rbase + l16;
   double af[D / 4];
 #pragma unroll
-  for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)(4 * s + g) * T + row] : 0.0;
+  for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)row * D + 4 * s + g] : 0.0;
 
   const int nchunks = (T + kScoreCols - 1) / kScoreCols;
-  // each thread stages PER doubles of a chunk: column tid % 32, dims tid / 32 + 8 i
+  // each thread stages PER doubles of a chunk: element tid + 256 i of the
+  // chunk's contiguous [32][D] block
   constexpr int PER = D * kScoreCols / 256;
-  const int cl = tid % kScoreCols, d0 = tid / kScoreCols;
   double pre[PER];
   auto fetch = [&](int cc) {
-    const int col = cc * kScoreCols + cl;
+    const double* src = kb + (size_t)cc * kScoreCols * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) pre[i] = col < T ? kb[(size_t)(d0 + 8 * i) * T + col] : 0.0;
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      pre[i] = cc * kScoreCols + e / D < T ? src[e] : 0.0;
+    }
   };
   auto put = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kbuf[buf][(d0 + 8 * i) * kScoreStride + cl] = pre[i];
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      kbuf[buf][(e / D) * CS + e % D] = pre[i];
+    }
   };
   fetch(0);
   put(0);
@@ -62,8 +68,8 @@ __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict_
     const double* kt = kbuf[buf];
 #pragma unroll
     for (int s = 0; s < D / 4; ++s) {
-      const double b0 = kt[(4 * s + g) * kScoreStride + l16];
-      const double b1 = kt[(4 * s + g) * kScoreStride + 16 + l16];
+      const double b0 = kt[l16 * CS + 4 * s + g];
+      const double b1 = kt[(16 + l16) * CS + 4 * s + g];
       acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b1, acc1, 0, 0, 0);
     }
@@ -281,8 +287,8 @@ __global__ void k_compact(int rows, int stride, const int32_t* __restrict__ tmp,
 
 hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st) {
   dim3 g1((s.T + 63) / 64, s.B * s.H);
-  if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
-  else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qbarT, w.kbarT, w.scores);
+  if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
+  else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
   return hipGetLastError();
 }
 

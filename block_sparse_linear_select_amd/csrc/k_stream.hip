@@ -21,7 +21,7 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
   a.tpc = (s.T + a.nchunk - 1) / a.nchunk;
   a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
   a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
-  a.qbarT = w.qbarT; a.kbarT = w.kbarT; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
+  a.qmean = w.qmean; a.kmean = w.kmean; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
   a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope; a.vt = w.vt;
   a.nrope = rope_entries(s);
   switch (s.dt) {

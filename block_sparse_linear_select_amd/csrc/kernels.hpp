@@ -44,8 +44,8 @@ inline int stream_chunks(const Shape& s) {
 
 // Device scratch of one call, carved out of the caller's workspace.
 struct Scratch {
-  double* qbarT = nullptr;     // [BH][d][T] tile means of Q
-  double* kbarT = nullptr;     // [BH][d][T] tile means of K
+  double* qmean = nullptr;     // [BH][T][d] tile means of Q
+  double* kmean = nullptr;     // [BH][T][d] tile means of K
   double* scores = nullptr;    // [BH][T][T] float64 pooled scores
   int32_t* sel_tmp = nullptr;  // [BH*T][kmax] per-row selection (forced-diagonal path)
   int32_t* sel_cnt = nullptr;  // [BH*T]
@@ -63,7 +63,7 @@ struct Scratch {
 // Workspace planning: byte offsets of each region for a given call.
 struct Plan {
   size_t total = 0;
-  size_t off_qbarT = 0, off_kbarT = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
+  size_t off_qmean = 0, off_kmean = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
   size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
   bool select = false, csr_internal = false, linear = false, vt = false;

@@ -154,8 +154,8 @@ struct StreamArgs {
   const float* vs;
   const void* uk;  // [H][d][r] in the parameter type
   int H;
-  double* qbarT;
-  double* kbarT;
+  double* qmean;  // [BH][T][d] tile means of Q
+  double* kmean;  // [BH][T][d] tile means of K
   double* qbar_out;
   double* kbar_out;
   float* part_s;
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           if (a.qs) sq *= (double)a.qs[(size_t)bh * a.T + t];
           if (a.ks) sk2 *= (double)a.ks[(size_t)bh * a.T + t];
           const double mq = sq / cnt, mk = sk2 / cnt;
-          a.qbarT[((size_t)bh * D + tid) * a.T + t] = mq;
-          a.kbarT[((size_t)bh * D + tid) * a.T + t] = mk;
+          a.qmean[((size_t)bh * a.T + t) * D + tid] = mq;  // one 1 KB row per tile
+          a.kmean[((size_t)bh * a.T + t) * D + tid] = mk;
           if (a.qbar_out) a.qbar_out[((size_t)bh * a.T + t) * D + tid] = mq;
           if (a.kbar_out) a.kbar_out[((size_t)bh * a.T + t) * D + tid] = mk;
         }

@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b_720p_bf16")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads the oracle baseline runs (0 skips it)")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="skip the second measurement: calls that reuse one selected mask (no pooling, "
+                         "scores or top-k), as across denoising steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
                          "MiB each (reference for HBM byte counters)")
@@ -191,6 +194,29 @@ def main():
                          "kv_frac_hbm": kv_bytes / (stream_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                          "qkv_GBps": qkv_bytes / (stream_ms * 1e-3) / 1e9},
     }
+    if not args.no_reuse:
+        # Mask reuse: select once, then run the hybrid call on that CSR (the
+        # streaming pass then computes the linear state only).  Same inputs,
+        # same launch configuration; timed the same way.
+        sel = B.HybridPlan(cfg, dev, export_mask=True)
+        sel.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"], sc["v_scale"])
+        reuse = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
+                                 sc["v_scale"], row_ptr=sel.row_ptr, col_idx=sel.col_idx, check=False)
+        for _ in range(args.warmup):
+            reuse()
+        torch.cuda.synchronize()
+        B.timing_enable(args.steps)
+        e0.record(stream)
+        for _ in range(args.steps):
+            reuse()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_r = e0.elapsed_time(e1) / args.steps
+        kt_r = B.timing_read()
+        B.timing_enable(0)
+        log(f"  {args.steps} calls on a reused mask: {ms_r:.3f} ms/call")
+        out["mask_reuse"] = {"ms_per_call": ms_r, "value": dense_flops / (ms_r * 1e-3) / 1e12,
+                             "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
     if args.cpu_heads > 0:
         log(f"oracle baseline on {args.cpu_heads} heads")
         heads = list(range(min(args.cpu_heads, w.H)))

@@ -249,10 +249,22 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, nbytes), krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
   // Two tiles in flight per block: while tile t is processed from one
   // register set, tile t + 1 is already loading into the other, and tile t + 2
-  // is issued into the first set once tile t sits in LDS.
-  struct TileRegs { Chunk8<T> q[KCH], k[KCH], v[VROW ? KCH : 4]; };
+  // is issued into the first set once tile t sits in LDS.  Every step issues
+  // the same loads (a tile past the chunk has an index beyond T, which reads
+  // zeros from the bounds-checked views and moves no data), so that the
+  // compiler can count the loads in flight and waits for the current tile
+  // only.  fp8 inputs load their per-tile scales with the tile.
+  constexpr bool SCALED = sizeof(T) == 1;
+  struct TileRegs { Chunk8<T> q[KCH], k[KCH], v[VROW ? KCH : 4]; float sq, sk, sv; };
   TileRegs tra, trb;
+  const size_t sbase = (size_t)bh * a.T;
   auto load_tile = [&](int t, TileRegs& c) {
+    if constexpr (SCALED) {  // (scales exist for every fp8 tensor a step reads)
+      const size_t i = sbase + min(t, a.T - 1);
+      if constexpr (POOL) c.sq = a.qs[i];
+      c.sk = a.ks[i];
+      if constexpr (STATE) c.sv = a.vs[i];
+    }
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int e = (t * 64 + row0 + i * NCONT) * D + col8 * 8;
@@ -272,6 +284,10 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   };
 
   auto process = [&](int t, TileRegs& c) {
+    const bool live = t < t1;  // false: a step past the chunk, which only issues its loads
+    // this tile's scales, taken before the registers are reloaded
+    const float tsq = SCALED && POOL ? c.sq : 1.f, tsk = SCALED ? c.sk : 1.f, tsv = SCALED && STATE ? c.sv : 1.f;
+    if (live) {
       // ---- registers -> LDS
       if constexpr (POOL) {
         double pq[8], pk[8];
@@ -306,15 +322,16 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
         }
       }
       __syncthreads();
-      if (t + 2 < t1) load_tile(t + 2, c);
+    }
+    load_tile(t + 2 < t1 ? t + 2 : a.T + 1, c);
+    if (live) {
       if constexpr (STATE && sizeof(T) == 1) {
         // hand the transposed fp8 tile to the sparse kernel
         if (a.vt) write_vt8(reinterpret_cast<uint8_t*>(a.vt) + ((size_t)bh * a.T + t) * D * 64, Vt8, tid);
       }
 
       if constexpr (STATE) {
-        const float sk = a.ks ? a.ks[(size_t)bh * a.T + t] : 1.f;
-        const float sv = a.vs ? a.vs[(size_t)bh * a.T + t] : 1.f;
+        const float sk = tsk, sv = tsv;
         f32x4 accF[4];
   #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -375,27 +392,36 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
         }
       }
       if constexpr (POOL) {
-        if (tid < D) {
-          double sq = 0.0, sk2 = 0.0;
-          for (int c = 0; c < NCONT; ++c) { sq += redq[c * D + tid]; sk2 += redk[c * D + tid]; }
-          const double cnt = (double)min(64, a.N - t * 64);
-          if (a.qs) sq *= (double)a.qs[(size_t)bh * a.T + t];
-          if (a.ks) sk2 *= (double)a.ks[(size_t)bh * a.T + t];
-          const double mq = sq / cnt, mk = sk2 / cnt;
-          a.qmean[((size_t)bh * a.T + t) * D + tid] = mq;  // one 1 KB row per tile
-          a.kmean[((size_t)bh * a.T + t) * D + tid] = mk;
-          if (a.qbar_out) a.qbar_out[((size_t)bh * a.T + t) * D + tid] = mq;
-          if (a.kbar_out) a.kbar_out[((size_t)bh * a.T + t) * D + tid] = mk;
+        // thread tid < D: column tid of Q; D <= tid < 2 D: column tid - D of K
+        static_assert(2 * D <= 256, "one thread per pooled column");
+        if (tid < 2 * D) {
+          const bool isk = tid >= D;
+          const int col = isk ? tid - D : tid;
+          const double* red = isk ? redk : redq;
+          double sum = 0.0;
+  #pragma unroll
+          for (int c = 0; c < NCONT; ++c) sum += red[c * D + col];
+          if constexpr (SCALED) sum *= (double)(isk ? tsk : tsq);
+          const double mean = sum / (double)min(64, a.N - t * 64);
+          const size_t o = ((size_t)bh * a.T + t) * D + col;  // one 1 KB row per tile
+          (isk ? a.kmean : a.qmean)[o] = mean;
+          double* ext = isk ? a.kbar_out : a.qbar_out;
+          if (ext) ext[o] = mean;
         }
       }
       __syncthreads();
+    }
   };
 
+  // (in this order: the loop expects the loads of tra to be the older ones,
+  // and the compiler's wait counts at the loop head cover both ways in)
   load_tile(t0, tra);
-  if (t0 + 1 < t1) load_tile(t0 + 1, trb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(t0 + 1 < t1 ? t0 + 1 : a.T + 1, trb);
+  __builtin_amdgcn_sched_barrier(0);
   for (int t = t0; t < t1; t += 2) {
     process(t, tra);
-    if (t + 1 < t1) process(t + 1, trb);
+    process(t + 1, trb);
   }
 
   if constexpr (STATE) {

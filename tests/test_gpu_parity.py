@@ -165,6 +165,36 @@ def test_workspace_contents_do_not_matter(case, monkeypatch):
         assert torch.equal(x, y), f"output {i} depends on the workspace contents"
 
 
+@pytest.mark.parametrize("name", ["bf16_ragged", "fp8_ragged", "bf16_many_heads"])
+def test_mask_reused_on_the_next_step(name):
+    """A mask selected on one step's inputs, passed back in for the next
+    step's inputs (the selection is skipped): outputs match the oracle
+    evaluated on the new inputs with the old mask."""
+    from workloads.gen import next_step
+    inp1 = Hp.gen(name)
+    w = inp1.w
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows1 = [Hp.oracle_mask_head(inp1, b, h)[1] for b, h in heads]
+    inp2 = next_step(inp1, eps=0.1, seed=w.seed + 1)
+    d2 = Hp.to_device(inp2, DEV)
+    rp, ci = Hp.csr_tensors(rows1, DEV)
+    cfg = _cfg(w)
+    o = B.hybrid_attn(cfg, d2["q"], d2["k"], d2["v"], d2["uq"], d2["uk"], d2["wo"], d2["q_scale"], d2["k_scale"],
+                      d2["v_scale"], row_ptr=rp, col_idx=ci)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    err = Hp.RelL2()
+    changed = 0
+    for i, (b, h) in enumerate(heads):
+        ref = Hp.oracle_head(inp2, b, h, kept_rows=rows1[i])
+        err.add(o[b, h, :w.N], ref["o"][:w.N])
+        fresh = Hp.oracle_mask_head(inp2, b, h)[1]
+        changed += sum(not np.array_equal(x, y) for x, y in zip(fresh, rows1[i]))
+    print(f"  O rel L2 {err.value:.3e}; rows whose fresh selection differs: {changed} of {len(heads) * w.T}",
+          flush=True)
+    assert err.value <= Hp.TOL[w.dtype]
+
+
 # ---------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("name", ["bf16_ragged", "fp8_ragged"])
 def test_given_csr_with_empty_row_and_out_of_range_columns(name):

@@ -216,6 +216,33 @@ def generate(w: Workload, heads: Optional[list] = None) -> Inputs:
     return out
 
 
+def next_step(inp: Inputs, eps: float, seed: int) -> Inputs:
+    """Inputs of a following denoising step: q, k, v of `inp` (as the kernels
+    read them, dequantised for fp8) plus eps * N(0, 1) noise from PCG64(seed),
+    stored again in the workload's type (fp8: quantised again per tile).  The
+    parameters are shared.  Pad rows stay zero."""
+    w = inp.w
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = Inputs(w, None, None, None, inp.uq, inp.uk, inp.wo)
+    for name in ("q", "k", "v"):
+        t = getattr(inp, name)
+        if w.dtype == "fp8":
+            sc = getattr(inp, name + "_scale")
+            x = t.to(torch.float32).reshape(w.B, w.H, w.T, w.tile, w.d) * sc[..., None, None]
+            x = x.reshape(w.B, w.H, w.N_pad, w.d)
+        else:
+            x = t.to(torch.float32)
+        x = x + eps * torch.from_numpy(rng.standard_normal(x.shape).astype(np.float32))
+        x[:, :, w.N:] = 0.0
+        if w.dtype == "fp8":
+            codes, sc = quantize_fp8_tiles(x, w.tile)
+            setattr(out, name, codes)
+            setattr(out, name + "_scale", sc)
+        else:
+            setattr(out, name, x.to(t.dtype))
+    return out
+
+
 def to_fp64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a float32/bfloat16 tensor to a float64 numpy array."""
     assert t.dtype in (torch.float32, torch.bfloat16)

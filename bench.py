@@ -98,6 +98,51 @@ def cpu_baseline(w, inp, heads):
             "seconds_per_call_extrapolated": t_total / len(heads) * w.H * w.B}
 
 
+def bench_proj(w, args, dev):
+    """The W8A8 FP8 QKV projection in front of the attention, timed like the
+    hybrid call: per step one row quantisation of the bf16 activations
+    [B*N_pad, H*d] and one projection to FP8 q, k, v with their tile scales."""
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+    from workloads.gen import generate_proj
+    t0 = time.time()
+    p = generate_proj(w)
+    C = w.H * w.d
+    M = w.B * w.N_pad
+    x = p.x.reshape(M, C).to(dev)
+    wq, sw = p.wq.to(dev), p.sw.to(dev)
+    log(f"  projection inputs: x [{M}, {C}] bf16, w [{3 * C}, {C}] fp8 ({time.time() - t0:.1f} s)")
+    del p
+
+    def step():
+        xc, xs = B.quantize_rows_fp8(x)
+        return B.qkv_proj_fp8(xc, xs, wq, sw, w.B, w.N_pad, w.H, w.d)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.timing_enable(args.steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kt = B.timing_read()
+    B.timing_enable(0)
+    q_ms = kt["quant"][0] / kt["quant"][1]
+    p_ms = kt["proj"][0] / kt["proj"][1]
+    flops = 2.0 * M * C * 3 * C
+    log(f"  {args.steps} projection steps: {ms:.3f} ms/step (quant {q_ms:.3f}, proj {p_ms:.3f})")
+    achieved = flops / (p_ms * 1e-3) / 1e12
+    return {"ms_per_step": ms, "quant_ms": q_ms, "proj_ms": p_ms, "flops": flops,
+            "quant_GBps": 3.0 * M * C / (q_ms * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "kernel": "k_proj_fp8", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +153,9 @@ def main():
     ap.add_argument("--no-reuse", action="store_true",
                     help="skip the second measurement: calls that reuse one selected mask (no pooling, "
                          "scores or top-k), as across denoising steps")
+    ap.add_argument("--no-proj", action="store_true",
+                    help="skip the third measurement: the W8A8 FP8 QKV projection (activation quantisation + "
+                         "projection with fused output quantisation) at the workload's shape")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
                          "MiB each (reference for HBM byte counters)")
@@ -217,6 +265,8 @@ def main():
         log(f"  {args.steps} calls on a reused mask: {ms_r:.3f} ms/call")
         out["mask_reuse"] = {"ms_per_call": ms_r, "value": dense_flops / (ms_r * 1e-3) / 1e12,
                              "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
+    if not args.no_proj and w.d == 128:
+        out["qkv_proj"] = bench_proj(w, args, dev)
     if args.cpu_heads > 0:
         log(f"oracle baseline on {args.cpu_heads} heads")
         heads = list(range(min(args.cpu_heads, w.H)))

@@ -23,8 +23,9 @@ ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: 
 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
-            "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_hybrid_attn"]
-KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend"]
+            "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_hybrid_attn",
+            "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
+KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj"]
 
 
 class Desc(ctypes.Structure):
@@ -62,6 +63,9 @@ def lib():
         L.hsa_linear_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, vp, vp, sz, vp]
         L.hsa_hybrid_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                       vp, vp, sz, vp]
+        L.hsa_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, f32p, vp]
+        i32 = ctypes.c_int32
+        L.hsa_qkv_proj_fp8.argtypes = [vp, f32p, vp, f32p, i32, i32, i32, i32, i32, vp, vp, vp, f32p, f32p, f32p, vp]
         L.hsa_attn_timing_enable.argtypes = [ctypes.c_int]
         L.hsa_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         for name in EXPORTED:
@@ -274,3 +278,33 @@ def timing_read() -> dict:
 
 def version() -> str:
     return lib().hsa_attn_version().decode()
+
+
+# ------------------------------------------------------------ W8A8 projections
+def quantize_rows_fp8(x: torch.Tensor):
+    """Per-row E4M3 codes of a bfloat16 [M, C] device tensor: (codes uint8 [M, C], scales float32 [M])."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    M, C = x.shape
+    codes = torch.empty((M, C), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().hsa_quantize_rows_fp8(_ptr(x), M, C, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def qkv_proj_fp8(x_codes, x_scales, w_codes, w_scales, B: int, N_pad: int, H: int, d: int = 128):
+    """FP8 Q, K, V [B, H, N_pad, d] (as float8_e4m3fn views) and their per-tile
+    scales [B, H, N_pad // 64] from quantised activations [B*N_pad, C] and
+    weights [3*H*d, C]."""
+    M, C = x_codes.shape
+    if M != B * N_pad or tuple(w_codes.shape) != (3 * H * d, C):
+        raise ValueError("shapes: x_codes [B*N_pad, C], w_codes [3*H*d, C]")
+    for t, dt in ((x_codes, torch.uint8), (w_codes, torch.uint8), (x_scales, torch.float32), (w_scales, torch.float32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x_codes / w_codes must be uint8 and the scales float32, contiguous device tensors")
+    dev = x_codes.device
+    outs = [torch.empty((B, H, N_pad, d), dtype=torch.uint8, device=dev) for _ in range(3)]
+    scs = [torch.empty((B, H, N_pad // 64), dtype=torch.float32, device=dev) for _ in range(3)]
+    _check(lib().hsa_qkv_proj_fp8(_ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales), B, N_pad, C, H, d,
+                                  *[_ptr(o) for o in outs], *[_ptr(c) for c in scs], _stream()))
+    return tuple(o.view(torch.float8_e4m3fn) for o in outs) + tuple(scs)

@@ -375,3 +375,47 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if (e != hipSuccess) return hip_fail(e, "hybrid attention");
   return HSA_ATTN_OK;
 }
+
+// ---------------------------------------------------------------- W8A8 projections
+namespace hsa {
+hipError_t launch_quant_rows(const void* x, long M, int C, void* codes, float* scales, hipStream_t st);
+hipError_t launch_proj_fp8(const void* x, const float* sx, const void* wq, const float* sw, long M, int C, int H,
+                           int n_pad, void* const* out, float* const* osc, hipStream_t st);
+}  // namespace hsa
+
+HSA_API int hsa_quantize_rows_fp8(const void* x, int64_t M, int64_t C, void* codes_out, float* scales_out,
+                                  void* stream) {
+  if (M < 0 || C <= 0 || C % 8 != 0 || C > (1 << 30))
+    return fail(HSA_ATTN_ERR_SHAPE, "quantize_rows: C must be a positive multiple of 8 and M >= 0 (M=%lld C=%lld)",
+                (long long)M, (long long)C);
+  if (M > 0 && (!x || !codes_out || !scales_out))
+    return fail(HSA_ATTN_ERR_NULL, "quantize_rows: x, codes_out and scales_out are required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(HSA_ATTN_KERNEL_QUANT, st, [&] {
+    return launch_quant_rows(x, (long)M, (int)C, codes_out, scales_out, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "row quantisation");
+  return HSA_ATTN_OK;
+}
+
+HSA_API int hsa_qkv_proj_fp8(const void* x_codes, const float* x_scales, const void* w_codes, const float* w_scales,
+                             int32_t B, int32_t N_pad, int32_t C, int32_t H, int32_t d,
+                             void* q, void* k, void* v, float* q_scales, float* k_scales, float* v_scales,
+                             void* stream) {
+  if (d != 128) return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: head dim must be 128 (d=%d)", d);
+  if (B < 1 || H < 1 || N_pad < 64 || N_pad % 64 != 0)
+    return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: need B, H >= 1 and N_pad a positive multiple of 64 (B=%d H=%d N_pad=%d)",
+                B, H, N_pad);
+  if (C < 128 || C % 128 != 0 || (long long)128 * C >= (1LL << 31))
+    return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: C must be a multiple of 128 with 128*C < 2^31 (C=%d)", C);
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !q || !k || !v || !q_scales || !k_scales || !v_scales)
+    return fail(HSA_ATTN_ERR_NULL, "qkv_proj: every pointer is required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* out[3] = {q, k, v};
+  float* osc[3] = {q_scales, k_scales, v_scales};
+  hipError_t e = timed(HSA_ATTN_KERNEL_PROJ, st, [&] {
+    return launch_proj_fp8(x_codes, x_scales, w_codes, w_scales, (long)B * N_pad, C, H, N_pad, out, osc, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "qkv projection");
+  return HSA_ATTN_OK;
+}

@@ -1,0 +1,232 @@
+// W8A8 FP8 QKV projection in front of the attention (SparkDiffusion news
+// article, section 07: the linear projections run as W8A8 FP8 E4M3 with the
+// activation scaling and the type conversions fused into the kernels; the
+// project blog, "A simple staging principle", item 3).
+//
+//  * k_quant_rows: per-token-row E4M3 quantisation of bf16 activations,
+//    s_x = max|x| / 448, code = round-to-nearest-even(x / s_x).  One wave per
+//    row, two passes over the row (the second from L2).
+//  * k_proj_fp8: Y = diag(s_x) X8 W8^T diag(s_w) on the fp8 matrix cores, with
+//    the output quantisation of the attention's FP8 input fused into the
+//    epilogue: each block owns 128 tokens (two 64-token tiles) x 128 output
+//    columns (one head of one of q, k, v), so every per-(tile, head) scale is
+//    decided inside one block, and the codes are written straight into the
+//    [B, H, N_pad, d] layout the attention reads.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "lds_dma.hpp"
+
+namespace hsa {
+
+// --------------------------------------------------------- activation rows
+// x: bf16 [M, C], C a multiple of 8.  Exact: max|x| is exact, and both
+// divisions are correctly rounded float32 divisions.
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ x, long M, int C,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const long m = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const uint16_t* row = x + (size_t)m * C;
+  const int nch = C / 8;  // 16-byte chunks of the row
+  float amax = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  uint8_t* out = codes + (size_t)m * C;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
+    uint32_t w2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float y0 = __fdiv_rn(bf16_bits_to_f32(v[2 * h] & 0xFFFFu), s);
+      const float y1 = __fdiv_rn(bf16_bits_to_f32(v[2 * h] >> 16), s);
+      const float y2 = __fdiv_rn(bf16_bits_to_f32(v[2 * h + 1] & 0xFFFFu), s);
+      const float y3 = __fdiv_rn(bf16_bits_to_f32(v[2 * h + 1] >> 16), s);
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      w2[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, p, true);
+    }
+    *reinterpret_cast<uint2*>(out + 8 * c) = make_uint2(w2[0], w2[1]);
+  }
+  if (lane == 0) scales[m] = s;
+}
+
+// ------------------------------------------------------------- projection
+struct ProjArgs {
+  const uint8_t* x;  // [M, C] E4M3 codes of the activations (M = B * N_pad)
+  const float* sx;   // [M]
+  const uint8_t* w;  // [3 H d, C] E4M3 codes of the weights
+  const float* sw;   // [3 H d]
+  uint8_t* out[3];   // q, k, v codes [B, H, N_pad, d]
+  float* osc[3];     // their scales [B, H, T]
+  long M;
+  int C, H, n_pad, T;
+};
+
+constexpr int kPM = 128;  // tokens per block (two 64-token tiles)
+constexpr int kPN = 128;  // output columns per block (one head, d = 128)
+constexpr int kPK = 128;  // contraction bytes per stage (one 16x16x128 step)
+constexpr int kPStages = 2;
+
+// Tile rows are 128 bytes (8 granules); two rows share a 256-byte bank set.
+// Granule p of row r sits at position p ^ ((r >> 1) & 7), so the 16 rows of
+// one fragment read (two granules per lane group) hit distinct banks.
+__device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
+
+// Block: 256 threads = 2 x 2 waves; wave (wr, wc) computes tokens 64 wr ..
+// +63 x columns 64 wc .. +63 as 4 x 4 steps of 16 columns x 16 tokens:
+// A = W rows (columns of Y), B = X rows (tokens), so a lane's accumulator
+// holds 4 consecutive columns of one token, written as one 4-byte store.
+__global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
+  __shared__ __align__(16) uint8_t Ws[kPStages][kPN * kPK];
+  __shared__ __align__(16) uint8_t Xs[kPStages][kPM * kPK];
+  __shared__ float amax_sh[2][2];
+
+  const int units = 3 * a.H;
+  const int unit = uniform(blockIdx.x % units);
+  const long m0 = (long)uniform(blockIdx.x / units) * kPM;
+  const int j0 = unit * kPN;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int wr = w >> 1, wc = w & 1, l16 = lane & 15, g = lane >> 4;
+
+  // This block's 128 weight rows and 128 activation rows (rows past M read
+  // as zeros through the bounds-checked view).
+  const long mrows = min((long)kPM, a.M - m0);
+  const i32x4_t wrs = make_rsrc_regs(a.w + (size_t)j0 * a.C, kPN * a.C);
+  const i32x4_t xrs = make_rsrc_regs(a.x + (size_t)m0 * a.C, (int)mrows * a.C);
+  // LDS-direct load i of a tile fills bytes [1024 i, +1024): rows 8 i + lane / 8,
+  // slot lane % 8; the slot holds granule slot ^ swz(row).  The lane part of
+  // the source offset depends on i only through i & 1.
+  int lp[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + lane / 8;
+    lp[r] = (lane / 8) * a.C + 16 * ((lane % 8) ^ swz_p(row));
+  }
+  auto stage = [&](int s, int buf) {
+    const int k0 = s * kPK;
+    static_for<0, 4>([&](auto ic) {
+      constexpr int ii = decltype(ic)::value;
+      const int i = 4 * w + ii;
+      lds_dma16<1024 * ii>(wrs, &Ws[buf][4096 * w], lp[ii & 1] + 8 * i * a.C + k0);
+      lds_dma16<1024 * ii>(xrs, &Xs[buf][4096 * w], lp[ii & 1] + 8 * i * a.C + k0);
+    });
+  };
+  if (a.C < 0) { Ws[0][tid] = 0; Xs[0][tid] = 0; }  // never executed: the tiles are written by LDS-direct loads
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment (rows 16 blk + l16 of the wave's 64, bytes 32 g .. +31): granules 2g, 2g + 1
+  auto frag = [&](const uint8_t* tile, int row) {
+    const int sw = swz_p(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * kPK + 16 * ((2 * g) ^ sw));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * kPK + 16 * ((2 * g + 1) ^ sw));
+    return cat8(lo, hi);
+  };
+
+  const int nk = a.C / kPK;
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nk;
+    if (more) stage(s + 1, cur ^ 1);  // lands while this stage's steps run
+    i32x8_t bf[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) bf[tb] = frag(Xs[cur], 64 * wr + 16 * tb + l16);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const i32x8_t af = frag(Ws[cur], 64 * wc + 16 * fb + l16);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mma_fp8(af, bf[tb], acc[fb][tb]);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next stage has landed
+    lds_barrier();                              // next stage visible; every wave is done with this one
+  }
+
+  // ---- epilogue: scale, per-(tile, head) absmax, E4M3 codes
+  float sxv[4], swv[4][4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const long m = m0 + 64 * wr + 16 * tb + l16;
+    sxv[tb] = m < a.M ? a.sx[m] : 0.f;
+  }
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) swv[fb][i] = a.sw[j0 + 64 * wc + 16 * fb + 4 * g + i];
+  float amax = 0.f;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = acc[fb][tb][i] * sxv[tb] * swv[fb][i];
+        acc[fb][tb][i] = y;
+        amax = fmaxf(amax, fabsf(y));
+      }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane == 0) amax_sh[wr][wc] = amax;
+  __syncthreads();
+  amax = fmaxf(amax_sh[wr][0], amax_sh[wr][1]);  // the unit: 64 tokens x 128 columns
+  const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  const float inv = __fdiv_rn(1.f, sc);
+
+  const long mh = m0 + 64 * wr;  // first token of this wave's tile
+  if (mh >= a.M) return;
+  const int t = unit / a.H, h = unit % a.H;
+  const long b = mh / a.n_pad;
+  const int n0 = (int)(mh - b * a.n_pad);
+  uint8_t* dst = a.out[t] + (((size_t)b * a.H + h) * a.n_pad + n0) * kPN + 64 * wc + 4 * g;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+      const f32x4 y = acc[fb][tb];
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * inv, y[1] * inv, 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * inv, y[3] * inv, p, true);
+      *reinterpret_cast<uint32_t*>(dst + (size_t)(16 * tb + l16) * kPN + 16 * fb) = (uint32_t)p;
+    }
+  if (wc == 0 && tid % 128 == 0) a.osc[t][((size_t)b * a.H + h) * a.T + n0 / 64] = sc;
+}
+
+hipError_t launch_quant_rows(const void* x, long M, int C, void* codes, float* scales, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const long grid = (M + 3) / 4;
+  k_quant_rows<<<dim3((unsigned)grid), 256, 0, st>>>(static_cast<const uint16_t*>(x), M, C,
+                                                      static_cast<uint8_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_fp8(const void* x, const float* sx, const void* wq, const float* sw, long M, int C, int H,
+                           int n_pad, void* const* out, float* const* osc, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  ProjArgs a{};
+  a.x = static_cast<const uint8_t*>(x);
+  a.sx = sx;
+  a.w = static_cast<const uint8_t*>(wq);
+  a.sw = sw;
+  for (int t = 0; t < 3; ++t) { a.out[t] = static_cast<uint8_t*>(out[t]); a.osc[t] = osc[t]; }
+  a.M = M; a.C = C; a.H = H; a.n_pad = n_pad; a.T = n_pad / 64;
+  const long grid = ((M + kPM - 1) / kPM) * 3 * H;
+  k_proj_fp8<<<dim3((unsigned)grid), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

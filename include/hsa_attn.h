@@ -134,7 +134,9 @@ enum {
   HSA_ATTN_KERNEL_SCORES = 3,    /* pooled score grid */
   HSA_ATTN_KERNEL_TOPK = 4,      /* per-row top-k and CSR emission */
   HSA_ATTN_KERNEL_ATTEND = 5,    /* block-sparse flash attention + linear readout */
-  HSA_ATTN_KERNEL_KINDS = 6
+  HSA_ATTN_KERNEL_QUANT = 6,     /* per-row FP8 quantisation of activations */
+  HSA_ATTN_KERNEL_PROJ = 7,      /* W8A8 FP8 QKV projection with fused output quantisation */
+  HSA_ATTN_KERNEL_KINDS = 8
 };
 int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
@@ -192,6 +194,43 @@ int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     const int32_t* row_ptr_in, const int32_t* col_idx_in,
                     int32_t* row_ptr_out, int32_t* col_idx_out,
                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * W8A8 FP8 projections in front of the attention (SparkDiffusion news
+ * article, section 07: the linear projections are quantised to W8A8 FP8
+ * E4M3, with activation scaling and type conversion fused into the kernels).
+ *
+ * Per-row FP8 quantisation of activations (the A8 half):
+ *   x: bfloat16 [M, C] row-major, device.  C a multiple of 8 (HSA_ATTN_ERR_SHAPE
+ *   otherwise), M >= 0.
+ *   codes_out: E4M3FN bytes [M, C]; scales_out: float [M], device, caller-owned.
+ *   Row m: s = max|x_m| / 448 (1 for an all-zero row), code = round-to-nearest-
+ *   even(x / s); both divisions correctly rounded float32.
+ */
+int hsa_quantize_rows_fp8(const void* x, int64_t M, int64_t C, void* codes_out, float* scales_out,
+                          void* stream);
+
+/*
+ * QKV projection on the FP8 matrix cores, writing the attention's FP8 inputs:
+ *   Y[m, j] = s_x[m] s_w[j] sum_c x8[m, c] w8[j, c],  m = b N_pad + n,
+ *   j = (t H + h) d + e for tensor t (0 = q, 1 = k, 2 = v), head h, dim e;
+ *   then, per (tensor, b, h, 64-token tile): s = max|Y| / 448 over the tile's
+ *   64 x d values (1 if all zero) and code = round-to-nearest-even(Y / s),
+ *   taken from the float32 accumulators (multiplied by the float32
+ *   reciprocal of s).
+ *   x_codes: E4M3FN [B*N_pad, C], x_scales: float [B*N_pad] (as written by
+ *   hsa_quantize_rows_fp8; pad rows should be zero).
+ *   w_codes: E4M3FN [3*H*d, C] (row j = output column j), w_scales: float [3*H*d].
+ *   q, k, v: E4M3FN [B, H, N_pad, d]; q_scales, k_scales, v_scales: float
+ *   [B, H, N_pad/64] -- exactly the FP8 inputs of hsa_hybrid_attn.
+ *   Requires d = 128, C a multiple of 128 (128 <= C, 128*C < 2^31),
+ *   N_pad a multiple of 64, B, H >= 1 (HSA_ATTN_ERR_SHAPE otherwise).  All
+ *   pointers device, caller-owned; nothing is allocated.
+ */
+int hsa_qkv_proj_fp8(const void* x_codes, const float* x_scales, const void* w_codes, const float* w_scales,
+                     int32_t B, int32_t N_pad, int32_t C, int32_t H, int32_t d,
+                     void* q, void* k, void* v, float* q_scales, float* k_scales, float* v_scales,
+                     void* stream);
 
 #ifdef __cplusplus
 }

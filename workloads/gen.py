@@ -216,6 +216,38 @@ def generate(w: Workload, heads: Optional[list] = None) -> Inputs:
     return out
 
 
+@dataclass
+class ProjInputs:
+    """Inputs of the QKV projection in front of the attention: x [B, N_pad, C]
+    bfloat16 activations (C = H d, pad rows zero), wq [3 H d, C] E4M3FN codes
+    of the weights (row j = output column j: tensor, head, dim), sw [3 H d]
+    float32 per-output-channel scales."""
+    w: Workload
+    x: torch.Tensor
+    wq: torch.Tensor
+    sw: torch.Tensor
+
+
+def generate_proj(w: Workload, rows: Optional[int] = None) -> ProjInputs:
+    """Activations ~ N(0, 1) from PCG64 (seed, 2, b) per batch element and
+    weights ~ N(0, 1/C) from PCG64 (seed, 3), the weights quantised per output
+    channel (absmax / 448 scale, round to nearest even).  `rows` limits the
+    activations drawn per batch element (the rest stay zero), for small cases."""
+    C = w.H * w.d
+    nout = 3 * C
+    x = torch.zeros((w.B, w.N_pad, C), dtype=torch.bfloat16)
+    n = w.N if rows is None else min(rows, w.N)
+    for b in range(w.B):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(2, b))))
+        x[b, :n] = torch.from_numpy(rng.standard_normal((n, C), dtype=np.float32)).to(torch.bfloat16)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(3,))))
+    wf = torch.from_numpy(rng.standard_normal((nout, C), dtype=np.float32) / np.float32(math.sqrt(C)))
+    amax = wf.abs().amax(dim=1)
+    sw = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
+    wq = (wf / sw[:, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return ProjInputs(w, x, wq, sw)
+
+
 def next_step(inp: Inputs, eps: float, seed: int) -> Inputs:
     """Inputs of a following denoising step: q, k, v of `inp` (as the kernels
     read them, dequantised for fp8) plus eps * N(0, 1) noise from PCG64(seed),

@@ -8,7 +8,7 @@
 //    row, two passes over the row (the second from L2).
 //  * k_proj_fp8: Y = diag(s_x) X8 W8^T diag(s_w) on the fp8 matrix cores, with
 //    the output quantisation of the attention's FP8 input fused into the
-//    epilogue: each block owns 128 tokens (two 64-token tiles) x 128 output
+//    epilogue: each block owns 256 tokens (four 64-token tiles) x 128 output
 //    columns (one head of one of q, k, v), so every per-(tile, head) scale is
 //    decided inside one block, and the codes are written straight into the
 //    [B, H, N_pad, d] layout the attention reads.
@@ -72,24 +72,31 @@ struct ProjArgs {
   int C, H, n_pad, T;
 };
 
-constexpr int kPM = 128;  // tokens per block (two 64-token tiles)
-constexpr int kPN = 128;  // output columns per block (one head, d = 128)
-constexpr int kPK = 128;  // contraction bytes per stage (one 16x16x128 step)
-constexpr int kPStages = 2;
+constexpr int kPTG = 4;            // 64-token groups per block
+constexpr int kPM = 64 * kPTG;     // tokens per block
+constexpr int kPN = 128;           // output columns per block (one head, d = 128)
+constexpr int kPK = 128;           // contraction bytes per stage (one 16x16x128 step)
+constexpr int kPStages = 3;        // LDS ring: stage s + 2 loads while stage s is multiplied
+constexpr int kPWaves = 2 * kPTG;  // waves per block
+constexpr int kPXL = kPM * kPK / 1024 / kPWaves;  // LDS-direct loads per wave per stage: activations
+constexpr int kPWL = kPN * kPK / 1024 / kPWaves;  // ... and weights
+constexpr int kPLoads = kPXL + kPWL;
 
 // Tile rows are 128 bytes (8 granules); two rows share a 256-byte bank set.
 // Granule p of row r sits at position p ^ ((r >> 1) & 7), so the 16 rows of
 // one fragment read (two granules per lane group) hit distinct banks.
 __device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
 
-// Block: 256 threads = 2 x 2 waves; wave (wr, wc) computes tokens 64 wr ..
-// +63 x columns 64 wc .. +63 as 4 x 4 steps of 16 columns x 16 tokens:
-// A = W rows (columns of Y), B = X rows (tokens), so a lane's accumulator
-// holds 4 consecutive columns of one token, written as one 4-byte store.
-__global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
+// Block: 2 kPTG waves; wave (wr, wc) computes tokens 64 wr .. +63 x columns
+// 64 wc .. +63 as 4 x 4 steps of 16 columns x 16 tokens: A = W rows (columns
+// of Y), B = X rows (tokens), so a lane's accumulator holds 4 consecutive
+// columns of one token, written as one 4-byte store.  Stages are filled by
+// LDS-direct loads into a ring of kPStages buffers; each load has two stages
+// of matrix-core work to land.
+__global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
   __shared__ __align__(16) uint8_t Ws[kPStages][kPN * kPK];
   __shared__ __align__(16) uint8_t Xs[kPStages][kPM * kPK];
-  __shared__ float amax_sh[2][2];
+  __shared__ float amax_sh[kPTG][2];
 
   const int units = 3 * a.H;
   const int unit = uniform(blockIdx.x % units);
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int wr = w >> 1, wc = w & 1, l16 = lane & 15, g = lane >> 4;
 
-  // This block's 128 weight rows and 128 activation rows (rows past M read
+  // This block's 128 weight rows and kPM activation rows (rows past M read
   // as zeros through the bounds-checked view).
   const long mrows = min((long)kPM, a.M - m0);
   const i32x4_t wrs = make_rsrc_regs(a.w + (size_t)j0 * a.C, kPN * a.C);
@@ -114,11 +121,15 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
   }
   auto stage = [&](int s, int buf) {
     const int k0 = s * kPK;
-    static_for<0, 4>([&](auto ic) {
+    static_for<0, kPXL>([&](auto ic) {
       constexpr int ii = decltype(ic)::value;
-      const int i = 4 * w + ii;
-      lds_dma16<1024 * ii>(wrs, &Ws[buf][4096 * w], lp[ii & 1] + 8 * i * a.C + k0);
-      lds_dma16<1024 * ii>(xrs, &Xs[buf][4096 * w], lp[ii & 1] + 8 * i * a.C + k0);
+      const int i = kPXL * w + ii;
+      lds_dma16<1024 * ii>(xrs, &Xs[buf][1024 * kPXL * w], lp[i & 1] + 8 * i * a.C + k0);
+    });
+    static_for<0, kPWL>([&](auto ic) {
+      constexpr int ii = decltype(ic)::value;
+      const int i = kPWL * w + ii;
+      lds_dma16<1024 * ii>(wrs, &Ws[buf][1024 * kPWL * w], lp[i & 1] + 8 * i * a.C + k0);
     });
   };
   if (a.C < 0) { Ws[0][tid] = 0; Xs[0][tid] = 0; }  // never executed: the tiles are written by LDS-direct loads
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment (rows 16 blk + l16 of the wave's 64, bytes 32 g .. +31): granules 2g, 2g + 1
+  // fragment (row of the tile, bytes 32 g .. +31): granules 2g, 2g + 1
   auto frag = [&](const uint8_t* tile, int row) {
     const int sw = swz_p(row);
     const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * kPK + 16 * ((2 * g) ^ sw));
@@ -139,12 +150,17 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
 
   const int nk = a.C / kPK;
   stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (nk > 1) {
+    stage(1, 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPLoads));  // stage 0 has landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
   lds_barrier();
+  int cur = 0;
   for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nk;
-    if (more) stage(s + 1, cur ^ 1);  // lands while this stage's steps run
+    const bool issue = s + 2 < nk;
+    if (issue) stage(s + 2, cur == 0 ? 2 : cur - 1);  // the buffer of stage s - 1, free since the last barrier
     i32x8_t bf[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) bf[tb] = frag(Xs[cur], 64 * wr + 16 * tb + l16);
@@ -154,8 +170,11 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mma_fp8(af, bf[tb], acc[fb][tb]);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next stage has landed
-    lds_barrier();                              // next stage visible; every wave is done with this one
+    // stage s + 1 has landed (stage s + 2, issued after it, may still be in flight)
+    if (issue) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPLoads));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();  // stage s + 1 visible; every wave is done with stage s
+    cur = cur == kPStages - 1 ? 0 : cur + 1;
   }
 
   // ---- epilogue: scale, per-(tile, head) absmax, E4M3 codes
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void k_proj_fp8(ProjArgs a) {
       p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * inv, y[3] * inv, p, true);
       *reinterpret_cast<uint32_t*>(dst + (size_t)(16 * tb + l16) * kPN + 16 * fb) = (uint32_t)p;
     }
-  if (wc == 0 && tid % 128 == 0) a.osc[t][((size_t)b * a.H + h) * a.T + n0 / 64] = sc;
+  if (wc == 0 && lane == 0) a.osc[t][((size_t)b * a.H + h) * a.T + n0 / 64] = sc;
 }
 
 hipError_t launch_quant_rows(const void* x, long M, int C, void* codes, float* scales, hipStream_t st) {
@@ -225,7 +244,7 @@ hipError_t launch_proj_fp8(const void* x, const float* sx, const void* wq, const
   for (int t = 0; t < 3; ++t) { a.out[t] = static_cast<uint8_t*>(out[t]); a.osc[t] = osc[t]; }
   a.M = M; a.C = C; a.H = H; a.n_pad = n_pad; a.T = n_pad / 64;
   const long grid = ((M + kPM - 1) / kPM) * 3 * H;
-  k_proj_fp8<<<dim3((unsigned)grid), 256, 0, st>>>(a);
+  k_proj_fp8<<<dim3((unsigned)grid), 64 * kPWaves, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -406,8 +406,8 @@ HSA_API int hsa_qkv_proj_fp8(const void* x_codes, const float* x_scales, const v
   if (B < 1 || H < 1 || N_pad < 64 || N_pad % 64 != 0)
     return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: need B, H >= 1 and N_pad a positive multiple of 64 (B=%d H=%d N_pad=%d)",
                 B, H, N_pad);
-  if (C < 128 || C % 128 != 0 || (long long)128 * C >= (1LL << 31))
-    return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: C must be a multiple of 128 with 128*C < 2^31 (C=%d)", C);
+  if (C < 128 || C % 128 != 0 || (long long)256 * C >= (1LL << 31))
+    return fail(HSA_ATTN_ERR_SHAPE, "qkv_proj: C must be a multiple of 128 with 256*C < 2^31 (C=%d)", C);
   if (!x_codes || !x_scales || !w_codes || !w_scales || !q || !k || !v || !q_scales || !k_scales || !v_scales)
     return fail(HSA_ATTN_ERR_NULL, "qkv_proj: every pointer is required");
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -8,10 +8,10 @@
 //    row, two passes over the row (the second from L2).
 //  * k_proj_fp8: Y = diag(s_x) X8 W8^T diag(s_w) on the fp8 matrix cores, with
 //    the output quantisation of the attention's FP8 input fused into the
-//    epilogue: each block owns 256 tokens (four 64-token tiles) x 128 output
-//    columns (one head of one of q, k, v), so every per-(tile, head) scale is
-//    decided inside one block, and the codes are written straight into the
-//    [B, H, N_pad, d] layout the attention reads.
+//    epilogue: each block owns 256 tokens (four 64-token tiles) x 256 output
+//    columns (two heads), so every per-(tile, head) scale is decided inside
+//    one block, and the codes are written straight into the [B, H, N_pad, d]
+//    layout the attention reads.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -72,12 +72,10 @@ struct ProjArgs {
   int C, H, n_pad, T;
 };
 
-constexpr int kPTG = 4;            // 64-token groups per block
-constexpr int kPM = 64 * kPTG;     // tokens per block
-constexpr int kPN = 128;           // output columns per block (one head, d = 128)
-constexpr int kPK = 128;           // contraction bytes per stage (one 16x16x128 step)
-constexpr int kPStages = 3;        // LDS ring: stage s + 2 loads while stage s is multiplied
-constexpr int kPWaves = 2 * kPTG;  // waves per block
+constexpr int kPM = 256;   // tokens per block (four 64-token tiles)
+constexpr int kPN = 256;   // output columns per block (two heads, d = 128)
+constexpr int kPK = 128;   // contraction bytes per stage (one 16x16x128 step)
+constexpr int kPWaves = 8; // 2 token halves x 4 column quarters
 constexpr int kPXL = kPM * kPK / 1024 / kPWaves;  // LDS-direct loads per wave per stage: activations
 constexpr int kPWL = kPN * kPK / 1024 / kPWaves;  // ... and weights
 constexpr int kPLoads = kPXL + kPWL;
@@ -87,28 +85,31 @@ constexpr int kPLoads = kPXL + kPWL;
 // one fragment read (two granules per lane group) hit distinct banks.
 __device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
 
-// Block: 2 kPTG waves; wave (wr, wc) computes tokens 64 wr .. +63 x columns
-// 64 wc .. +63 as 4 x 4 steps of 16 columns x 16 tokens: A = W rows (columns
+// Block: 8 waves; wave (wr, wc) computes tokens 128 wr .. +127 x columns
+// 64 wc .. +63 as 4 x 8 steps of 16 columns x 16 tokens: A = W rows (columns
 // of Y), B = X rows (tokens), so a lane's accumulator holds 4 consecutive
-// columns of one token, written as one 4-byte store.  Stages are filled by
-// LDS-direct loads into a ring of kPStages buffers; each load has two stages
-// of matrix-core work to land.
+// columns of one token, written as one 4-byte store.  A wave tile of 128 x 64
+// reads 24 KB of LDS per stage for 32 steps.  Two LDS stages: the loads of
+// stage s + 1 are issued at the start of stage s and have its 32 steps per
+// wave (two waves per SIMD) to land.
 __global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
-  __shared__ __align__(16) uint8_t Ws[kPStages][kPN * kPK];
-  __shared__ __align__(16) uint8_t Xs[kPStages][kPM * kPK];
-  __shared__ float amax_sh[kPTG][2];
+  __shared__ __align__(16) uint8_t Ws[2][kPN * kPK];
+  __shared__ __align__(16) uint8_t Xs[2][kPM * kPK];
+  __shared__ float amax_sh[4][4];  // [64-token tile][column quarter]
 
-  const int units = 3 * a.H;
-  const int unit = uniform(blockIdx.x % units);
-  const long m0 = (long)uniform(blockIdx.x / units) * kPM;
-  const int j0 = unit * kPN;
+  const int ncb = (3 * a.H + 1) / 2;  // 256-column blocks (the last may hold one head)
+  const int cb = uniform(blockIdx.x % ncb);
+  const long m0 = (long)uniform(blockIdx.x / ncb) * kPM;
+  const int j0 = cb * kPN;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int wr = w >> 1, wc = w & 1, l16 = lane & 15, g = lane >> 4;
+  const int wr = w >> 2, wc = w & 3, l16 = lane & 15, g = lane >> 4;
 
-  // This block's 128 weight rows and kPM activation rows (rows past M read
-  // as zeros through the bounds-checked view).
+  // This block's 256 weight rows and 256 activation rows; rows past the end
+  // (M, or 3 H d for a last block of one head) read as zeros through the
+  // bounds-checked views.
   const long mrows = min((long)kPM, a.M - m0);
-  const i32x4_t wrs = make_rsrc_regs(a.w + (size_t)j0 * a.C, kPN * a.C);
+  const int wrows = min(kPN, 3 * a.H * 128 - j0);
+  const i32x4_t wrs = make_rsrc_regs(a.w + (size_t)j0 * a.C, wrows * a.C);
   const i32x4_t xrs = make_rsrc_regs(a.x + (size_t)m0 * a.C, (int)mrows * a.C);
   // LDS-direct load i of a tile fills bytes [1024 i, +1024): rows 8 i + lane / 8,
   // slot lane % 8; the slot holds granule slot ^ swz(row).  The lane part of
@@ -134,11 +135,11 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
   };
   if (a.C < 0) { Ws[0][tid] = 0; Xs[0][tid] = 0; }  // never executed: the tiles are written by LDS-direct loads
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 8; ++tb) acc[fb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // fragment (row of the tile, bytes 32 g .. +31): granules 2g, 2g + 1
   auto frag = [&](const uint8_t* tile, int row) {
@@ -150,79 +151,78 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
 
   const int nk = a.C / kPK;
   stage(0, 0);
-  if (nk > 1) {
-    stage(1, 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPLoads));  // stage 0 has landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   lds_barrier();
-  int cur = 0;
   for (int s = 0; s < nk; ++s) {
-    const bool issue = s + 2 < nk;
-    if (issue) stage(s + 2, cur == 0 ? 2 : cur - 1);  // the buffer of stage s - 1, free since the last barrier
-    i32x8_t bf[4];
+    const int cur = s & 1;
+    if (s + 1 < nk) stage(s + 1, cur ^ 1);  // lands while this stage's steps run
+    i32x8_t af[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) bf[tb] = frag(Xs[cur], 64 * wr + 16 * tb + l16);
+    for (int fb = 0; fb < 4; ++fb) af[fb] = frag(Ws[cur], 64 * wc + 16 * fb + l16);
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      const i32x8_t af = frag(Ws[cur], 64 * wc + 16 * fb + l16);
+    for (int tb = 0; tb < 8; ++tb) {
+      const i32x8_t bf = frag(Xs[cur], 128 * wr + 16 * tb + l16);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[fb][tb] = mma_fp8(af, bf[tb], acc[fb][tb]);
+      for (int fb = 0; fb < 4; ++fb) acc[fb][tb] = mma_fp8(af[fb], bf, acc[fb][tb]);
     }
-    // stage s + 1 has landed (stage s + 2, issued after it, may still be in flight)
-    if (issue) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPLoads));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    lds_barrier();  // stage s + 1 visible; every wave is done with stage s
-    cur = cur == kPStages - 1 ? 0 : cur + 1;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next stage has landed
+    lds_barrier();                              // next stage visible; every wave is done with this one
   }
 
   // ---- epilogue: scale, per-(tile, head) absmax, E4M3 codes
-  float sxv[4], swv[4][4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const long m = m0 + 64 * wr + 16 * tb + l16;
-    sxv[tb] = m < a.M ? a.sx[m] : 0.f;
-  }
+  float swv[4][4];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) swv[fb][i] = a.sw[j0 + 64 * wc + 16 * fb + 4 * g + i];
-  float amax = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 64 * wc + 16 * fb + 4 * g + i;
+      swv[fb][i] = j < 3 * a.H * 128 ? a.sw[j] : 0.f;
+    }
+  float amax[2] = {0.f, 0.f};  // this wave's two 64-token tiles
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
+  for (int tb = 0; tb < 8; ++tb) {
+    const long m = m0 + 128 * wr + 16 * tb + l16;
+    const float sx = m < a.M ? a.sx[m] : 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float y = acc[fb][tb][i] * sxv[tb] * swv[fb][i];
+        const float y = acc[fb][tb][i] * sx * swv[fb][i];
         acc[fb][tb][i] = y;
-        amax = fmaxf(amax, fabsf(y));
+        amax[tb >> 2] = fmaxf(amax[tb >> 2], fabsf(y));
       }
+  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if (lane == 0) amax_sh[wr][wc] = amax;
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax[q] = fmaxf(amax[q], __shfl_xor(amax[q], off, 64));
+    if (lane == 0) amax_sh[2 * wr + q][wc] = amax[q];
+  }
   __syncthreads();
-  amax = fmaxf(amax_sh[wr][0], amax_sh[wr][1]);  // the unit: 64 tokens x 128 columns
-  const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
-  const float inv = __fdiv_rn(1.f, sc);
-
-  const long mh = m0 + 64 * wr;  // first token of this wave's tile
-  if (mh >= a.M) return;
-  const int t = unit / a.H, h = unit % a.H;
-  const long b = mh / a.n_pad;
-  const int n0 = (int)(mh - b * a.n_pad);
-  uint8_t* dst = a.out[t] + (((size_t)b * a.H + h) * a.n_pad + n0) * kPN + 64 * wc + 4 * g;
+  const int t_unit = 2 * cb + (wc >> 1);  // the head unit of this wave's columns
+  if (t_unit >= 3 * a.H) return;
+  const int t = t_unit / a.H, h = t_unit % a.H;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int q = 0; q < 2; ++q) {
+    const long mh = m0 + 128 * wr + 64 * q;  // first token of the tile
+    if (mh >= a.M) break;
+    const float am = fmaxf(amax_sh[2 * wr + q][wc & 2], amax_sh[2 * wr + q][(wc & 2) + 1]);
+    const float sc = am > 0.f ? __fdiv_rn(am, 448.f) : 1.f;
+    const float inv = __fdiv_rn(1.f, sc);
+    const long b = mh / a.n_pad;
+    const int n0 = (int)(mh - b * a.n_pad);
+    uint8_t* dst = a.out[t] + (((size_t)b * a.H + h) * a.n_pad + n0) * 128 + 64 * (wc & 1) + 4 * g;
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      const f32x4 y = acc[fb][tb];
-      int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * inv, y[1] * inv, 0, false);
-      p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * inv, y[3] * inv, p, true);
-      *reinterpret_cast<uint32_t*>(dst + (size_t)(16 * tb + l16) * kPN + 16 * fb) = (uint32_t)p;
-    }
-  if (wc == 0 && lane == 0) a.osc[t][((size_t)b * a.H + h) * a.T + n0 / 64] = sc;
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const f32x4 y = acc[fb][4 * q + tt];
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * inv, y[1] * inv, 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * inv, y[3] * inv, p, true);
+        *reinterpret_cast<uint32_t*>(dst + (size_t)(16 * tt + l16) * 128 + 16 * fb) = (uint32_t)p;
+      }
+    if ((wc & 1) == 0 && lane == 0) a.osc[t][((size_t)b * a.H + h) * a.T + n0 / 64] = sc;
+  }
 }
 
 hipError_t launch_quant_rows(const void* x, long M, int C, void* codes, float* scales, hipStream_t st) {
@@ -243,7 +243,7 @@ hipError_t launch_proj_fp8(const void* x, const float* sx, const void* wq, const
   a.sw = sw;
   for (int t = 0; t < 3; ++t) { a.out[t] = static_cast<uint8_t*>(out[t]); a.osc[t] = osc[t]; }
   a.M = M; a.C = C; a.H = H; a.n_pad = n_pad; a.T = n_pad / 64;
-  const long grid = ((M + kPM - 1) / kPM) * 3 * H;
+  const long grid = ((M + kPM - 1) / kPM) * ((3 * H + 1) / 2);
   k_proj_fp8<<<dim3((unsigned)grid), 64 * kPWaves, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -223,7 +223,7 @@ int hsa_quantize_rows_fp8(const void* x, int64_t M, int64_t C, void* codes_out, 
  *   w_codes: E4M3FN [3*H*d, C] (row j = output column j), w_scales: float [3*H*d].
  *   q, k, v: E4M3FN [B, H, N_pad, d]; q_scales, k_scales, v_scales: float
  *   [B, H, N_pad/64] -- exactly the FP8 inputs of hsa_hybrid_attn.
- *   Requires d = 128, C a multiple of 128 (128 <= C, 128*C < 2^31),
+ *   Requires d = 128, C a multiple of 128 (128 <= C, 256*C < 2^31),
  *   N_pad a multiple of 64, B, H >= 1 (HSA_ATTN_ERR_SHAPE otherwise).  All
  *   pointers device, caller-owned; nothing is allocated.
  */

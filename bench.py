@@ -33,7 +33,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-ATTEND_SOURCES = ("common.hpp", "attend.hpp", "k_attend.hip")
+ATTEND_SOURCES = ("common.hpp", "lds_dma.hpp", "attend.hpp", "k_attend.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attend_hbm_traffic.md")
 
 

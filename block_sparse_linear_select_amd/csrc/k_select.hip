@@ -38,7 +38,10 @@ __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict_
 #pragma unroll
   for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)row * D + 4 * s + g] : 0.0;
 
-  const int nchunks = (T + kScoreCols - 1) / kScoreCols;
+  // this block's part of the columns: chunks [c_lo, c_hi) of blockIdx.z's share
+  const int nchunks_all = (T + kScoreCols - 1) / kScoreCols;
+  const int c_lo = (int)((long)nchunks_all * blockIdx.z / gridDim.z);
+  const int c_hi = (int)((long)nchunks_all * (blockIdx.z + 1) / gridDim.z);
   // each thread stages PER doubles of a chunk: element tid + 256 i of the
   // chunk's contiguous [32][D] block
   constexpr int PER = D * kScoreCols / 256;
@@ -58,12 +61,13 @@ __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict_
       kbuf[buf][(e / D) * CS + e % D] = pre[i];
     }
   };
-  fetch(0);
+  if (c_lo >= c_hi) return;
+  fetch(c_lo);
   put(0);
   __syncthreads();
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const int buf = cc & 1;
-    if (cc + 1 < nchunks) fetch(cc + 1);  // in flight while this chunk is multiplied
+  for (int cc = c_lo; cc < c_hi; ++cc) {
+    const int buf = (cc - c_lo) & 1;
+    if (cc + 1 < c_hi) fetch(cc + 1);  // in flight while this chunk is multiplied
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
     const double* kt = kbuf[buf];
 #pragma unroll
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict_
         if (c1 < T) out[(size_t)rr * T + c1] = acc1[i];
       }
     }
-    if (cc + 1 < nchunks) put(buf ^ 1);  // that buffer was last read before the previous barrier
+    if (cc + 1 < c_hi) put(buf ^ 1);  // that buffer was last read before the previous barrier
     __syncthreads();
   }
 }
@@ -286,7 +290,19 @@ __global__ void k_compact(int rows, int stride, const int32_t* __restrict__ tmp,
 }
 
 hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st) {
-  dim3 g1((s.T + 63) / 64, s.B * s.H);
+  // Column parts (1..4): the split whose blocks fill the 512 block slots (two
+  // blocks per CU) best over whole rounds, so that no last round runs mostly
+  // empty (760 row blocks at 720P: 2 parts, 1520 blocks, 99% of 3 rounds).
+  const long rowblocks = (long)((s.T + 63) / 64) * s.B * s.H;
+  const int nch = (s.T + kScoreCols - 1) / kScoreCols;
+  int parts = 1;
+  double best = 0.0;
+  for (int p = 1; p <= 4 && p <= nch; ++p) {
+    const long blocks = rowblocks * p;
+    const double fill = (double)blocks / (double)(((blocks + 511) / 512) * 512);
+    if (fill > best + 1e-9) { best = fill; parts = p; }
+  }
+  dim3 g1((s.T + 63) / 64, s.B * s.H, parts);
   if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
   else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
   return hipGetLastError();

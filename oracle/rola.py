@@ -29,6 +29,7 @@ in short:
                  block of D dims turns by p_axis * base^(-2m/D)
   O8 linear      O_l,i = sum_j (rho_i phi_q,i . rho_j phi_k,j) v_j / sum_j phi_q,i . phi_k,j
                  over all valid keys, RoPE in the numerator only
+  O8c variant    the same sums over the valid keys outside the query tile's kept tiles
   O9 output      O_i = O_s,i + O_l,i W_o for valid rows, 0 for pad rows
   O11 fp8        X = E4M3FN code value * per-(tile) scale
 
@@ -205,20 +206,63 @@ def linear_branch_explicit(q, k, v, n, uq, uk, pos, base):
     return out
 
 
+# -------------------------------------- O8c linear branch over the complement
+def complement_keys(kept, n, t, tile=TILE):
+    """Valid keys j < n whose tile is not in `kept` (a list of tile indices;
+    repeats count once and indices outside [0, t) name no tile)."""
+    in_kept = np.zeros(t, dtype=bool)
+    for b in kept:
+        if 0 <= int(b) < t:
+            in_kept[int(b)] = True
+    return np.nonzero(~in_kept[np.arange(n) // tile])[0]
+
+
+def linear_branch_complement(q, k, v, n, uq, uk, pos, base, rows, tile=TILE, tiles=None):
+    """The linear branch over the context the sparse branch leaves out (the RoLA
+    section of the SparkDiffusion news article: the linear branch restores what
+    sparsification discards; SLA in the 2026-05-02 survey post routes the
+    non-critical weights to linear attention).  For the queries of tile a the
+    sums of O8 run over complement_keys(M_a) only:
+      O_l,i = sum_{j in C_a} (rho_i phi_q,i . rho_j phi_k,j) v_j / sum_{j in C_a} phi_q,i . phi_k,j.
+    A tile whose kept set covers every tile has no such key: its rows are 0.
+    `tiles`: compute only these query tiles (the others stay 0).  [N_pad, d]"""
+    q = np.asarray(q, np.float64)
+    fq = elu1(q[:n] @ np.asarray(uq, np.float64))
+    fk = elu1(np.asarray(k[:n], np.float64) @ np.asarray(uk, np.float64))
+    rq, rk = rope(fq, pos[:n], base), rope(fk, pos[:n], base)
+    vv = np.asarray(v[:n], np.float64)
+    t = q.shape[0] // tile
+    out = np.zeros((q.shape[0], q.shape[1]), dtype=np.float64)
+    for a in (range(len(rows)) if tiles is None else tiles):
+        lo, hi = a * tile, min(a * tile + tile, n)
+        c = complement_keys(rows[a], n, t, tile)
+        if hi <= lo or c.size == 0:
+            continue
+        S = rk[c].T @ vv[c]          # [r, d] state of the complement keys
+        z = fk[c].sum(axis=0)        # [r]
+        out[lo:hi] = (rq[lo:hi] @ S) / (fq[lo:hi] @ z)[:, None]
+    return out
+
+
 # --------------------------------------------------------------- O9 the hybrid
 def hybrid_head(q, k, v, n, grid, uq, uk, wo, topk, force_diag, scale, base,
-                tile=TILE, kept_rows=None):
+                tile=TILE, kept_rows=None, linear_keys="all"):
     """Everything for one (b, h): mask, O_s, O_lW = O_l W_o and O = O_s + O_lW.
 
     kept_rows: use this mask instead of selecting one (e.g. to evaluate outputs
-    on a given CSR)."""
+    on a given CSR).  linear_keys: "all" (O8) or "complement" (O8c)."""
     pos = token_positions(grid, n)
     scores = None
     if kept_rows is None:
         scores = pooled_scores(tile_means(q, n, tile), tile_means(k, n, tile))
         kept_rows = select(scores, topk, force_diag)
     o_s = sparse_branch(q, k, v, n, kept_rows, scale, tile)
-    o_l = linear_branch(q, k, v, n, uq, uk, pos, base)
+    if linear_keys == "all":
+        o_l = linear_branch(q, k, v, n, uq, uk, pos, base)
+    elif linear_keys == "complement":
+        o_l = linear_branch_complement(q, k, v, n, uq, uk, pos, base, kept_rows, tile)
+    else:
+        raise ValueError(f"linear_keys={linear_keys!r}")
     o_lw = o_l @ np.asarray(wo, np.float64)
     o_lw[n:] = 0.0
     row_ptr, col_idx = to_csr(kept_rows)

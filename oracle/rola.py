@@ -109,12 +109,15 @@ def from_csr(row_ptr, col_idx):
 # ------------------------------------------------------------- O5 sparse branch
 def sparse_tile(q, k, v, n, a, kept, scale, tile=TILE):
     """Softmax attention of the valid query rows of tile a over the valid keys of
-    the kept tiles.  Returns [rows, d] for rows a*tile .. min(a*tile+tile, n)."""
+    the kept tiles.  Returns [rows, d] for rows a*tile .. min(a*tile+tile, n).
+    With no kept key the rows are 0 (a softmax over nothing adds nothing)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     qlo, qhi = a * tile, min(a * tile + tile, n)
-    keys = np.concatenate([np.arange(b * tile, min(b * tile + tile, n)) for b in kept])
+    keys = np.array([j for b in kept for j in range(b * tile, min(b * tile + tile, n))], dtype=np.int64)
+    if keys.size == 0:
+        return np.zeros((qhi - qlo, q.shape[1]), dtype=np.float64)
     s = scale * (q[qlo:qhi] @ k[keys].T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)

@@ -135,3 +135,18 @@ def test_hybrid_head_with_complement_keys():
     with pytest.raises(ValueError):
         R.hybrid_head(q, k, v, n, grid, uq, uk, wo, topk=1, force_diag=False, scale=0.25, base=BASE,
                       linear_keys="kept")
+
+
+def test_a_row_with_no_kept_tile_has_zero_sparse_output():
+    """The sparse branch of a row that keeps nothing is 0, and the hybrid of
+    such a row is the all-keys linear branch alone."""
+    grid, npad, d, r = (2, 8, 9), 192, 16, 16
+    rng, n, q, k, v, uq, uk = _head(18, grid, npad, d, r)
+    rows = [np.array([], dtype=np.int64), np.array([0, 2]), np.array([1])]
+    o_s = R.sparse_branch(q, k, v, n, rows, scale=0.3)
+    assert np.all(o_s[:64] == 0) and np.any(o_s[64:n] != 0)
+    wo = rng.standard_normal((d, d)) * 0.1
+    out = R.hybrid_head(q, k, v, n, grid, uq, uk, wo, topk=1, force_diag=False, scale=0.3, base=BASE,
+                        kept_rows=rows, linear_keys="complement")
+    full = R.linear_branch(q, k, v, n, uq, uk, R.token_positions(grid, n), BASE) @ wo
+    assert np.allclose(out["o"][:64], full[:64], rtol=0, atol=1e-13)

@@ -18,14 +18,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhsa_attn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-CALL_BLOCK_SELECT, CALL_SPARSE, CALL_LINEAR, CALL_HYBRID = 0, 1, 2, 3
+CALL_BLOCK_SELECT, CALL_SPARSE, CALL_LINEAR, CALL_HYBRID, CALL_LINEAR_COMPLEMENT = 0, 1, 2, 3, 4
 ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: "HIP"}
 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
-            "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_hybrid_attn",
+            "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
+            "hsa_hybrid_attn",
             "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
-KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj"]
+KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj", "compl"]
+LINEAR_KEYS = {"all": 0, "complement": 1}
 
 
 class Desc(ctypes.Structure):
@@ -34,7 +36,7 @@ class Desc(ctypes.Structure):
                 ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("force_diag", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("linear_keys", ctypes.c_int32)]
 
 
 class HsaError(RuntimeError):
@@ -61,6 +63,8 @@ def lib():
         L.hsa_block_select.argtypes = [dp, vp, vp, f32p, f32p, i32p, i32p, f64p, f64p, vp, sz, vp]
         L.hsa_sparse_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, i32p, i32p, vp, f32p, vp, sz, vp]
         L.hsa_linear_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, vp, vp, sz, vp]
+        L.hsa_linear_attn_complement.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, vp, vp,
+                                                 sz, vp]
         L.hsa_hybrid_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                       vp, vp, sz, vp]
         L.hsa_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, f32p, vp]
@@ -95,6 +99,7 @@ class Config:
     softmax_scale: float
     rope_base: float
     dtype: str  # "f32" | "bf16" | "fp8"
+    linear_keys: str = "all"  # "all" | "complement" (keys outside each row's kept tiles)
 
     @property
     def T(self) -> int:
@@ -109,7 +114,8 @@ class Config:
         outd = F32 if self.dtype == "f32" else BF16
         gt, gh, gw = self.grid
         return Desc(self.B, self.H, self.N, self.N_pad, self.d, 64, gt, gh, gw, self.topk,
-                    int(self.force_diag), self.rank, self.softmax_scale, self.rope_base, ind, outd)
+                    int(self.force_diag), self.rank, self.softmax_scale, self.rope_base, ind, outd,
+                    LINEAR_KEYS[self.linear_keys])
 
     @staticmethod
     def from_workload(w) -> "Config":
@@ -222,6 +228,25 @@ def linear_attn(cfg: Config, q, k, v, uq, uk, wo, q_scale=None, k_scale=None, v_
     _check(lib().hsa_linear_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
                                  _ptr(v_scale), _ptr(uq), _ptr(uk), _ptr(wo), _ptr(o),
                                  _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+def linear_attn_complement(cfg: Config, q, k, v, uq, uk, wo, row_ptr, col_idx, q_scale=None, k_scale=None,
+                           v_scale=None):
+    """O_l W_o with the linear sums of tile a's queries over the valid keys
+    outside the tiles of CSR row a."""
+    _check_inputs(cfg, q, k, v, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_params(cfg, uq, uk, wo)
+    _need(row_ptr, "row_ptr", (cfg.B * cfg.H * cfg.T + 1,), torch.int32)
+    if col_idx.dtype != torch.int32 or not col_idx.is_cuda or col_idx.dim() != 1:
+        raise ValueError("col_idx must be a 1-D int32 device tensor")
+    o = torch.empty((cfg.B, cfg.H, cfg.N_pad, cfg.d), dtype=_out_dtype(cfg), device=q.device)
+    ws = _workspace(cfg, CALL_LINEAR_COMPLEMENT, q.device)
+    d = cfg.desc()
+    _check(lib().hsa_linear_attn_complement(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(uq), _ptr(uk), _ptr(wo),
+                                            _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(ws), ws.numel(),
+                                            _stream()))
     return o
 
 

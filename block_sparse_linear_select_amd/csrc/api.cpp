@@ -30,6 +30,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt) {
   Plan p;
   p.select = select; p.csr_internal = csr_internal; p.linear = linear;
+  p.compl_keys = linear && s.compl_keys;
   p.vt = vt && s.dt == Dt::FP8;  // the fp8 sparse kernel reads V pre-transposed
   const size_t bh = (size_t)s.B * s.H, rows = bh * s.T;
   size_t off = 0;
@@ -57,6 +58,12 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     p.off_z = take(bh * s.rank * sizeof(float));
     p.off_uq = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
     p.off_rope = take((size_t)rope_entries(s) * sizeof(float2));
+    if (p.compl_keys) {
+      p.off_tile_s = take(bh * s.T * s.rank * s.d * elt);
+      p.off_tile_z = take(bh * s.T * s.rank * sizeof(float));
+      p.off_s_full = take(bh * s.rank * s.d * sizeof(float));
+      p.off_wo = take((size_t)s.H * s.d * s.d * elt);
+    }
   }
   if (p.vt) p.off_vt = take(bh * (size_t)s.N_pad * s.d);  // one byte per code
   p.total = off;
@@ -84,6 +91,12 @@ Scratch bind_plan(const Plan& p, void* ws) {
     w.z = reinterpret_cast<float*>(b + p.off_z);
     w.uq_frag = b + p.off_uq;
     w.rope = reinterpret_cast<float2*>(b + p.off_rope);
+    if (p.compl_keys) {
+      w.tile_s = b + p.off_tile_s;
+      w.tile_z = reinterpret_cast<float*>(b + p.off_tile_z);
+      w.s_full = reinterpret_cast<float*>(b + p.off_s_full);
+      w.wo_frag = b + p.off_wo;
+    }
   }
   if (p.vt) w.vt = b + p.off_vt;
   return w;
@@ -117,6 +130,10 @@ static int check_desc(const hsa_attn_desc* d, Shape& s, bool need_rank, bool nee
                      (d->in_dtype == HSA_ATTN_FP8_E4M3 && d->out_dtype == HSA_ATTN_BF16);
   if (!ok_dt) return fail(HSA_ATTN_ERR_DTYPE, "dtype pair (%d, %d) unsupported: use (F32,F32), (BF16,BF16) or (FP8_E4M3,BF16)",
                           d->in_dtype, d->out_dtype);
+  if (d->linear_keys != HSA_ATTN_LINEAR_ALL_KEYS && d->linear_keys != HSA_ATTN_LINEAR_COMPLEMENT)
+    return fail(HSA_ATTN_ERR_SHAPE, "linear_keys=%d must be 0 (all keys) or 1 (complement)", d->linear_keys);
+  if (need_rank && d->linear_keys == HSA_ATTN_LINEAR_COMPLEMENT && T > kComplMaxT)
+    return fail(HSA_ATTN_ERR_SHAPE, "T=%d tiles: the complement variant supports at most %d", T, kComplMaxT);
   const long long rows = (long long)d->B * d->H * T;
   if (rows * (d->topk + 1) >= (1ll << 31)) return fail(HSA_ATTN_ERR_SHAPE, "B*H*T*(topk+1) exceeds int32 CSR range");
   s.B = d->B; s.H = d->H; s.N = d->N; s.N_pad = d->N_pad; s.d = d->d; s.T = T;
@@ -124,6 +141,7 @@ static int check_desc(const hsa_attn_desc* d, Shape& s, bool need_rank, bool nee
   s.topk = d->topk; s.force_diag = d->force_diag; s.kmax = d->topk + d->force_diag;
   s.rank = d->rank; s.scale = d->softmax_scale; s.rope_base = d->rope_base;
   s.dt = static_cast<Dt>(d->in_dtype);
+  s.compl_keys = d->linear_keys == HSA_ATTN_LINEAR_COMPLEMENT;
   return HSA_ATTN_OK;
 }
 
@@ -231,11 +249,18 @@ HSA_API int hsa_attn_timing_read(double* ms_out, int32_t* launches_out) {
 HSA_API int hsa_attn_workspace_size(const hsa_attn_desc* desc, int call, size_t* bytes) {
   if (!bytes) return fail(HSA_ATTN_ERR_NULL, "bytes is NULL");
   Shape s;
-  const bool lin = call == HSA_ATTN_CALL_LINEAR || call == HSA_ATTN_CALL_HYBRID;
+  const bool lin = call == HSA_ATTN_CALL_LINEAR || call == HSA_ATTN_CALL_HYBRID ||
+                   call == HSA_ATTN_CALL_LINEAR_COMPLEMENT;
   const bool sel = call == HSA_ATTN_CALL_BLOCK_SELECT || call == HSA_ATTN_CALL_HYBRID;
-  if (call < 0 || call > 3) return fail(HSA_ATTN_ERR_SHAPE, "unknown call %d", call);
+  if (call < 0 || call > 4) return fail(HSA_ATTN_ERR_SHAPE, "unknown call %d", call);
   int rc = check_desc(desc, s, lin, sel);
   if (rc) return rc;
+  if (call == HSA_ATTN_CALL_LINEAR && s.compl_keys)
+    return fail(HSA_ATTN_ERR_SHAPE, "the complement variant needs a mask: use hsa_linear_attn_complement");
+  if (call == HSA_ATTN_CALL_LINEAR_COMPLEMENT) {
+    if (s.T > kComplMaxT) return fail(HSA_ATTN_ERR_SHAPE, "T=%d tiles: the complement variant supports at most %d", s.T, kComplMaxT);
+    s.compl_keys = true;
+  }
   // the hybrid figure covers its largest variant (selection + internal CSR)
   const bool sparse = call == HSA_ATTN_CALL_SPARSE || call == HSA_ATTN_CALL_HYBRID;
   *bytes = make_plan(s, sel, call == HSA_ATTN_CALL_HYBRID, lin, sparse).total;
@@ -317,6 +342,8 @@ HSA_API int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void
   Shape s;
   int rc = check_desc(desc, s, true, false);
   if (rc) return rc;
+  if (s.compl_keys)
+    return fail(HSA_ATTN_ERR_SHAPE, "the complement variant needs a mask: use hsa_linear_attn_complement");
   if (!q || !k || !v || !U_q || !U_k || !W_o || !o_lin)
     return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o and o_lin are required");
   if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
@@ -330,6 +357,33 @@ HSA_API int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void
     return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, nullptr, nullptr, false, true, w, o_lin, nullptr, st);
   });
   if (e != hipSuccess) return hip_fail(e, "linear readout");
+  return HSA_ATTN_OK;
+}
+
+HSA_API int hsa_linear_attn_complement(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                       const float* q_scale, const float* k_scale, const float* v_scale,
+                                       const void* U_q, const void* U_k, const void* W_o,
+                                       const int32_t* row_ptr, const int32_t* col_idx, void* o_lin,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, s, true, false);
+  if (rc) return rc;
+  if (s.T > kComplMaxT) return fail(HSA_ATTN_ERR_SHAPE, "T=%d tiles: the complement variant supports at most %d", s.T, kComplMaxT);
+  s.compl_keys = true;  // this call always sums over the complement
+  if (!q || !k || !v || !U_q || !U_k || !W_o || !o_lin)
+    return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o and o_lin are required");
+  if (!row_ptr || !col_idx) return fail(HSA_ATTN_ERR_CSR, "row_ptr and col_idx are required");
+  if ((rc = check_scales(s, q_scale, k_scale, v_scale, 3))) return rc;
+  if (s.dt == Dt::FP8 && s.d != 128) return fail(HSA_ATTN_ERR_SHAPE, "FP8 attention needs head dim 128 (d=%d)", s.d);
+  Plan p = make_plan(s, false, false, true, false);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  Scratch w = bind_plan(p, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = run_linear_state(s, q, k, v, q_scale, k_scale, v_scale, U_q, U_k, W_o, false, w, st))) return rc;
+  hipError_t e = timed(HSA_ATTN_KERNEL_COMPL, st, [&] {
+    return launch_compl(s, q, q_scale, row_ptr, col_idx, w, o_lin, false, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "complement linear branch");
   return HSA_ATTN_OK;
 }
 
@@ -369,10 +423,16 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
     rp = rpo;
     ci = cio;
   }
+  // all keys: the query-tile kernel also reads the linear branch out; the
+  // complement variant adds its own readout to the sparse output afterwards
   hipError_t e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
-    return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, rp, ci, true, true, w, o, nullptr, st);
+    return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, rp, ci, true, !s.compl_keys, w, o, nullptr, st);
   });
   if (e != hipSuccess) return hip_fail(e, "hybrid attention");
+  if (s.compl_keys) {
+    e = timed(HSA_ATTN_KERNEL_COMPL, st, [&] { return launch_compl(s, q, q_scale, rp, ci, w, o, true, st); });
+    if (e != hipSuccess) return hip_fail(e, "complement linear branch");
+  }
   return HSA_ATTN_OK;
 }
 

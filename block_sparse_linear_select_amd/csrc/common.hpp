@@ -81,6 +81,20 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<f
   for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
 }
 
+// Position of element (rank row rr, column e) of an r x d state inside its
+// readout A fragments (rows: d, contraction: r in chunks of 32): fragment
+// (e / 16, rr / 32), lane e % 16 + 16 g, slot s, where within a 32-row chunk
+// row 16 h + 4 g + i sits at slot 4 h + i -- the order in which the readout
+// packs its rotated features into B fragments.
+template <int D, int R>
+__host__ __device__ __forceinline__ int sp_frag_index(int rr, int e) {
+  constexpr int NRC = (R + 31) / 32;
+  const int rc = rr >> 5, rem = rr & 31;
+  const int s = 4 * (rem >> 4) + (rem & 3), g = (rem >> 2) & 3;
+  const int lane = (e & 15) + 16 * g, db = e >> 4;
+  return ((db * NRC + rc) * 64 + lane) * 8 + s;
+}
+
 // Load 8 consecutive elements (one fragment's worth) from memory of type T.
 __device__ __forceinline__ void load8(Frag<bf16_t>& f, const bf16_t* p) {
   f.w = *reinterpret_cast<const u32x4*>(p);

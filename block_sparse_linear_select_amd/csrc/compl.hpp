@@ -1,0 +1,334 @@
+// Linear branch over the complement of the kept tiles.  For the queries of
+// tile a the sums S and z of the rotary low-rank branch run over the valid
+// keys outside the kept tiles M_a only: the context the block-sparse branch
+// leaves out (SparkDiffusion news article, section 05: the linear branch
+// restores what the sparsification discards; SLA in the 2026-05-02 survey post
+// on sparse attention for video generation routes the non-critical weights to
+// linear attention).
+//
+// The streaming pass writes every key tile's own state S_b = sum_{j in b}
+// k'_j v_j^T (r x d, parameter type) and feature sum z_b; the finalize step
+// writes the full S (float) and W_o^T as A fragments.  One block per
+// (b, h, query tile a), 4 waves of 16 queries:
+//  1. flags of the tiles in CSR row a (entries outside [0, T) and repeats
+//     name no extra tile); a row keeping every tile has no complement keys
+//     and leaves O as it is;
+//  2. S_c = S - sum_{b in M_a} S_b and z_c = z - sum z_b, or, when the row
+//     keeps more than half of the tiles, S_c = sum_{b not in M_a} S_b (so that
+//     a small complement is never the difference of two large sums); float
+//     sums in ascending tile order, every thread owning a fixed slice of the
+//     r x d elements, four tiles' loads in flight;
+//  3. S_c as readout A fragments in LDS (bf16 hi + lo halves, or float);
+//  4. per wave: phi_q = elu(q U_q) + 1, q' = rope(phi_q), n = q' S_c,
+//     den = phi_q . z_c, then O_lW^T = W_o^T (n / den)^T on the matrix cores
+//     (n split into bf16 hi + lo halves), added to the O_s already in o (the
+//     hybrid) or written with zero pad rows (the branch alone).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "readout.hpp"
+
+namespace hsa {
+
+struct ComplArgs {
+  int N, N_pad, T, H;
+  int gt, gh, gw;
+  const void* q;           // [BH][N_pad][d] storage type
+  const float* qs;         // fp8: [BH][T] Q tile scales
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* tile_s;      // [BH][T][r][d] parameter type
+  const float* tile_z;     // [BH][T][r]
+  const float* s_full;     // [BH][r][d]
+  const float* z;          // [BH][r]
+  const void* uq_frag;     // [H] U_q^T A fragments
+  const void* wo_frag;     // [H] W_o^T A fragments
+  const float2* rope;
+  void* o;                 // [BH][N_pad][d] output type
+  int add;                 // 1: add O_lW to the O_s held in o; 0: write O_lW (pad rows 0)
+  long nrows;
+};
+
+// CE consecutive state elements of the parameter type, loaded as one unit
+// (8 or 4 elements: 16 or 8 bytes of bf16, 32 or 16 bytes of float).
+template <typename OT, int CE> struct StateChunk;
+template <> struct StateChunk<bf16_t, 8> {
+  u32x4 w;
+  __device__ void load(const bf16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ float get(int s) const { return bf16_bits_to_f32((w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu); }
+};
+template <> struct StateChunk<bf16_t, 4> {
+  uint2 w;
+  __device__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ float get(int s) const {
+    const uint32_t x = (s < 2) ? w.x : w.y;
+    return bf16_bits_to_f32((x >> (16 * (s & 1))) & 0xFFFFu);
+  }
+};
+template <> struct StateChunk<float, 8> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ float get(int s) const {
+    const float4& v = s < 4 ? a : b;
+    switch (s & 3) { case 0: return v.x; case 1: return v.y; case 2: return v.z; default: return v.w; }
+  }
+};
+template <> struct StateChunk<float, 4> {
+  float4 a;
+  __device__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
+  __device__ float get(int s) const {
+    switch (s & 3) { case 0: return a.x; case 1: return a.y; case 2: return a.z; default: return a.w; }
+  }
+};
+
+// Output element access: 4 consecutive values of a row of o.
+__device__ __forceinline__ void add4_out(bf16_t* p, const f32x4& x) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  const float a0 = bf16_bits_to_f32(u.x & 0xFFFFu) + x[0], a1 = bf16_bits_to_f32(u.x >> 16) + x[1];
+  const float a2 = bf16_bits_to_f32(u.y & 0xFFFFu) + x[2], a3 = bf16_bits_to_f32(u.y >> 16) + x[3];
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+}
+__device__ __forceinline__ void add4_out(float* p, const f32x4& x) {
+  float4 u = *reinterpret_cast<const float4*>(p);
+  u.x += x[0]; u.y += x[1]; u.z += x[2]; u.w += x[3];
+  *reinterpret_cast<float4*>(p) = u;
+}
+__device__ __forceinline__ void put4_out(bf16_t* p, const f32x4& x) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+}
+__device__ __forceinline__ void put4_out(float* p, const f32x4& x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// T: storage type of Q (float, bf16_t or fp8_t); OT: parameter / operand type
+// (float for float inputs, bf16_t otherwise); output type = OT.
+template <typename T, typename OT, int D, int R>
+__global__ __launch_bounds__(256) void k_compl(ComplArgs a) {
+  constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
+  constexpr int NFE = NDB * NRC * 512;            // elements of one set of state fragments
+  constexpr bool SPLIT = sizeof(OT) == 2;         // bf16 operands: hi + lo halves
+  constexpr int EPT = R * D / 256;                // state elements per thread
+  constexpr int CE = EPT < 8 ? EPT : 8;           // per load
+  constexpr int NCH = EPT / CE;
+  constexpr int U = SPLIT ? 4 : 2;                // tiles in flight
+  constexpr int SFB = (SPLIT ? 2 : 1) * NFE * (int)sizeof(OT);
+  constexpr int LISTB = 3 * kComplMaxT;           // tile flags (1 byte) + index list (2 bytes)
+  static_assert(EPT >= 4 && EPT % CE == 0, "state split");
+  __shared__ __align__(16) uint8_t lds[SFB > LISTB ? SFB : LISTB];
+  __shared__ float ZC[R];
+  __shared__ int wcnt[4];
+  __shared__ int nkept_sh;
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
+  const int h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  uint8_t* kept = lds;
+  uint16_t* list = reinterpret_cast<uint16_t*>(lds + kComplMaxT);
+  const int beg = uniform(a.row_ptr[(size_t)bh * a.T + qa]);
+  const int end = uniform(a.row_ptr[(size_t)bh * a.T + qa + 1]);
+
+  // ---- 1. the row's tile flags and their count
+  for (int b = tid; b < a.T; b += 256) kept[b] = 0;
+  if (tid == 0) nkept_sh = 0;
+  __syncthreads();
+  for (int j = beg + tid; j < end; j += 256) {
+    const int b = a.col_idx[j];
+    if (b >= 0 && b < a.T) kept[b] = 1;
+  }
+  __syncthreads();
+  int mine = 0;
+  for (int b = tid; b < a.T; b += 256) mine += kept[b];
+  if (mine) atomicAdd(&nkept_sh, mine);
+  __syncthreads();
+  const int nk = uniform(nkept_sh);
+  const int qrow = qa * 64 + 16 * w + l16;
+  const bool qvalid = qrow < a.N;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  OT* O = reinterpret_cast<OT*>(a.o) + base + (size_t)qrow * D;
+  if (nk >= a.T) {  // no key outside the kept tiles: O_l = 0
+    if (!a.add) {
+#pragma unroll
+      for (int jo = 0; jo < NDB; ++jo) put4_out(O + 16 * jo + 4 * g, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    return;
+  }
+  const bool sub = 2 * nk <= a.T;
+
+  // ---- 2. ascending list of the tiles to sum, then the float sums
+  int cnt = 0;
+  for (int cb = 0; cb < a.T; cb += 256) {
+    const int b = cb + tid;
+    const bool f = b < a.T && ((kept[b] != 0) == sub);
+    const uint64_t bal = __ballot(f);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int off = cnt;
+    for (int i = 0; i < w; ++i) off += wcnt[i];
+    if (f) {
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      list[off + rank] = (uint16_t)b;
+    }
+    cnt += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
+  }
+  cnt = uniform(cnt);
+
+  const size_t sbase = (size_t)bh * R * D;
+  const OT* TS = reinterpret_cast<const OT*>(a.tile_s) + (size_t)bh * a.T * R * D;
+  const float* TZ = a.tile_z + (size_t)bh * a.T * R;
+  float acc[NCH][CE];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int s = 0; s < CE; ++s) acc[i][s] = sub ? a.s_full[sbase + CE * (tid + 256 * i) + s] : 0.f;
+  float zc = (tid < R && sub) ? a.z[(size_t)bh * R + tid] : 0.f;
+  const float sg = sub ? -1.f : 1.f;
+  for (int j0 = 0; j0 < cnt; j0 += U) {
+    StateChunk<OT, CE> x[U][NCH];
+    float zx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = j0 + u < cnt;
+      const int b = ok ? (int)list[j0 + u] : 0;
+      const OT* src = TS + (size_t)b * R * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) x[u][i].load(src + CE * (tid + 256 * i));
+      zx[u] = (tid < R) ? TZ[(size_t)b * R + tid] : 0.f;
+      if (!ok) zx[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float su = (j0 + u < cnt) ? sg : 0.f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int s = 0; s < CE; ++s) acc[i][s] = fmaf(su, x[u][i].get(s), acc[i][s]);
+      zc = fmaf(su, zx[u], zc);
+    }
+  }
+  __syncthreads();  // every thread is done with the flags and the list
+
+  // ---- 3. S_c as readout A fragments, z_c
+  OT* SF = reinterpret_cast<OT*>(lds);
+  if constexpr (R % 32 != 0) {  // rank 16: the upper half of each 32-row chunk stays zero
+    for (int e = tid; e < (SPLIT ? 2 : 1) * NFE; e += 256) {
+      if constexpr (SPLIT) reinterpret_cast<uint16_t*>(SF)[e] = 0;
+      else reinterpret_cast<float*>(SF)[e] = 0.f;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int s = 0; s < CE; ++s) {
+      const int e = CE * (tid + 256 * i) + s;
+      const int idx = sp_frag_index<D, R>(e / D, e % D);
+      const float x = acc[i][s];
+      if constexpr (SPLIT) {
+        const uint32_t hi = f32_to_bf16_bits(x);
+        reinterpret_cast<uint16_t*>(SF)[idx] = (uint16_t)hi;
+        reinterpret_cast<uint16_t*>(SF)[NFE + idx] = (uint16_t)f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+      } else {
+        reinterpret_cast<float*>(SF)[idx] = x;
+      }
+    }
+  if (tid < R) ZC[tid] = zc;
+  __syncthreads();
+
+  // ---- 4. readout of this wave's 16 queries, W_o, added to O_s or written
+  Frag<OT> qf[D / 32];
+  float qscale = 1.f;
+  if constexpr (sizeof(T) == 1) {
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.q) + base;
+    qscale = a.qs[(size_t)bh * a.T + qa];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const uint2 u = qvalid ? *reinterpret_cast<const uint2*>(Q + (size_t)qrow * D + 32 * c + 8 * g) : make_uint2(0, 0);
+      codes_to_bf16(qf[c], u.x, u.y);
+    }
+  } else {
+    const OT* Q = reinterpret_cast<const OT*>(a.q) + base;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (qvalid) load8(qf[c], Q + (size_t)qrow * D + 32 * c + 8 * g);
+      else qf[c].zero();
+    }
+  }
+  ReadoutSrc<OT> src;
+  src.uq = reinterpret_cast<const OT*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
+  src.sp = SF;
+  src.z = ZC;
+  src.rope = a.rope;
+  src.gt = a.gt; src.gh = a.gh; src.gw = a.gw;
+  f32x4 acc_n[1][NDB];
+  float inv_den[1];
+  readout<OT, D, R, 1>(src, &qf, &qrow, &qvalid, lane, acc_n, inv_den, qscale);
+
+  // n / den as B fragments of a contraction over d: slot s of lane group g in
+  // chunk c is dim 16 (2c + s/4) + 4g + s%4 (W_o^T fragments use the same order)
+  Frag<OT> nh[D / 32], nl[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = acc_n[0][2 * c + (s >> 2)][s & 3] * inv_den[0];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if constexpr (SPLIT) {
+        const float h0 = bf16_bits_to_f32(f32_to_bf16_bits(x[2 * p]));
+        const float h1 = bf16_bits_to_f32(f32_to_bf16_bits(x[2 * p + 1]));
+        nh[c].set_pair(p, h0, h1);
+        nl[c].set_pair(p, x[2 * p] - h0, x[2 * p + 1] - h1);
+      } else {
+        nh[c].set_pair(p, x[2 * p], x[2 * p + 1]);
+      }
+    }
+  }
+  const OT* WO = reinterpret_cast<const OT*>(a.wo_frag) + (size_t)h * NDB * (D / 32) * 512;
+#pragma unroll
+  for (int jo = 0; jo < NDB; ++jo) {
+    f32x4 acc_w = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      Frag<OT> wf;
+      load8(wf, WO + ((size_t)(jo * (D / 32) + c) * 64 + lane) * 8);
+      mma(acc_w, wf, nh[c]);
+      if constexpr (SPLIT) mma(acc_w, wf, nl[c]);
+    }
+    if (a.add) {
+      if (qvalid) add4_out(O + 16 * jo + 4 * g, acc_w);
+    } else {
+      put4_out(O + 16 * jo + 4 * g, qvalid ? acc_w : f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+  }
+}
+
+template <typename T, typename OT, int D, int R>
+static hipError_t compl_dispatch(const ComplArgs& a, hipStream_t st) {
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  k_compl<T, OT, D, R><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, typename OT>
+static hipError_t compl_by_shape(const Shape& s, const ComplArgs& a, hipStream_t st) {
+  if (s.d == 64) {
+    if (s.rank == 16) return compl_dispatch<T, OT, 64, 16>(a, st);
+    if (s.rank == 32) return compl_dispatch<T, OT, 64, 32>(a, st);
+    return compl_dispatch<T, OT, 64, 64>(a, st);
+  }
+  if (s.rank == 16) return compl_dispatch<T, OT, 128, 16>(a, st);
+  if (s.rank == 32) return compl_dispatch<T, OT, 128, 32>(a, st);
+  return compl_dispatch<T, OT, 128, 64>(a, st);
+}
+
+hipError_t launch_compl_f32(const Shape& s, const ComplArgs& a, hipStream_t st);
+
+}  // namespace hsa

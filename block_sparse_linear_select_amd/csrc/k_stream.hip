@@ -23,6 +23,7 @@ hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, cons
   a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
   a.qmean = w.qmean; a.kmean = w.kmean; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
   a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope; a.vt = w.vt;
+  if (state && s.compl_keys) { a.tile_s = w.tile_s; a.tile_z = w.tile_z; }
   a.nrope = rope_entries(s);
   switch (s.dt) {
     case Dt::F32: return launch_stream_f32(s, a, pool, state, st);
@@ -36,6 +37,7 @@ hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const
   a.nchunk = stream_chunks(s); a.H = s.H; a.B = s.B;
   a.part_s = w.part_s; a.part_z = w.part_z; a.wo = wo; a.uq = uq;
   a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag;
+  if (s.compl_keys) { a.s_full = w.s_full; a.wo_frag = w.wo_frag; }
   if (s.dt == Dt::F32) return launch_finalize_f32(s, a, st);
   return finalize_by_shape<bf16_t>(s, a, st);
 }

@@ -18,7 +18,12 @@ struct Shape {
   float scale;      // softmax scale
   float rope_base;
   Dt dt;
+  bool compl_keys;  // linear branch over the complement of each row's kept tiles
 };
+
+// Most tiles per (b, h) the complement variant handles (its per-block tile
+// flags and index list live in LDS).
+constexpr int kComplMaxT = 4096;
 
 // RoPE table: for axis a (t, h, w) with D_a feature dims, the float2
 // (cos, sin) of pos * base^(-2m/D_a) at tab[rope_off(a) + pos * D_a/2 + m].
@@ -58,6 +63,10 @@ struct Scratch {
   void* uq_frag = nullptr;     // [H] U_q^T as readout fragments
   float2* rope = nullptr;      // RoPE table
   void* vt = nullptr;          // [BH][T][d][64] V tiles transposed, keys permuted (bf16 sparse path)
+  void* tile_s = nullptr;      // complement variant: [BH][T][r][d] per-tile states (parameter type)
+  float* tile_z = nullptr;     // [BH][T][r] per-tile feature sums
+  float* s_full = nullptr;     // [BH][r][d] full state S (before W_o)
+  void* wo_frag = nullptr;     // [H] W_o^T as matrix-core A fragments
 };
 
 // Workspace planning: byte offsets of each region for a given call.
@@ -66,7 +75,8 @@ struct Plan {
   size_t off_qmean = 0, off_kmean = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
   size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
-  bool select = false, csr_internal = false, linear = false, vt = false;
+  size_t off_tile_s = 0, off_tile_z = 0, off_s_full = 0, off_wo = 0;
+  bool select = false, csr_internal = false, linear = false, vt = false, compl_keys = false;
 };
 
 Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt);
@@ -87,5 +97,9 @@ hipError_t launch_attend(const Shape& s, const void* q, const void* k, const voi
                          const float* qs, const float* ks, const float* vs,
                          const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,
                          const Scratch& w, void* o, float* lse, hipStream_t st);
+// The complement variant's O_l W_o: added to o (which holds O_s) when `add`,
+// else written to o.
+hipError_t launch_compl(const Shape& s, const void* q, const float* qs, const int32_t* row_ptr,
+                        const int32_t* col_idx, const Scratch& w, void* o, bool add, hipStream_t st);
 
 }  // namespace hsa

@@ -163,6 +163,8 @@ struct StreamArgs {
   const float2* rope;
   int nrope;  // RoPE table entries
   void* vt;  // optional: V tiles transposed, [BH][T][d][64] with keys permuted as in LDS
+  void* tile_s;   // with TILES: [BH][T][r][d] state of each tile alone (parameter type)
+  float* tile_z;  // with TILES: [BH][T][r] feature sum of each tile alone
 };
 
 // RoPE tables up to this many entries (11.5 KB at 720P, rank 64) are staged
@@ -170,7 +172,9 @@ struct StreamArgs {
 // two blocks per CU still fit).
 constexpr int kRopeLdsMax = 1536;
 
-template <typename T, typename OT, int D, int R, bool POOL, bool STATE, bool RLDS = false>
+// TILES: also write every tile's own state and feature sum (the partial
+// state of the block is then their sum).
+template <typename T, typename OT, int D, int R, bool POOL, bool STATE, bool RLDS = false, bool TILES = false>
 __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   constexpr int CPR = D / 8;              // 8-element chunks per row
   constexpr int NCONT = 256 / CPR;        // threads sharing a column chunk
@@ -344,6 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           }
         }
         float kp[4][4];
+        float ztile = 0.f;  // this lane's share of the tile's feature sum
   #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
   #pragma unroll
@@ -351,13 +356,19 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
             const int tok = 16 * tb + 4 * g + i;
             const float e1 = elu1(accF[tb][i] * sk);
             const float phi = (t * 64 + tok < a.N) ? e1 : 0.f;
-            zacc += phi;
+            if constexpr (TILES) ztile += phi;
+            else zacc += phi;
             const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
             const int pa = (spos[tok] >> psh) & pmask;
             const float2 cs = RLDS ? rtab[rs.off + pa * rs.half + rs.m] : a.rope[rs.off + pa * rs.half + rs.m];
             float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
             kp[tb][i] = rot * sv;
           }
+        }
+        if constexpr (TILES) {
+          zacc += ztile;
+          const float zt = group4_sum(ztile);
+          if (dg == 0 && g == 0) a.tile_z[((size_t)bh * a.T + t) * R + r] = zt;
         }
         Frag<OT> kf2[2];
   #pragma unroll
@@ -366,6 +377,11 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           kf2[c].set_pair(1, kp[2 * c][2], kp[2 * c][3]);
           kf2[c].set_pair(2, kp[2 * c + 1][0], kp[2 * c + 1][1]);
           kf2[c].set_pair(3, kp[2 * c + 1][2], kp[2 * c + 1][3]);
+        }
+        f32x4 accT[TILES ? DBW : 1];
+        if constexpr (TILES) {
+  #pragma unroll
+          for (int j = 0; j < DBW; ++j) accT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
   #pragma unroll
         for (int j = 0; j < DBW; ++j) {
@@ -387,7 +403,18 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
             } else {
               load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
             }
-            mma(accS[j], vf, kf2[c]);
+            if constexpr (TILES) mma(accT[j], vf, kf2[c]);
+            else mma(accS[j], vf, kf2[c]);
+          }
+        }
+        if constexpr (TILES) {
+          // the tile's own S^T block: row r, columns 16 db + 4 g .. + 3
+          OT* ts = reinterpret_cast<OT*>(a.tile_s) + (((size_t)bh * a.T + t) * R + r) * D;
+  #pragma unroll
+          for (int j = 0; j < DBW; ++j) {
+            const int db = dg * DBW + j;
+            st4(ts + 16 * db + 4 * g, accT[j][0], accT[j][1], accT[j][2], accT[j][3]);
+            accS[j] += accT[j];
           }
         }
       }
@@ -474,6 +501,8 @@ struct FinalArgs {
   void* sp_frag;
   float* z;
   void* uq_frag;
+  float* s_full;   // optional: [BH][r][d] S itself (before W_o)
+  void* wo_frag;   // optional: [H] W_o^T as A fragments
 };
 
 constexpr int kFinRows = 8;  // rank rows per finalize block
@@ -488,10 +517,7 @@ template <typename OT, int D, int R>
 __device__ __forceinline__ void put_sp(void* frag, size_t bh, int rr, int e, float x) {
   constexpr int NRC = (R + 31) / 32;
   constexpr int NFE = (D / 16) * NRC * 512;
-  const int rc = rr >> 5, rem = rr & 31;
-  const int s = 4 * (rem >> 4) + (rem & 3), g = (rem >> 2) & 3;
-  const int lane = (e & 15) + 16 * g, db = e >> 4;
-  const size_t idx = ((size_t)(db * NRC + rc) * 64 + lane) * 8 + s;
+  const size_t idx = sp_frag_index<D, R>(rr, e);
   if constexpr (sizeof(OT) == 4) {
     reinterpret_cast<float*>(frag)[bh * NFE + idx] = x;
   } else {
@@ -522,6 +548,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
     a.z[(size_t)bh * R + tid] = s;
   }
   __syncthreads();
+  if (a.s_full) {
+    for (int e = tid; e < kFinRows * D; e += 256) a.s_full[((size_t)bh * R + r0) * D + e] = S[e];
+  }
   const OT* W = reinterpret_cast<const OT*>(a.wo) + (size_t)h * D * D;
   constexpr int PER = kFinRows * D / 256;  // outputs per thread
   const int col = tid % D;
@@ -551,6 +580,19 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
         int rr = 16 * rbk + (l & 15), d = 32 * c + 8 * (l >> 4) + s2;
         out[idx] = U[(size_t)d * R + rr];
       }
+      // W_o^T fragments for O_lW^T = W_o^T O_l^T: frag (jo, c), lane l, slot
+      // s -> W_o[i][o] with o = 16 jo + l%16 and i = 16 (2c + s/4) + 4 (l/16)
+      // + s%4, the order in which accumulator columns pack into B fragments.
+      if (a.wo_frag) {
+        constexpr int nwe = (D / 16) * (D / 32) * 512;
+        OT* wout = reinterpret_cast<OT*>(a.wo_frag) + (size_t)h * nwe;
+        for (int idx = tid; idx < nwe; idx += 256) {
+          const int s2 = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
+          const int c = fr % (D / 32), jo = fr / (D / 32);
+          const int i = 16 * (2 * c + (s2 >> 2)) + 4 * (l >> 4) + (s2 & 3), o = 16 * jo + (l & 15);
+          wout[idx] = W[(size_t)i * D + o];
+        }
+      }
     }
   }
 }
@@ -561,6 +603,13 @@ static hipError_t stream_dispatch(const Shape& s, const StreamArgs& a, bool pool
   dim3 grid(a.nchunk, s.B * s.H);
   // (the fp8 variant's LDS is already full with its two V^T tiles)
   const bool rlds = a.nrope <= kRopeLdsMax && std::is_same<T, bf16_t>::value;
+  if (state && a.tile_s) {  // per-tile states for the complement variant
+    if (pool && rlds) k_stream<T, OT, D, R, true, true, true, true><<<grid, 256, 0, st>>>(a);
+    else if (pool) k_stream<T, OT, D, R, true, true, false, true><<<grid, 256, 0, st>>>(a);
+    else if (rlds) k_stream<T, OT, D, R, false, true, true, true><<<grid, 256, 0, st>>>(a);
+    else k_stream<T, OT, D, R, false, true, false, true><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   if (pool && state && rlds) k_stream<T, OT, D, R, true, true, true><<<grid, 256, 0, st>>>(a);
   else if (pool && state) k_stream<T, OT, D, R, true, true><<<grid, 256, 0, st>>>(a);
   else if (pool) k_stream<T, OT, D, R, true, false><<<grid, 256, 0, st>>>(a);

@@ -25,6 +25,15 @@
  *             S = sum_j rho_j phi_k,j v_j^T, z = sum_j phi_k,j over valid j
  *   output    O_i = O_s,i + O_l,i W_o (valid rows), 0 (pad rows)
  *
+ * Variant of the linear branch (descriptor field linear_keys): the sums of S
+ * and z may instead run, for the queries of tile a, over the valid keys
+ * outside the kept tiles M_a only -- the context the sparse branch leaves
+ * out (the RoLA section of the SparkDiffusion news article speaks of the
+ * linear branch restoring what the sparsification discards; SLA, in the
+ * 2026-05-02 survey post on sparse attention for video generation, hands the
+ * non-critical weights to linear attention).  A tile whose kept set covers
+ * every tile then has O_l = 0.
+ *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers, owned by the caller; the
  *     library never frees or retains them past the call's stream work.
@@ -87,11 +96,17 @@ enum {
   HSA_ATTN_ERR_HIP = -6        /* a kernel launch failed */
 };
 
+enum { /* keys summed by the linear branch (hsa_attn_desc.linear_keys) */
+  HSA_ATTN_LINEAR_ALL_KEYS = 0,   /* every valid key (the default) */
+  HSA_ATTN_LINEAR_COMPLEMENT = 1  /* per query tile, the valid keys outside its kept tiles */
+};
+
 enum { /* which call a workspace size is asked for */
   HSA_ATTN_CALL_BLOCK_SELECT = 0,
   HSA_ATTN_CALL_SPARSE = 1,
   HSA_ATTN_CALL_LINEAR = 2,
-  HSA_ATTN_CALL_HYBRID = 3
+  HSA_ATTN_CALL_HYBRID = 3,
+  HSA_ATTN_CALL_LINEAR_COMPLEMENT = 4
 };
 
 typedef struct hsa_attn_desc {
@@ -107,6 +122,10 @@ typedef struct hsa_attn_desc {
   float rope_base;          /* usually 10000 */
   int32_t in_dtype;         /* HSA_ATTN_F32 | HSA_ATTN_BF16 | HSA_ATTN_FP8_E4M3 */
   int32_t out_dtype;        /* F32 with F32 inputs; BF16 with BF16 or FP8 inputs */
+  int32_t linear_keys;      /* HSA_ATTN_LINEAR_ALL_KEYS (0) or HSA_ATTN_LINEAR_COMPLEMENT (1),
+                               read by hsa_hybrid_attn; the complement needs a mask, so
+                               hsa_linear_attn rejects it (HSA_ATTN_ERR_SHAPE; the branch alone
+                               is hsa_linear_attn_complement); the complement needs T <= 4096 */
 } hsa_attn_desc;
 
 /* Bytes of workspace `call` needs for `desc` (written to *bytes). */
@@ -136,7 +155,8 @@ enum {
   HSA_ATTN_KERNEL_ATTEND = 5,    /* block-sparse flash attention + linear readout */
   HSA_ATTN_KERNEL_QUANT = 6,     /* per-row FP8 quantisation of activations */
   HSA_ATTN_KERNEL_PROJ = 7,      /* W8A8 FP8 QKV projection with fused output quantisation */
-  HSA_ATTN_KERNEL_KINDS = 8
+  HSA_ATTN_KERNEL_COMPL = 8,     /* linear branch over the complement of the kept tiles */
+  HSA_ATTN_KERNEL_KINDS = 9
 };
 int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
@@ -181,7 +201,29 @@ int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     void* o_lin, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The linear branch over the complement of a given mask, alone, already
+ * multiplied by W_o: for the queries of tile a, the sums of S and z run over
+ * the valid keys outside the tiles of CSR row a (entries outside [0, T) and
+ * repeats name no extra tile; a row naming every tile gives O_l = 0).  The
+ * descriptor's linear_keys is not read; T <= 4096.  The workspace size is the
+ * one of HSA_ATTN_CALL_LINEAR_COMPLEMENT.
+ *   o_lin: [B, H, N_pad, d] in out_dtype (rows >= N zero).
+ */
+int hsa_linear_attn_complement(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                               const float* q_scale, const float* k_scale, const float* v_scale,
+                               const void* U_q, const void* U_k, const void* W_o,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* o_lin,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The whole hybrid: O = O_s + O_l W_o.
+ *   With linear_keys = HSA_ATTN_LINEAR_COMPLEMENT, O_l of the queries of tile
+ *   a sums over the valid keys outside the tiles of CSR row a (entries
+ *   outside [0, T) and repeats name no extra tile); the workspace then also
+ *   holds one r x d state per key tile (B*H*T*r*d elements of the parameter
+ *   type), and the kept tiles' states are subtracted from the full state, or,
+ *   when a row keeps more than half of the tiles, the others' states are
+ *   summed directly.
  *   row_ptr_in / col_idx_in: if both non-NULL, use this mask and skip
  *   selection; if both NULL, select as hsa_block_select does.
  *   row_ptr_out / col_idx_out: if both non-NULL (and no mask was given),

@@ -108,3 +108,34 @@ def test_null_and_workspace_errors_enqueue_nothing():
     rc = L.hsa_sparse_attn(ctypes.byref(d8), fake, fake, fake, fake, fake, fake, fake, fake, fake, None,
                            fake, need, None)
     assert rc == -2 and b"128" in L.hsa_attn_last_error()
+
+
+def test_complement_variant_arguments():
+    L = B.lib()
+    cfg = _cfg(linear_keys="complement")
+    d = cfg.desc()
+    # the descriptor field takes 0 or 1 only
+    bad = _cfg().desc()
+    bad.linear_keys = 2
+    n = ctypes.c_size_t(0)
+    assert L.hsa_attn_workspace_size(ctypes.byref(bad), B.CALL_HYBRID, ctypes.byref(n)) == -2
+    # the hybrid workspace grows by the per-tile states (B*H*T*r*d bf16 values) and more
+    rc_all, n_all = _ws(_cfg(), B.CALL_HYBRID)
+    rc_c, n_c = _ws(cfg, B.CALL_HYBRID)
+    assert rc_all == rc_c == 0 and n_c >= n_all + cfg.B * cfg.H * cfg.T * cfg.rank * cfg.d * 2
+    # the linear call cannot take the complement (it has no mask); the masked call can, whatever the field
+    assert _ws(cfg, B.CALL_LINEAR)[0] == -2 and b"complement" in L.hsa_attn_last_error()
+    rc_l, n_l = _ws(cfg, B.CALL_LINEAR_COMPLEMENT)
+    assert rc_l == 0 and _ws(_cfg(), B.CALL_LINEAR_COMPLEMENT) == (0, n_l) and n_l > _ws(_cfg(), B.CALL_LINEAR)[1]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    rc = L.hsa_linear_attn(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, fake, fake,
+                           fake, 1 << 40, None)
+    assert rc == -2
+    # the masked call needs its CSR
+    rc = L.hsa_linear_attn_complement(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, fake,
+                                      None, None, fake, fake, 1 << 40, None)
+    assert rc == -5
+    # at most 4096 tiles per (b, h) (selection inside the hybrid call stops at 2048)
+    big = _cfg(linear_keys="complement", grid=(65, 64, 64), N=65 * 64 * 64, N_pad=65 * 64 * 64)
+    assert _ws(big, B.CALL_LINEAR_COMPLEMENT)[0] == -2 and b"4096" in L.hsa_attn_last_error()
+    assert _ws(_cfg(grid=(65, 64, 64), N=65 * 64 * 64, N_pad=65 * 64 * 64, topk=3), B.CALL_LINEAR)[0] == 0

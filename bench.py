@@ -143,6 +143,53 @@ def bench_proj(w, args, dev):
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS}}
 
 
+def bench_compl(w, cfg, d, sc, args, dev):
+    """Hybrid calls with the linear branch over the complement of each row's
+    kept tiles (selection inside, as the main measurement), timed the same way.
+    The complement kernel gathers min(k, T - k) per-tile states per row (from
+    L2 / MALL; each state is read from HBM at least once) and reads Q and
+    reads + writes O."""
+    import dataclasses
+
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+
+    ccfg = dataclasses.replace(cfg, linear_keys="complement")
+    plan = B.HybridPlan(ccfg, dev)
+    run = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
+                           sc["v_scale"], check=False)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    B.timing_enable(args.steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kt = B.timing_read()
+    B.timing_enable(0)
+    kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    log(f"  {args.steps} calls, complement keys: {ms:.3f} ms/call (complement kernel {kern['compl']:.3f} ms)")
+    rows = w.B * w.H * w.T
+    summed = rows * min(w.topk, w.T - w.topk)            # states gathered per call (no forced diagonal)
+    st_elt = 4 if w.dtype == "f32" else 2
+    in_elt = 1 if w.dtype == "fp8" else (4 if w.dtype == "f32" else 2)
+    state_bytes = w.rank * w.d * st_elt
+    gathered = summed * state_bytes
+    hbm = (w.B * w.H * w.N_pad * w.d * (in_elt + 2 * st_elt)   # Q read, O read and written
+           + rows * state_bytes)                              # every tile state at least once
+    cms = kern["compl"]
+    return {"ms_per_call": ms, "kernels_ms": kern,
+            "compl_kernel": {"ms": cms, "states_gathered": summed, "gathered_bytes": gathered,
+                             "gathered_GBps": gathered / (cms * 1e-3) / 1e9,
+                             "hbm_bytes_min": hbm, "hbm_GBps_min": hbm / (cms * 1e-3) / 1e9,
+                             "hbm_frac_min": hbm / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +203,9 @@ def main():
     ap.add_argument("--no-proj", action="store_true",
                     help="skip the third measurement: the W8A8 FP8 QKV projection (activation quantisation + "
                          "projection with fused output quantisation) at the workload's shape")
+    ap.add_argument("--no-compl", action="store_true",
+                    help="skip the fourth measurement: hybrid calls whose linear branch sums over the complement "
+                         "of each row's kept tiles")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
                          "MiB each (reference for HBM byte counters)")
@@ -267,6 +317,8 @@ def main():
                              "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
     if not args.no_proj and w.d == 128:
         out["qkv_proj"] = bench_proj(w, args, dev)
+    if not args.no_compl:
+        out["linear_complement"] = bench_compl(w, cfg, d, sc, args, dev)
     if args.cpu_heads > 0:
         log(f"oracle baseline on {args.cpu_heads} heads")
         heads = list(range(min(args.cpu_heads, w.H)))

@@ -59,9 +59,10 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     p.off_uq = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
     p.off_rope = take((size_t)rope_entries(s) * sizeof(float2));
     if (p.compl_keys) {
-      p.off_tile_s = take(bh * s.T * s.rank * s.d * elt);
+      const size_t nfe = (size_t)ndb * nrc * 512;  // state elements as readout fragments
+      p.off_tile_s = take(bh * s.T * nfe * elt);
       p.off_tile_z = take(bh * s.T * s.rank * sizeof(float));
-      p.off_s_full = take(bh * s.rank * s.d * sizeof(float));
+      p.off_s_full = take(bh * nfe * sizeof(float));
       p.off_wo = take((size_t)s.H * s.d * s.d * elt);
     }
   }

@@ -63,9 +63,9 @@ struct Scratch {
   void* uq_frag = nullptr;     // [H] U_q^T as readout fragments
   float2* rope = nullptr;      // RoPE table
   void* vt = nullptr;          // [BH][T][d][64] V tiles transposed, keys permuted (bf16 sparse path)
-  void* tile_s = nullptr;      // complement variant: [BH][T][r][d] per-tile states (parameter type)
+  void* tile_s = nullptr;      // complement variant: [BH][T] per-tile states as readout fragments
   float* tile_z = nullptr;     // [BH][T][r] per-tile feature sums
-  float* s_full = nullptr;     // [BH][r][d] full state S (before W_o)
+  float* s_full = nullptr;     // [BH] full state S (before W_o) as float readout fragments
   void* wo_frag = nullptr;     // [H] W_o^T as matrix-core A fragments
 };
 

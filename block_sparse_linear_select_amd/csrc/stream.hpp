@@ -163,7 +163,7 @@ struct StreamArgs {
   const float2* rope;
   int nrope;  // RoPE table entries
   void* vt;  // optional: V tiles transposed, [BH][T][d][64] with keys permuted as in LDS
-  void* tile_s;   // with TILES: [BH][T][r][d] state of each tile alone (parameter type)
+  void* tile_s;   // with TILES: [BH][T] state of each tile alone as readout A fragments (parameter type)
   float* tile_z;  // with TILES: [BH][T][r] feature sum of each tile alone
 };
 
@@ -173,7 +173,10 @@ struct StreamArgs {
 constexpr int kRopeLdsMax = 1536;
 
 // TILES: also write every tile's own state and feature sum (the partial
-// state of the block is then their sum).
+// state of the block is then their sum).  The state product then runs with
+// swapped operands, S = k'^T V, so that each lane holds 4 consecutive ranks
+// of one d column: exactly 4 consecutive slots of a readout A fragment of
+// S^T (d rows, contraction over r), written with one store.
 template <typename T, typename OT, int D, int R, bool POOL, bool STATE, bool RLDS = false, bool TILES = false>
 __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   constexpr int CPR = D / 8;              // 8-element chunks per row
@@ -403,17 +406,21 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
             } else {
               load8(vf, &Vt[(16 * db + l16) * VSTR + 32 * c + 8 * g]);
             }
-            if constexpr (TILES) mma(accT[j], vf, kf2[c]);
+            if constexpr (TILES) mma(accT[j], kf2[c], vf);
             else mma(accS[j], vf, kf2[c]);
           }
         }
         if constexpr (TILES) {
-          // the tile's own S^T block: row r, columns 16 db + 4 g .. + 3
-          OT* ts = reinterpret_cast<OT*>(a.tile_s) + (((size_t)bh * a.T + t) * R + r) * D;
+          // the tile's own S block: column d = 16 db + l16, ranks 16 rb + 4 g .. + 3,
+          // i.e. fragment (db, rb / 2), lane l16 + 16 g, slots 4 (rb % 2) .. + 3
+          constexpr int NRC = (R + 31) / 32, NFE = (D / 16) * NRC * 512;
+          OT* ts = reinterpret_cast<OT*>(a.tile_s) + ((size_t)bh * a.T + t) * NFE;
   #pragma unroll
           for (int j = 0; j < DBW; ++j) {
             const int db = dg * DBW + j;
-            st4(ts + 16 * db + 4 * g, accT[j][0], accT[j][1], accT[j][2], accT[j][3]);
+            OT* dst = ts + ((db * NRC + (rb >> 1)) * 64 + l16 + 16 * g) * 8 + 4 * (rb & 1);
+            st4(dst, accT[j][0], accT[j][1], accT[j][2], accT[j][3]);
+            if constexpr (R % 32 != 0) st4(dst + 4, 0.f, 0.f, 0.f, 0.f);  // rank 16: no upper half
             accS[j] += accT[j];
           }
         }
@@ -456,8 +463,13 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 #pragma unroll
     for (int j = 0; j < DBW; ++j) {
       int db = dg * DBW + j;
-      *reinterpret_cast<float4*>(&a.part_s[(pbase * R + r) * D + 16 * db + 4 * g]) =
-          make_float4(accS[j][0], accS[j][1], accS[j][2], accS[j][3]);
+      if constexpr (TILES) {  // swapped layout: column d = 16 db + l16, ranks 16 rb + 4 g + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.part_s[(pbase * R + 16 * rb + 4 * g + i) * D + 16 * db + l16] = accS[j][i];
+      } else {
+        *reinterpret_cast<float4*>(&a.part_s[(pbase * R + r) * D + 16 * db + 4 * g]) =
+            make_float4(accS[j][0], accS[j][1], accS[j][2], accS[j][3]);
+      }
     }
     float zt = group4_sum(zacc);
     if (dg == 0 && g == 0) a.part_z[pbase * R + r] = zt;
@@ -501,7 +513,7 @@ struct FinalArgs {
   void* sp_frag;
   float* z;
   void* uq_frag;
-  float* s_full;   // optional: [BH][r][d] S itself (before W_o)
+  float* s_full;   // optional: [BH] S itself (before W_o) as float readout A fragments
   void* wo_frag;   // optional: [H] W_o^T as A fragments
 };
 
@@ -549,7 +561,11 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
   }
   __syncthreads();
   if (a.s_full) {
-    for (int e = tid; e < kFinRows * D; e += 256) a.s_full[((size_t)bh * R + r0) * D + e] = S[e];
+    constexpr int NFE = (D / 16) * NRC * 512;
+    float* sf = a.s_full + (size_t)bh * NFE;
+    for (int e = tid; e < kFinRows * D; e += 256) sf[sp_frag_index<D, R>(r0 + e / D, e % D)] = S[e];
+    if (blockIdx.y == 0)  // rank 16: the upper half of each 32-row chunk is zero
+      for (int e = tid; e < (32 * NRC - R) * D; e += 256) sf[sp_frag_index<D, R>(R + e / D, e % D)] = 0.f;
   }
   const OT* W = reinterpret_cast<const OT*>(a.wo) + (size_t)h * D * D;
   constexpr int PER = kFinRows * D / 256;  // outputs per thread

@@ -220,10 +220,10 @@ int hsa_linear_attn_complement(const hsa_attn_desc* desc, const void* q, const v
  *   With linear_keys = HSA_ATTN_LINEAR_COMPLEMENT, O_l of the queries of tile
  *   a sums over the valid keys outside the tiles of CSR row a (entries
  *   outside [0, T) and repeats name no extra tile); the workspace then also
- *   holds one r x d state per key tile (B*H*T*r*d elements of the parameter
- *   type), and the kept tiles' states are subtracted from the full state, or,
- *   when a row keeps more than half of the tiles, the others' states are
- *   summed directly.
+ *   holds one r x d state per key tile (B*H*T*d*32*ceil(r/32) elements of
+ *   the parameter type), and the kept tiles' states are subtracted from the
+ *   full state, or, when a row keeps more than half of the tiles, the others'
+ *   states are summed directly.
  *   row_ptr_in / col_idx_in: if both non-NULL, use this mask and skip
  *   selection; if both NULL, select as hsa_block_select does.
  *   row_ptr_out / col_idx_out: if both non-NULL (and no mask was given),

@@ -33,7 +33,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-ATTEND_SOURCES = ("common.hpp", "lds_dma.hpp", "attend.hpp", "k_attend.hip")
+ATTEND_SOURCES = ("common.hpp", "lds_dma.hpp", "readout.hpp", "attend.hpp", "k_attend.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attend_hbm_traffic.md")
 
 
@@ -174,20 +174,25 @@ def bench_compl(w, cfg, d, sc, args, dev):
     B.timing_enable(0)
     kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
     log(f"  {args.steps} calls, complement keys: {ms:.3f} ms/call (complement kernel {kern['compl']:.3f} ms)")
+    return {"ms_per_call": ms, "kernels_ms": kern, "compl_kernel": compl_figures(w, kern["compl"])}
+
+
+def compl_figures(w, cms):
+    """Bytes of the complement kernel per call: the per-row state sums read
+    min(k, T - k) tile states per row (before the reuse that four rows per
+    block and the caches give), and Q, O and every tile state at least once."""
     rows = w.B * w.H * w.T
-    summed = rows * min(w.topk, w.T - w.topk)            # states gathered per call (no forced diagonal)
+    summed = rows * min(w.topk, w.T - w.topk)            # no forced diagonal
     st_elt = 4 if w.dtype == "f32" else 2
     in_elt = 1 if w.dtype == "fp8" else (4 if w.dtype == "f32" else 2)
-    state_bytes = w.rank * w.d * st_elt
+    state_bytes = 32 * ((w.rank + 31) // 32) * w.d * st_elt
     gathered = summed * state_bytes
     hbm = (w.B * w.H * w.N_pad * w.d * (in_elt + 2 * st_elt)   # Q read, O read and written
            + rows * state_bytes)                              # every tile state at least once
-    cms = kern["compl"]
-    return {"ms_per_call": ms, "kernels_ms": kern,
-            "compl_kernel": {"ms": cms, "states_gathered": summed, "gathered_bytes": gathered,
-                             "gathered_GBps": gathered / (cms * 1e-3) / 1e9,
-                             "hbm_bytes_min": hbm, "hbm_GBps_min": hbm / (cms * 1e-3) / 1e9,
-                             "hbm_frac_min": hbm / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+    return {"ms": cms, "states_summed": summed, "summed_bytes": gathered,
+            "summed_GBps": gathered / (cms * 1e-3) / 1e9,
+            "hbm_bytes_min": hbm, "hbm_GBps_min": hbm / (cms * 1e-3) / 1e9,
+            "hbm_frac_min": hbm / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def main():
@@ -203,6 +208,9 @@ def main():
     ap.add_argument("--no-proj", action="store_true",
                     help="skip the third measurement: the W8A8 FP8 QKV projection (activation quantisation + "
                          "projection with fused output quantisation) at the workload's shape")
+    ap.add_argument("--linear-keys", choices=("all", "complement"), default="all",
+                    help="keys of the linear branch in the main measurement: every valid key, or the complement "
+                         "of each row's kept tiles")
     ap.add_argument("--no-compl", action="store_true",
                     help="skip the fourth measurement: hybrid calls whose linear branch sums over the complement "
                          "of each row's kept tiles")
@@ -222,6 +230,9 @@ def main():
 
     w = make_workload(args.workload)
     cfg = B.Config.from_workload(w)
+    if args.linear_keys != "all":
+        import dataclasses
+        cfg = dataclasses.replace(cfg, linear_keys=args.linear_keys)
     dev = torch.device("cuda:0")
     log(f"generating {w.name}: B={w.B} H={w.H} N={w.N} (pad {w.N_pad}) d={w.d} top-{w.topk} of {w.T}, r={w.rank}")
     t0 = time.time()
@@ -281,11 +292,13 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_pad": w.N_pad, "d": w.d,
                    "grid": list(w.grid), "tile": 64, "topk": w.topk, "tiles_per_row": w.T,
-                   "density": w.topk / w.T, "rank": w.rank, "parallelism": "single GPU"},
+                   "density": w.topk / w.T, "rank": w.rank, "linear_keys": args.linear_keys,
+                   "parallelism": "single GPU"},
         "executed_tflops": exec_flops / (ms * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "k_attend (block-sparse flash + linear readout)",
+        "roofline": {"bound": "mfma", "kernel": "k_attend (block-sparse flash" + (
+                         " + linear readout)" if args.linear_keys == "all" else ")"),
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name) if args.linear_keys == "all" else None},
         "kernels_ms": kern,
         "linear_state": {"kernel": "k_stream (pooling + key/value state)", "ms": stream_ms,
                          "kv_bytes": kv_bytes, "kv_GBps": kv_bytes / (stream_ms * 1e-3) / 1e9,
@@ -317,7 +330,9 @@ def main():
                              "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
     if not args.no_proj and w.d == 128:
         out["qkv_proj"] = bench_proj(w, args, dev)
-    if not args.no_compl:
+    if args.linear_keys == "complement":
+        out["compl_kernel"] = compl_figures(w, kern["compl"])
+    elif not args.no_compl:
         out["linear_complement"] = bench_compl(w, cfg, d, sc, args, dev)
     if args.cpu_heads > 0:
         log(f"oracle baseline on {args.cpu_heads} heads")

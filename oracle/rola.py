@@ -273,6 +273,89 @@ def hybrid_head(q, k, v, n, grid, uq, uk, wo, topk, force_diag, scale, base,
             "o_s": o_s, "o_l": o_l, "o_lw": o_lw, "o": o_s + o_lw}
 
 
+# ------------------------------------------------- backward (gradients of O)
+# The mask is held fixed (the top-k selection is piecewise constant in the
+# inputs and has no gradient); upstream gradient g = dL/dO on the valid rows.
+def elu1_grad(x):
+    """phi'(x): 1 for x > 0, exp(x) otherwise."""
+    x = np.asarray(x, np.float64)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def rope_transpose(f, pos, base):
+    """rho_i^T applied row-wise: each pair turned back by its angle."""
+    f = np.asarray(f, np.float64)
+    ang = rope_angles(pos, f.shape[1], base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = f[:, 0::2], f[:, 1::2]
+    out = np.empty_like(f)
+    out[:, 0::2] = x0 * c + x1 * s
+    out[:, 1::2] = -x0 * s + x1 * c
+    return out
+
+
+def sparse_backward(q, k, v, n, rows, scale, g, tile=TILE):
+    """Gradients of O_s (O5) for upstream g [N_pad, d].  For the queries of tile
+    a over the kept keys: P = softmax(scale q k^T), dP = g v^T,
+    dS = P * (dP - rowsum(P * dP)), dq = scale dS k, dk += scale dS^T q,
+    dv += P^T g.  Returns (dq, dk, dv), each [N_pad, d], zero on pad rows."""
+    q, k, v, g = (np.asarray(x, np.float64) for x in (q, k, v, g))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a, kept in enumerate(rows):
+        lo, hi = a * tile, min(a * tile + tile, n)
+        keys = np.array([j for b in kept for j in range(b * tile, min(b * tile + tile, n))], dtype=np.int64)
+        if hi <= lo or keys.size == 0:
+            continue
+        s = scale * (q[lo:hi] @ k[keys].T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dp = g[lo:hi] @ v[keys].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq[lo:hi] = scale * (ds @ k[keys])
+        np.add.at(dk, keys, scale * (ds.T @ q[lo:hi]))
+        np.add.at(dv, keys, p.T @ g[lo:hi])
+    return dq, dk, dv
+
+
+def linear_backward(q, k, v, n, uq, uk, pos, base, gl):
+    """Gradients of O_l (O8, all valid keys) for upstream gl = dL/dO_l [N_pad, d],
+    by the chain rule through O_l = num / den, num = rho(phi(q U_q)) S,
+    den = phi(q U_q) . z, S = sum_j rho_j phi(k_j U_k) v_j^T, z = sum_j phi(k_j U_k).
+    Returns (dq, dk, dv), each [N_pad, d], zero on pad rows."""
+    q, k, v, gl = (np.asarray(x, np.float64) for x in (q, k, v, gl))
+    uq, uk = np.asarray(uq, np.float64), np.asarray(uk, np.float64)
+    xq, xk = q[:n] @ uq, k[:n] @ uk
+    fq, fk = elu1(xq), elu1(xk)
+    rq, rk = rope(fq, pos[:n], base), rope(fk, pos[:n], base)
+    S, z = rk.T @ v[:n], fk.sum(axis=0)
+    den = fq @ z
+    ol = (rq @ S) / den[:, None]
+    gnum = gl[:n] / den[:, None]                 # dL/dnum
+    gden = -(gl[:n] * ol).sum(axis=1) / den      # dL/dden
+    d_rq = gnum @ S.T                            # dL/d(rho phi_q)   [n, r]
+    dS = rq.T @ gnum                             # dL/dS             [r, d]
+    dz = fq.T @ gden                             # dL/dz             [r]
+    d_xq = (gden[:, None] * z[None, :] + rope_transpose(d_rq, pos[:n], base)) * elu1_grad(xq)
+    d_rk = v[:n] @ dS.T                          # dL/d(rho phi_k)   [n, r]
+    d_xk = (dz[None, :] + rope_transpose(d_rk, pos[:n], base)) * elu1_grad(xk)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dq[:n] = d_xq @ uq.T
+    dk[:n] = d_xk @ uk.T
+    dv[:n] = rk @ dS
+    return dq, dk, dv
+
+
+def hybrid_backward(q, k, v, n, grid, uq, uk, wo, rows, scale, base, g, tile=TILE):
+    """Gradients of O = O_s + O_l W_o (all-keys linear branch) on a fixed mask,
+    for upstream g = dL/dO [N_pad, d] (pad rows of g are ignored)."""
+    g = np.asarray(g, np.float64).copy()
+    g[n:] = 0.0
+    pos = token_positions(grid, n)
+    s_grads = sparse_backward(q, k, v, n, rows, scale, g, tile)
+    l_grads = linear_backward(q, k, v, n, uq, uk, pos, base, g @ np.asarray(wo, np.float64).T)
+    return tuple(a + b for a, b in zip(s_grads, l_grads))
+
+
 # ----------------------------------------------------------------- O11 FP8
 def e4m3fn_decode(codes):
     """Value of OCP FP8 E4M3FN byte codes: 1 sign bit, 4 exponent bits (bias 7),

@@ -18,15 +18,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhsa_attn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-CALL_BLOCK_SELECT, CALL_SPARSE, CALL_LINEAR, CALL_HYBRID, CALL_LINEAR_COMPLEMENT = 0, 1, 2, 3, 4
+CALL_BLOCK_SELECT, CALL_SPARSE, CALL_LINEAR, CALL_HYBRID, CALL_LINEAR_COMPLEMENT, CALL_BACKWARD = 0, 1, 2, 3, 4, 5
 ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: "HIP"}
 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
-            "hsa_hybrid_attn",
+            "hsa_hybrid_attn", "hsa_hybrid_attn_backward",
             "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
-KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj", "compl"]
+KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj", "compl", "bwd_linear",
+                "bwd_sparse"]
 LINEAR_KEYS = {"all": 0, "complement": 1}
 
 
@@ -65,6 +66,8 @@ def lib():
         L.hsa_linear_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, vp, vp, sz, vp]
         L.hsa_linear_attn_complement.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, vp, vp,
                                                  sz, vp]
+        L.hsa_hybrid_attn_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, f32p, f32p, f32p, vp,
+                                               sz, vp]
         L.hsa_hybrid_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                       vp, vp, sz, vp]
         L.hsa_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, f32p, vp]
@@ -285,6 +288,24 @@ def hybrid_attn(cfg: Config, q, k, v, uq, uk, wo, q_scale=None, k_scale=None, v_
     if export_mask and row_ptr is None:
         return o, plan.row_ptr, plan.col_idx
     return o
+
+
+def hybrid_attn_backward(cfg: Config, q, k, v, uq, uk, wo, row_ptr, col_idx, d_o):
+    """(dQ, dK, dV) float32 for dL/dO = d_o, on the forward's mask (held fixed)."""
+    _check_inputs(cfg, q, k, v)
+    _check_params(cfg, uq, uk, wo)
+    _need(d_o, "d_o", (cfg.B, cfg.H, cfg.N_pad, cfg.d), _TORCH_IN[cfg.dtype])
+    _need(row_ptr, "row_ptr", (cfg.B * cfg.H * cfg.T + 1,), torch.int32)
+    if col_idx.dtype != torch.int32 or not col_idx.is_cuda or col_idx.dim() != 1:
+        raise ValueError("col_idx must be a 1-D int32 device tensor")
+    shape = (cfg.B, cfg.H, cfg.N_pad, cfg.d)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    ws = _workspace(cfg, CALL_BACKWARD, q.device)
+    d = cfg.desc()
+    _check(lib().hsa_hybrid_attn_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(uq), _ptr(uk), _ptr(wo),
+                                          _ptr(row_ptr), _ptr(col_idx), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
 
 
 def timing_enable(max_launches: int):

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libhsa_attn.so")
 SOURCES = ["k_stream.hip", "k_stream_f32.hip", "k_select.hip", "k_attend.hip", "k_attend_f32.hip", "k_proj.hip",
-           "k_compl.hip", "k_compl_f32.hip", "api.cpp"]
+           "k_compl.hip", "k_compl_f32.hip", "k_backward.hip", "k_backward_f32.hip", "api.cpp"]
 # per-file optimisation level (hipcc -O3 crashes on the float32 instantiations)
 OPT = {"k_stream_f32.hip": "-O1", "k_attend_f32.hip": "-O1"}
 # extra flags per file: the attend kernels never see NaNs, so max/min need no

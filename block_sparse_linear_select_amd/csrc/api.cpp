@@ -27,9 +27,11 @@ static int fail(int code, const char* fmt, ...) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt) {
+Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt, bool backward) {
   Plan p;
-  p.select = select; p.csr_internal = csr_internal; p.linear = linear;
+  p.select = select; p.csr_internal = csr_internal; p.linear = linear || backward;
+  p.backward = backward;
+  linear = p.linear;
   p.compl_keys = linear && s.compl_keys;
   p.vt = vt && s.dt == Dt::FP8;  // the fp8 sparse kernel reads V pre-transposed
   const size_t bh = (size_t)s.B * s.H, rows = bh * s.T;
@@ -67,6 +69,25 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     }
   }
   if (p.vt) p.off_vt = take(bh * (size_t)s.N_pad * s.d);  // one byte per code
+  if (backward) {
+    const size_t elt = s.dt == Dt::F32 ? 4 : 2;
+    const int nrc = (s.rank + 31) / 32, ndb = s.d / 16, nrb = s.rank / 16;
+    const size_t nfe = (size_t)ndb * nrc * 512, nch = stream_chunks(s), rd = (size_t)s.rank * s.d;
+    if (!p.compl_keys) p.off_s_full = take(bh * nfe * sizeof(float));
+    p.off_s_plain = take(bh * rd * sizeof(float));
+    p.off_os = take(bh * (size_t)s.N_pad * s.d * elt);
+    p.off_lse = take(bh * (size_t)s.N_pad * sizeof(float));
+    p.off_dsum = take(bh * (size_t)s.N_pad * sizeof(float));
+    p.off_part_ds = take(bh * nch * rd * sizeof(float));
+    p.off_part_dz = take(bh * nch * s.rank * sizeof(float));
+    p.off_ds_plain = take(bh * rd * sizeof(float));
+    p.off_ds_frag = take(bh * nfe * sizeof(float));
+    p.off_dz = take(bh * s.rank * sizeof(float));
+    p.off_uk = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
+    p.off_csc_cnt = take(rows * sizeof(int32_t));
+    p.off_col_ptr = take((rows + 1) * sizeof(int32_t));
+    p.off_row_idx = take(rows * s.kmax * sizeof(int32_t));
+  }
   p.total = off;
   return p;
 }
@@ -100,6 +121,22 @@ Scratch bind_plan(const Plan& p, void* ws) {
     }
   }
   if (p.vt) w.vt = b + p.off_vt;
+  if (p.backward) {
+    w.s_full = reinterpret_cast<float*>(b + p.off_s_full);
+    w.s_plain = reinterpret_cast<float*>(b + p.off_s_plain);
+    w.os = b + p.off_os;
+    w.lse = reinterpret_cast<float*>(b + p.off_lse);
+    w.dsum = reinterpret_cast<float*>(b + p.off_dsum);
+    w.part_ds = reinterpret_cast<float*>(b + p.off_part_ds);
+    w.part_dz = reinterpret_cast<float*>(b + p.off_part_dz);
+    w.ds_plain = reinterpret_cast<float*>(b + p.off_ds_plain);
+    w.ds_frag = reinterpret_cast<float*>(b + p.off_ds_frag);
+    w.dz = reinterpret_cast<float*>(b + p.off_dz);
+    w.uk_frag = b + p.off_uk;
+    w.csc_cnt = reinterpret_cast<int32_t*>(b + p.off_csc_cnt);
+    w.col_ptr = reinterpret_cast<int32_t*>(b + p.off_col_ptr);
+    w.row_idx = reinterpret_cast<int32_t*>(b + p.off_row_idx);
+  }
   return w;
 }
 
@@ -247,13 +284,21 @@ HSA_API int hsa_attn_timing_read(double* ms_out, int32_t* launches_out) {
   return HSA_ATTN_OK;
 }
 
+// The backward pass covers float32 and bf16 inputs and the all-keys linear branch.
+static int check_backward(const Shape& s) {
+  if (s.dt == Dt::FP8) return fail(HSA_ATTN_ERR_DTYPE, "the backward pass takes float32 or bf16 inputs");
+  if (s.compl_keys) return fail(HSA_ATTN_ERR_SHAPE, "the backward pass covers the all-keys linear branch only");
+  if (s.topk < 1 || s.topk > s.T) return fail(HSA_ATTN_ERR_SHAPE, "topk=%d must be in [1, T=%d]", s.topk, s.T);
+  return HSA_ATTN_OK;
+}
+
 HSA_API int hsa_attn_workspace_size(const hsa_attn_desc* desc, int call, size_t* bytes) {
   if (!bytes) return fail(HSA_ATTN_ERR_NULL, "bytes is NULL");
   Shape s;
   const bool lin = call == HSA_ATTN_CALL_LINEAR || call == HSA_ATTN_CALL_HYBRID ||
-                   call == HSA_ATTN_CALL_LINEAR_COMPLEMENT;
+                   call == HSA_ATTN_CALL_LINEAR_COMPLEMENT || call == HSA_ATTN_CALL_BACKWARD;
   const bool sel = call == HSA_ATTN_CALL_BLOCK_SELECT || call == HSA_ATTN_CALL_HYBRID;
-  if (call < 0 || call > 4) return fail(HSA_ATTN_ERR_SHAPE, "unknown call %d", call);
+  if (call < 0 || call > 5) return fail(HSA_ATTN_ERR_SHAPE, "unknown call %d", call);
   int rc = check_desc(desc, s, lin, sel);
   if (rc) return rc;
   if (call == HSA_ATTN_CALL_LINEAR && s.compl_keys)
@@ -261,6 +306,11 @@ HSA_API int hsa_attn_workspace_size(const hsa_attn_desc* desc, int call, size_t*
   if (call == HSA_ATTN_CALL_LINEAR_COMPLEMENT) {
     if (s.T > kComplMaxT) return fail(HSA_ATTN_ERR_SHAPE, "T=%d tiles: the complement variant supports at most %d", s.T, kComplMaxT);
     s.compl_keys = true;
+  }
+  if (call == HSA_ATTN_CALL_BACKWARD) {
+    if ((rc = check_backward(s))) return rc;
+    *bytes = make_plan(s, false, false, true, false, true).total;
+    return HSA_ATTN_OK;
   }
   // the hybrid figure covers its largest variant (selection + internal CSR)
   const bool sparse = call == HSA_ATTN_CALL_SPARSE || call == HSA_ATTN_CALL_HYBRID;
@@ -478,5 +528,40 @@ HSA_API int hsa_qkv_proj_fp8(const void* x_codes, const float* x_scales, const v
     return launch_proj_fp8(x_codes, x_scales, w_codes, w_scales, (long)B * N_pad, C, H, N_pad, out, osc, st);
   });
   if (e != hipSuccess) return hip_fail(e, "qkv projection");
+  return HSA_ATTN_OK;
+}
+
+// ---------------------------------------------------------------- backward
+HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                     const void* U_q, const void* U_k, const void* W_o,
+                                     const int32_t* row_ptr, const int32_t* col_idx, const void* d_o,
+                                     float* d_q, float* d_k, float* d_v,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, s, true, false);
+  if (rc) return rc;
+  if ((rc = check_backward(s))) return rc;
+  if (!q || !k || !v || !U_q || !U_k || !W_o || !d_o || !d_q || !d_k || !d_v)
+    return fail(HSA_ATTN_ERR_NULL, "q, k, v, U_q, U_k, W_o, d_o, d_q, d_k and d_v are required");
+  if (!row_ptr || !col_idx) return fail(HSA_ATTN_ERR_CSR, "row_ptr and col_idx are required");
+  Plan p = make_plan(s, false, false, true, false, true);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  Scratch w = bind_plan(p, workspace);
+  w.csc_cap = (long)s.B * s.H * s.T * s.kmax;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the forward state (S, z) and the sparse branch's output and log-sum-exp, recomputed
+  if ((rc = run_linear_state(s, q, k, v, nullptr, nullptr, nullptr, U_q, U_k, W_o, false, w, st))) return rc;
+  hipError_t e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
+    return launch_attend(s, q, k, v, nullptr, nullptr, nullptr, row_ptr, col_idx, true, false, w, w.os, w.lse, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "sparse recompute");
+  e = timed(HSA_ATTN_KERNEL_BWD_LINEAR, st, [&] {
+    return launch_backward(s, q, k, v, d_o, U_q, U_k, W_o, row_ptr, col_idx, w, d_q, d_k, d_v, 1, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "linear backward");
+  e = timed(HSA_ATTN_KERNEL_BWD_SPARSE, st, [&] {
+    return launch_backward(s, q, k, v, d_o, U_q, U_k, W_o, row_ptr, col_idx, w, d_q, d_k, d_v, 2, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "sparse backward");
   return HSA_ATTN_OK;
 }

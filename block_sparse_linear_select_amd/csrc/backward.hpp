@@ -1,0 +1,945 @@
+// Backward pass of the hybrid attention on a fixed mask: dQ, dK, dV (float32)
+// for an upstream dO, through both branches.  The forward is the RoLA hybrid
+// of the SparkDiffusion news article, section 05 (block-sparse softmax branch
+// + rotary low-rank linear branch); the gradients are those of that function
+// with the tile selection held fixed (it is piecewise constant in the inputs).
+//
+// Sparse branch (softmax recomputed from the forward's log-sum-exp, as flash
+// attention does):  P = exp(scale q k^T - lse), dP = dO v^T,
+//   dS = P * (dP - D) with D_i = dO_i . O_s,i,
+//   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dO.
+// k_bwd_dq walks each query tile's CSR row, k_bwd_dkv each key tile's column
+// of the transposed mask (CSC, built by k_csc_*).
+//
+// Linear branch, O_l = num / den, num = rho(phi(q U_q)) S, den = phi(q U_q) . z:
+//   gW = dO W_o^T, dnum = gW / den, dden = -(gW . O_l) / den,
+//   dq' = S dnum,  dS = sum_i q'_i dnum_i^T,  dz = sum_i dden_i phi_q,i,
+//   dq = ((dden z + rho^T dq') * phi'(x_q)) U_q^T,
+//   dk' = dS v,  dv = dS^T k',  dk = ((dz + rho^T dk') * phi'(x_k)) U_k^T.
+// k_bwd_q makes the query-side pass (dq of the linear branch, D, and partial
+// dS, dz per block), k_bwd_fin sums the partials in a fixed order, k_bwd_k
+// makes the key-side pass (dk, dv of the linear branch).  The sparse kernels
+// then add their parts.
+//
+// Matrix-core operands follow the fragment convention of common.hpp.  Where an
+// accumulator (lane: column l % 16, rows 4 (l / 16) + i) feeds a contraction
+// over its rows, two 16-row blocks form one 32-wide chunk, slot s of lane
+// group g holding row 16 (s / 4) + 4 g + s % 4; the other operand is read in
+// the same order (LDS tiles staged with that permutation, or two 4-element
+// runs from memory).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "readout.hpp"
+
+namespace hsa {
+
+struct BwdArgs {
+  int N, N_pad, T, H, nchunk, tpc;
+  int gt, gh, gw;
+  float scale;             // softmax scale
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;        // dO, [BH][N_pad][d] in the input type
+  const void* uq;          // [H][d][r] parameter type
+  const void* uk;
+  const void* wo;          // [H][d][d]
+  const int32_t* row_ptr;  // the forward's mask (CSR)
+  const int32_t* col_idx;
+  const int32_t* col_ptr;  // its transpose (CSC): query tiles per key tile, ascending
+  const int32_t* row_idx;
+  long csc_cap;            // entries row_idx holds
+  const void* os;          // [BH][N_pad][d] O_s in the output type
+  const float* lse;        // [BH][N_pad] natural-log log-sum-exp of the sparse branch
+  float* dsum;             // [BH][N_pad] D_i
+  const float* z;          // [BH][R]
+  const float* s_frag;     // [BH][NFE] S^T as float readout A fragments
+  const float* s_plain;    // [BH][R][D]
+  const void* uq_frag;     // [H] U_q^T A fragments
+  void* uk_frag;           // [H] U_k^T A fragments (written by k_bwd_fin)
+  const float2* rope;
+  float* part_ds;          // [BH][nchunk][R][D]
+  float* part_dz;          // [BH][nchunk][R]
+  float* ds_plain;         // [BH][R][D]
+  float* ds_frag;          // [BH][NFE] dS^T as float A fragments
+  float* dz;               // [BH][R]
+  float* dq;               // [BH][N_pad][D] float
+  float* dk;
+  float* dv;
+  long nrows;
+};
+
+// ------------------------------------------------------------ small helpers
+// 8 floats -> operand fragment(s): bf16 hi + lo halves (x = hi + lo to ~2^-17),
+// or the floats themselves.
+__device__ __forceinline__ void split8(const float* x, Frag<bf16_t>& hi, Frag<bf16_t>& lo) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float h0 = bf16_bits_to_f32(f32_to_bf16_bits(x[2 * p]));
+    const float h1 = bf16_bits_to_f32(f32_to_bf16_bits(x[2 * p + 1]));
+    hi.set_pair(p, h0, h1);
+    lo.set_pair(p, x[2 * p] - h0, x[2 * p + 1] - h1);
+  }
+}
+__device__ __forceinline__ void split8(const float* x, Frag<float>& hi, Frag<float>& lo) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) hi.v[s] = x[s];
+  lo.zero();
+}
+// acc += (hi + lo) b; float operands need no low half.
+template <typename OT>
+__device__ __forceinline__ void mma_hl(f32x4& acc, const Frag<OT>& hi, const Frag<OT>& lo, const Frag<OT>& b) {
+  mma(acc, hi, b);
+  if constexpr (sizeof(OT) == 2) mma(acc, lo, b);
+}
+// B fragment of a contraction over accumulator rows: blocks lo (rows 0..15)
+// and hi (rows 16..31) of one 32-wide chunk, each value times m.
+template <typename OT>
+__device__ __forceinline__ void pack_rows(Frag<OT>& f, const f32x4& lo, const f32x4& hi, float m) {
+  f.set_pair(0, lo[0] * m, lo[1] * m);
+  f.set_pair(1, lo[2] * m, lo[3] * m);
+  f.set_pair(2, hi[0] * m, hi[1] * m);
+  f.set_pair(3, hi[2] * m, hi[3] * m);
+}
+__device__ __forceinline__ void load8f(float* x, const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+// 8 elements of the storage type (or of float) as floats
+__device__ __forceinline__ void load8_any(float* x, const bf16_t* p) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) x[s] = bf16_bits_to_f32((w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+}
+__device__ __forceinline__ void load8_any(float* x, const float* p) { load8f(x, p); }
+// 4 consecutive elements as floats
+__device__ __forceinline__ void load4_any(float* x, const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  x[0] = bf16_bits_to_f32(w.x & 0xFFFFu); x[1] = bf16_bits_to_f32(w.x >> 16);
+  x[2] = bf16_bits_to_f32(w.y & 0xFFFFu); x[3] = bf16_bits_to_f32(w.y >> 16);
+}
+__device__ __forceinline__ void load4_any(float* x, const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+// A fragment of a parameter matrix P [d][r] (row-major) with rows d = row and
+// the contraction over r in the permuted chunk order: slot s of lane group g
+// of chunk rc is r = 32 rc + 16 (s / 4) + 4 g + s % 4 (zero past R).
+template <typename OT, int R>
+__device__ __forceinline__ void param_perm_frag(Frag<OT>& f, const OT* P, int row, int rc, int g) {
+  float x[8];
+  load4_any(x, P + (size_t)row * R + 32 * rc + 4 * g);
+  if (32 * rc + 16 < R) load4_any(x + 4, P + (size_t)row * R + 32 * rc + 16 + 4 * g);
+  else x[4] = x[5] = x[6] = x[7] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) f.set_pair(p, x[2 * p], x[2 * p + 1]);
+}
+// (cos, sin) of the rotation of feature pair jp (0 .. r/2 - 1) of token tok
+template <int R>
+__device__ __forceinline__ float2 rope_cs(const float2* rope, int gt, int gh, int gw, int tok, int jp) {
+  constexpr int ht = 3 * R / 16, hh = 3 * R / 16, hwp = R / 8;
+  const int hw = gh * gw;
+  const int t = tok / hw, rem = tok - t * hw, y = rem / gw, x = rem - y * gw;
+  if (jp < ht) return rope[t * ht + jp];
+  if (jp < ht + hh) return rope[gt * ht + y * hh + (jp - ht)];
+  return rope[gt * ht + gh * hh + x * hwp + (jp - ht - hh)];
+}
+
+// ------------------------------------------------- transposed mask (CSC)
+static __global__ void k_zero_i32(int n, int32_t* __restrict__ p) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// one thread per CSR row (b, h, a): count (FILL = false) or place (true) its entries
+template <bool FILL>
+__global__ __launch_bounds__(256) void k_csc_pass(int rows, int T, const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, int32_t* __restrict__ cnt,
+                                                  const int32_t* __restrict__ col_ptr, int32_t* __restrict__ row_idx,
+                                                  long cap) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int bh = r / T, a = r - bh * T;
+  for (int j = row_ptr[r]; j < row_ptr[r + 1]; ++j) {
+    const int b = col_idx[j];
+    if (b < 0 || b >= T) continue;
+    const int slot = atomicAdd(&cnt[bh * T + b], 1);
+    if constexpr (FILL) {
+      const long pos = (long)col_ptr[bh * T + b] + slot;
+      if (pos < cap) row_idx[pos] = a;
+    }
+  }
+}
+
+static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* __restrict__ cnt,
+                                                          int32_t* __restrict__ ptr) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int v = i < n ? cnt[i] : 0;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int t = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += t;
+      __syncthreads();
+    }
+    if (i < n) ptr[i] = carry + part[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) ptr[n] = carry;
+}
+
+// one thread per column: insertion sort of its query tiles (the fill order
+// depends on atomics; the sorted lists do not)
+static __global__ __launch_bounds__(256) void k_csc_sort(int cols, const int32_t* __restrict__ col_ptr,
+                                                          int32_t* __restrict__ row_idx, long cap) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  const long lo = col_ptr[c], hi = min((long)col_ptr[c + 1], cap);
+  for (long i = lo + 1; i < hi; ++i) {
+    const int x = row_idx[i];
+    long j = i - 1;
+    while (j >= lo && row_idx[j] > x) {
+      row_idx[j + 1] = row_idx[j];
+      --j;
+    }
+    row_idx[j + 1] = x;
+  }
+}
+
+// --------------------------------------------------------- sparse: dQ
+// One block per query tile (4 waves x 16 queries), over its CSR row; K, V and
+// K^T (keys permuted for the dS contraction) staged in LDS, the next tile
+// prefetched into registers.  Adds scale * dS K to dq.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
+  constexpr int CPR = D / 8, NVU = 16 * CPR;   // threads staging 4 keys x 8 dims each
+  constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
+  __shared__ __align__(16) T Ks[64 * KSTR];
+  __shared__ __align__(16) T Vs[64 * KSTR];
+  __shared__ __align__(16) T Kt[D * VSTR];
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const T* Q = reinterpret_cast<const T*>(a.q) + base;
+  const T* K = reinterpret_cast<const T*>(a.k) + base;
+  const T* V = reinterpret_cast<const T*>(a.v) + base;
+  const T* G = reinterpret_cast<const T*>(a.dout) + base;
+  const int qrow = qa * 64 + 16 * w + l16;
+  const bool qvalid = qrow < a.N;
+  Frag<T> qf[D / 32], gf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    if (qvalid) {
+      load8(qf[c], Q + (size_t)qrow * D + 32 * c + 8 * g);
+      load8(gf[c], G + (size_t)qrow * D + 32 * c + 8 * g);
+    } else {
+      qf[c].zero();
+      gf[c].zero();
+    }
+  }
+  const float c2 = a.scale * kLog2e;
+  const float lse2 = qvalid ? a.lse[(size_t)bh * a.N_pad + qrow] * kLog2e : 0.f;
+  const float dd = qvalid ? a.dsum[(size_t)bh * a.N_pad + qrow] : 0.f;
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int beg = a.row_ptr[(size_t)bh * a.T + qa], end = a.row_ptr[(size_t)bh * a.T + qa + 1];
+  const int kg = tid % 16, c8 = tid / 16;
+  Chunk8<T> kc[4], vc[4];
+  auto load_tile = [&](int col) {
+    const bool ok = col >= 0 && col < a.T;
+    if (tid < NVU) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int gr = col * 64 + 4 * kg + ii;
+        if (ok && gr < a.N) {
+          gload8(kc[ii], K + (size_t)gr * D + c8 * 8);
+          gload8(vc[ii], V + (size_t)gr * D + c8 * 8);
+        } else {
+          zero8(kc[ii]);
+          zero8(vc[ii]);
+        }
+      }
+    }
+  };
+  if (beg < end) load_tile(a.col_idx[beg]);
+  for (int j = beg; j < end; ++j) {
+    const int col = a.col_idx[j];
+    __syncthreads();  // the previous tile's LDS reads are done
+    if (tid < NVU) {
+      const int p0 = vt_pos_a(4 * kg);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        lds_row(&Ks[(4 * kg + ii) * KSTR + c8 * 8], kc[ii]);
+        lds_row(&Vs[(4 * kg + ii) * KSTR + c8 * 8], vc[ii]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        st4v(&Kt[(c8 * 8 + e) * VSTR + p0], elem(kc[0], e), elem(kc[1], e), elem(kc[2], e), elem(kc[3], e));
+    }
+    __syncthreads();
+    if (j + 1 < end) load_tile(a.col_idx[j + 1]);
+    const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
+    if (kvalid <= 0) continue;
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<T> kf, vf;
+        load8(kf, &Ks[(16 * kb + l16) * KSTR + 32 * c + 8 * g]);
+        load8(vf, &Vs[(16 * kb + l16) * KSTR + 32 * c + 8 * g]);
+        mma(s[kb], kf, qf[c]);
+        mma(dp[kb], vf, gf[c]);
+      }
+    }
+    // dS^T (keys x queries), scale folded in
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (16 * kb + 4 * g + i < kvalid) ? exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
+        s[kb][i] = p * (dp[kb][i] - dd) * a.scale;
+      }
+    Frag<T> dsf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pack_rows(dsf[c], s[2 * c], s[2 * c + 1], 1.f);
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<T> ktf;
+        load8(ktf, &Kt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        mma(acc[jd], ktf, dsf[c]);
+      }
+  }
+  if (qvalid) {
+    float* out = a.dq + base + (size_t)qrow * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float4 o = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
+      o.x += acc[jd][0]; o.y += acc[jd][1]; o.z += acc[jd][2]; o.w += acc[jd][3];
+      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------- sparse: dK, dV
+// One block per key tile (4 waves x 16 keys), over the query tiles that keep
+// it (CSC, ascending); Q, dO, their transposes (queries permuted) and the
+// per-query lse and D staged in LDS.  Adds scale * dS^T Q to dk and P^T dO to dv.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
+  constexpr int CPR = D / 8, NVU = 16 * CPR;
+  constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
+  __shared__ __align__(16) T Qs[64 * KSTR];
+  __shared__ __align__(16) T Gs[64 * KSTR];
+  __shared__ __align__(16) T Qt[D * VSTR];
+  __shared__ __align__(16) T Gt[D * VSTR];
+  __shared__ float ls[64];
+  __shared__ float dsm[64];
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const T* Q = reinterpret_cast<const T*>(a.q) + base;
+  const T* K = reinterpret_cast<const T*>(a.k) + base;
+  const T* V = reinterpret_cast<const T*>(a.v) + base;
+  const T* G = reinterpret_cast<const T*>(a.dout) + base;
+  const int krow = kt * 64 + 16 * w + l16;
+  const bool kvalid = krow < a.N;
+  Frag<T> kf[D / 32], vf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    if (kvalid) {
+      load8(kf[c], K + (size_t)krow * D + 32 * c + 8 * g);
+      load8(vf[c], V + (size_t)krow * D + 32 * c + 8 * g);
+    } else {
+      kf[c].zero();
+      vf[c].zero();
+    }
+  }
+  const float c2 = a.scale * kLog2e;
+  f32x4 acck[NDB], accv[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    acck[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int beg = a.col_ptr[(size_t)bh * a.T + kt];
+  const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
+  const int kg = tid % 16, c8 = tid / 16;
+  Chunk8<T> qc[4], gc[4];
+  float lsv = INFINITY, dv0 = 0.f;
+  auto load_tile = [&](int row) {
+    if (tid < NVU) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int gr = row * 64 + 4 * kg + ii;
+        if (gr < a.N) {
+          gload8(qc[ii], Q + (size_t)gr * D + c8 * 8);
+          gload8(gc[ii], G + (size_t)gr * D + c8 * 8);
+        } else {
+          zero8(qc[ii]);
+          zero8(gc[ii]);
+        }
+      }
+    }
+    if (tid < 64) {
+      const int gr = row * 64 + tid;
+      lsv = gr < a.N ? a.lse[(size_t)bh * a.N_pad + gr] * kLog2e : INFINITY;  // no such query: P = 0
+      dv0 = gr < a.N ? a.dsum[(size_t)bh * a.N_pad + gr] : 0.f;
+    }
+  };
+  if (beg < end) load_tile(a.row_idx[beg]);
+  for (int j = beg; j < end; ++j) {
+    __syncthreads();
+    if (tid < NVU) {
+      const int p0 = vt_pos_a(4 * kg);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        lds_row(&Qs[(4 * kg + ii) * KSTR + c8 * 8], qc[ii]);
+        lds_row(&Gs[(4 * kg + ii) * KSTR + c8 * 8], gc[ii]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        st4v(&Qt[(c8 * 8 + e) * VSTR + p0], elem(qc[0], e), elem(qc[1], e), elem(qc[2], e), elem(qc[3], e));
+        st4v(&Gt[(c8 * 8 + e) * VSTR + p0], elem(gc[0], e), elem(gc[1], e), elem(gc[2], e), elem(gc[3], e));
+      }
+    }
+    if (tid < 64) {
+      ls[tid] = lsv;
+      dsm[tid] = dv0;
+    }
+    __syncthreads();
+    if (j + 1 < end) load_tile(a.row_idx[j + 1]);
+    // S, dP: queries x this wave's 16 keys; lane: key column, query rows 16 qb + 4 g + i
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<T> qfr, gfr;
+        load8(qfr, &Qs[(16 * qb + l16) * KSTR + 32 * c + 8 * g]);
+        load8(gfr, &Gs[(16 * qb + l16) * KSTR + 32 * c + 8 * g]);
+        mma(s[qb], qfr, kf[c]);
+        mma(dp[qb], gfr, vf[c]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = 16 * qb + 4 * g + i;
+        const float p = exp2f(fmaf(s[qb][i], c2, -ls[ql]));
+        s[qb][i] = p;
+        dp[qb][i] = p * (dp[qb][i] - dsm[ql]) * a.scale;
+      }
+    Frag<T> pf[2], dsf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      pack_rows(pf[c], s[2 * c], s[2 * c + 1], 1.f);
+      pack_rows(dsf[c], dp[2 * c], dp[2 * c + 1], 1.f);
+    }
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<T> gtf, qtf;
+        load8(gtf, &Gt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        load8(qtf, &Qt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        mma(accv[jd], gtf, pf[c]);
+        mma(acck[jd], qtf, dsf[c]);
+      }
+  }
+  if (kvalid) {
+    float* ok = a.dk + base + (size_t)krow * D;
+    float* ov = a.dv + base + (size_t)krow * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float4 x = *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g);
+      x.x += acck[jd][0]; x.y += acck[jd][1]; x.z += acck[jd][2]; x.w += acck[jd][3];
+      *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g) = x;
+      float4 y = *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g);
+      y.x += accv[jd][0]; y.y += accv[jd][1]; y.z += accv[jd][2]; y.w += accv[jd][3];
+      *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g) = y;
+    }
+  }
+}
+
+// ---------------------------------------------------- linear: query side
+// One block per (b, h, chunk of query tiles), 4 waves x 16 queries per tile.
+// Per query: the readout's forward quantities (x_q, phi_q, q', num, den), gW,
+// D = dO . O_s, the linear branch's dq (written to dq: the sparse kernel adds
+// to it), and the contributions to dS (through LDS: dnum and q' of the 64
+// queries, contracted over queries on the matrix cores) and dz.  One partial
+// dS, dz per block.
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
+  constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
+  constexpr int NFE = NDB * NRC * 512;
+  constexpr int GST = D + 4, QST = R + 4;       // LDS row strides (floats)
+  constexpr int NB = NDB * NRB, NBW = NB / 4;    // 16x16 blocks of dS^T, per wave
+  static_assert(NB % 4 == 0, "dS blocks per wave");
+  __shared__ __align__(16) float GN[64 * GST];
+  __shared__ __align__(16) float QP[64 * QST];
+  __shared__ float zred[4][R];
+
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int h = bh % a.H;
+  const int t0 = chunk * a.tpc, t1 = min(a.T, t0 + a.tpc);
+  if (t0 >= t1) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const T* Q = reinterpret_cast<const T*>(a.q) + base;
+  const T* G = reinterpret_cast<const T*>(a.dout) + base;
+  const T* OS = reinterpret_cast<const T*>(a.os) + base;
+  const T* UQF = reinterpret_cast<const T*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
+  const T* UQ = reinterpret_cast<const T*>(a.uq) + (size_t)h * D * R;
+  const T* WO = reinterpret_cast<const T*>(a.wo) + (size_t)h * D * D;
+  const float* SF = a.s_frag + (size_t)bh * NFE;
+  const float* SP = a.s_plain + (size_t)bh * R * D;
+  const float* Z = a.z + (size_t)bh * R;
+
+  f32x4 dsacc[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) dsacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dzl[NRB][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dzl[rb][i] = 0.f;
+
+  for (int t = t0; t < t1; ++t) {
+    const int qrow = t * 64 + 16 * w + l16;
+    const bool qvalid = qrow < a.N;
+    Frag<T> qf[D / 32], gf[D / 32];
+    float gos = 0.f;  // dO . O_s, this lane's share
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (qvalid) {
+        load8(qf[c], Q + (size_t)qrow * D + 32 * c + 8 * g);
+        load8(gf[c], G + (size_t)qrow * D + 32 * c + 8 * g);
+        float gx[8], ox[8];
+        load8_any(gx, G + (size_t)qrow * D + 32 * c + 8 * g);
+        load8_any(ox, OS + (size_t)qrow * D + 32 * c + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gos = fmaf(gx[e], ox[e], gos);
+      } else {
+        qf[c].zero();
+        gf[c].zero();
+      }
+    }
+    gos = group4_sum(gos);
+    // x_q^T = U_q^T q^T; phi; den; q' = rope(phi)
+    f32x4 xq[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      xq[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<T> uf;
+        load8(uf, UQF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+        mma(xq[rb], uf, qf[c]);
+      }
+    }
+    const int tok = qvalid ? qrow : 0;
+    float fq[NRB][4], qp[NRB][4];
+    float den = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fq[rb][i] = elu1(xq[rb][i]);
+        den = fmaf(fq[rb][i], Z[16 * rb + 4 * g + i], den);
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, (16 * rb + 4 * g) / 2 + pr);
+        const float x0 = fq[rb][2 * pr], x1 = fq[rb][2 * pr + 1];
+        qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
+        qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+    den = group4_sum(den);
+    const float invden = 1.f / den;
+    Frag<T> qpf[NRC];
+#pragma unroll
+    for (int rc = 0; rc < NRC; ++rc) {
+      const f32x4 lo = f32x4{qp[2 * rc][0], qp[2 * rc][1], qp[2 * rc][2], qp[2 * rc][3]};
+      const f32x4 hi = (2 * rc + 1 < NRB) ? f32x4{qp[2 * rc + 1][0], qp[2 * rc + 1][1], qp[2 * rc + 1][2],
+                                                  qp[2 * rc + 1][3]}
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+      pack_rows(qpf[rc], lo, hi, 1.f);
+    }
+    // num^T = S^T q'^T and gW^T = W_o dO^T (rows d, query columns)
+    f32x4 num[NDB], gw[NDB];
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      num[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gw[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rc = 0; rc < NRC; ++rc) {
+        float x[8];
+        load8f(x, SF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        Frag<T> hi, lo;
+        split8(x, hi, lo);
+        mma_hl(num[jd], hi, lo, qpf[rc]);
+      }
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<T> wf;
+        load8(wf, WO + (size_t)(16 * jd + l16) * D + 32 * c + 8 * g);
+        mma(gw[jd], wf, gf[c]);
+      }
+    }
+    float gwol = 0.f;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gwol = fmaf(gw[jd][i], num[jd][i] * invden, gwol);
+    gwol = group4_sum(gwol);
+    const float gden = -gwol * invden;
+    if (g == 0 && qvalid) a.dsum[(size_t)bh * a.N_pad + qrow] = gos;
+    // dnum = gW / den as B fragments (chunks of 32 d); dq' = S dnum
+    Frag<T> gnf[D / 32];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) pack_rows(gnf[c], gw[2 * c], gw[2 * c + 1], invden);
+    f32x4 dqp[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      dqp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const float* sp = SP + (size_t)(16 * rb + l16) * D + 32 * c + 4 * g;
+        float x[8];
+        load4_any(x, sp);
+        load4_any(x + 4, sp + 16);
+        Frag<T> hi, lo;
+        split8(x, hi, lo);
+        mma_hl(dqp[rb], hi, lo, gnf[c]);
+      }
+    }
+    // dx_q = (dden z + rho^T dq') * phi'(x_q)
+    float dx[NRB][4];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int m = 16 * rb + 4 * g + 2 * pr;
+        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
+        const float x0 = dqp[rb][2 * pr], x1 = dqp[rb][2 * pr + 1];
+        const float d0 = fmaf(gden, Z[m], x0 * cs.x + x1 * cs.y);
+        const float d1 = fmaf(gden, Z[m + 1], -x0 * cs.y + x1 * cs.x);
+        const float e0 = xq[rb][2 * pr], e1 = xq[rb][2 * pr + 1];
+        dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : fq[rb][2 * pr]);
+        dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : fq[rb][2 * pr + 1]);
+      }
+    Frag<T> dxf[NRC];
+#pragma unroll
+    for (int rc = 0; rc < NRC; ++rc) {
+      const f32x4 lo = f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]};
+      const f32x4 hi = (2 * rc + 1 < NRB) ? f32x4{dx[2 * rc + 1][0], dx[2 * rc + 1][1], dx[2 * rc + 1][2],
+                                                  dx[2 * rc + 1][3]}
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};
+      pack_rows(dxf[rc], lo, hi, 1.f);
+    }
+    float* dqo = a.dq + base + (size_t)qrow * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rc = 0; rc < NRC; ++rc) {
+        Frag<T> uf;
+        param_perm_frag<T, R>(uf, UQ, 16 * jd + l16, rc, g);
+        mma(acc, uf, dxf[rc]);
+      }
+      *reinterpret_cast<float4*>(dqo + 16 * jd + 4 * g) =
+          qvalid ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // contributions to dz and dS
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dzl[rb][i] = fmaf(gden, fq[rb][i], dzl[rb][i]);
+    const int ql = 16 * w + l16;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+      *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
+          make_float4(gw[jd][0] * invden, gw[jd][1] * invden, gw[jd][2] * invden, gw[jd][3] * invden);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =
+          make_float4(qp[rb][0], qp[rb][1], qp[rb][2], qp[rb][3]);
+    __syncthreads();
+    // dS^T (d x r) += dnum^T q' over the tile's 64 queries
+#pragma unroll
+    for (int ii = 0; ii < NBW; ++ii) {
+      const int bi = w + 4 * ii, je = bi % NDB, rb = bi / NDB;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[8], y[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int qq = 32 * c + 8 * g + s2;
+          x[s2] = GN[qq * GST + 16 * je + l16];
+          y[s2] = QP[qq * QST + 16 * rb + l16];
+        }
+        Frag<T> hi, lo, qb;
+        split8(x, hi, lo);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) qb.set_pair(p, y[2 * p], y[2 * p + 1]);
+        mma_hl(dsacc[ii], hi, lo, qb);
+      }
+    }
+    __syncthreads();
+  }
+  // partials: dS [r][d] rows m = 16 rb + l16, columns 16 je + 4 g .. + 3
+  const size_t pb = (size_t)bh * a.nchunk + chunk;
+#pragma unroll
+  for (int ii = 0; ii < NBW; ++ii) {
+    const int bi = w + 4 * ii, je = bi % NDB, rb = bi / NDB;
+    *reinterpret_cast<float4*>(&a.part_ds[(pb * R + 16 * rb + l16) * D + 16 * je + 4 * g]) =
+        make_float4(dsacc[ii][0], dsacc[ii][1], dsacc[ii][2], dsacc[ii][3]);
+  }
+  // dz: sum over the 16 query lanes of each lane group, then over the waves
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = dzl[rb][i];
+      x += wave_xor(x, 1);
+      x += wave_xor(x, 2);
+      x += wave_xor(x, 4);
+      x += wave_xor(x, 8);
+      if (l16 == 0) zred[w][16 * rb + 4 * g + i] = x;
+    }
+  __syncthreads();
+  if (tid < R) a.part_dz[pb * R + tid] = (zred[0][tid] + zred[1][tid]) + (zred[2][tid] + zred[3][tid]);
+}
+
+// ------------------------------------------------ linear: partial sums
+// Per (b, h) and slice of 8 rank rows: dS = sum of the partials (fixed
+// order), written plain and as float readout A fragments of dS^T; the first
+// slice also writes dz and zero-fills the fragment slots past r, and, for
+// the heads of batch 0, U_k^T as A fragments.
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void k_bwd_fin(BwdArgs a) {
+  constexpr int NRB = R / 16, NRC = (R + 31) / 32, NFE = (D / 16) * NRC * 512;
+  const int tid = threadIdx.x, bh = blockIdx.x, h = bh % a.H;
+  const int r0 = blockIdx.y * 8;
+  float* fr = a.ds_frag + (size_t)bh * NFE;
+  for (int e = tid; e < 8 * D; e += 256) {
+    const int rr = r0 + e / D, col = e % D;
+    float s = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) s += a.part_ds[(((size_t)bh * a.nchunk + c) * R + rr) * D + col];
+    a.ds_plain[((size_t)bh * R + rr) * D + col] = s;
+    fr[sp_frag_index<D, R>(rr, col)] = s;
+  }
+  if (blockIdx.y == 0) {
+    for (int e = tid; e < (32 * NRC - R) * D; e += 256) fr[sp_frag_index<D, R>(R + e / D, e % D)] = 0.f;
+    if (tid < R) {
+      float s = 0.f;
+      for (int c = 0; c < a.nchunk; ++c) s += a.part_dz[((size_t)bh * a.nchunk + c) * R + tid];
+      a.dz[(size_t)bh * R + tid] = s;
+    }
+    if (bh < a.H) {  // U_k^T fragments: frag (rb, c), lane l, slot s -> U_k[32 c + 8 (l/16) + s][16 rb + l%16]
+      const int nue = NRB * (D / 32) * 512;
+      const T* U = reinterpret_cast<const T*>(a.uk) + (size_t)h * D * R;
+      T* out = reinterpret_cast<T*>(a.uk_frag) + (size_t)h * nue;
+      for (int idx = tid; idx < nue; idx += 256) {
+        const int s2 = idx & 7, l = (idx >> 3) & 63, f = idx >> 9;
+        const int c = f % (D / 32), rbk = f / (D / 32);
+        out[idx] = U[(size_t)(32 * c + 8 * (l >> 4) + s2) * R + 16 * rbk + (l & 15)];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ linear: key side
+// One block per key tile (4 waves x 16 keys): x_k, phi_k, k', then
+// dk' = dS v, dv = dS^T k' and dk = ((dz + rho^T dk') * phi'(x_k)) U_k^T,
+// written to dk and dv (pad rows 0; the sparse kernel adds to them).
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void k_bwd_k(BwdArgs a) {
+  constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
+  constexpr int NFE = NDB * NRC * 512;
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
+  const int h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const T* K = reinterpret_cast<const T*>(a.k) + base;
+  const T* V = reinterpret_cast<const T*>(a.v) + base;
+  const T* UKF = reinterpret_cast<const T*>(a.uk_frag) + (size_t)h * NRB * (D / 32) * 512;
+  const T* UK = reinterpret_cast<const T*>(a.uk) + (size_t)h * D * R;
+  const float* DSF = a.ds_frag + (size_t)bh * NFE;
+  const float* DSP = a.ds_plain + (size_t)bh * R * D;
+  const float* DZ = a.dz + (size_t)bh * R;
+  const int krow = kt * 64 + 16 * w + l16;
+  const bool kvalid = krow < a.N;
+  Frag<T> kf[D / 32], vf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    if (kvalid) {
+      load8(kf[c], K + (size_t)krow * D + 32 * c + 8 * g);
+      load8(vf[c], V + (size_t)krow * D + 32 * c + 8 * g);
+    } else {
+      kf[c].zero();
+      vf[c].zero();
+    }
+  }
+  f32x4 xk[NRB], dkp[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    xk[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dkp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      Frag<T> uf;
+      load8(uf, UKF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+      mma(xk[rb], uf, kf[c]);
+      float x[8];
+      load8f(x, DSP + (size_t)(16 * rb + l16) * D + 32 * c + 8 * g);
+      Frag<T> hi, lo;
+      split8(x, hi, lo);
+      mma_hl(dkp[rb], hi, lo, vf[c]);
+    }
+  }
+  const int tok = kvalid ? krow : 0;
+  float fk[NRB][4], kp[NRB][4], dx[NRB][4];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int m = 16 * rb + 4 * g + 2 * pr;
+      const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
+      const float e0 = xk[rb][2 * pr], e1 = xk[rb][2 * pr + 1];
+      const float f0 = elu1(e0), f1 = elu1(e1);
+      fk[rb][2 * pr] = f0;
+      fk[rb][2 * pr + 1] = f1;
+      kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
+      kp[rb][2 * pr + 1] = f0 * cs.y + f1 * cs.x;
+      const float x0 = dkp[rb][2 * pr], x1 = dkp[rb][2 * pr + 1];
+      const float d0 = DZ[m] + (x0 * cs.x + x1 * cs.y);
+      const float d1 = DZ[m + 1] + (-x0 * cs.y + x1 * cs.x);
+      dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : f0);
+      dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : f1);
+    }
+  Frag<T> kpf[NRC], dxf[NRC];
+#pragma unroll
+  for (int rc = 0; rc < NRC; ++rc) {
+    const bool two = 2 * rc + 1 < NRB;
+    const int b1 = two ? 2 * rc + 1 : 2 * rc;
+    const float keep = two ? 1.f : 0.f;
+    pack_rows(kpf[rc], f32x4{kp[2 * rc][0], kp[2 * rc][1], kp[2 * rc][2], kp[2 * rc][3]},
+              f32x4{keep * kp[b1][0], keep * kp[b1][1], keep * kp[b1][2], keep * kp[b1][3]}, 1.f);
+    pack_rows(dxf[rc], f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]},
+              f32x4{keep * dx[b1][0], keep * dx[b1][1], keep * dx[b1][2], keep * dx[b1][3]}, 1.f);
+  }
+  float* dko = a.dk + base + (size_t)krow * D;
+  float* dvo = a.dv + base + (size_t)krow * D;
+#pragma unroll
+  for (int jd = 0; jd < NDB; ++jd) {
+    f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f}, ak = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rc = 0; rc < NRC; ++rc) {
+      float x[8];
+      load8f(x, DSF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+      Frag<T> hi, lo;
+      split8(x, hi, lo);
+      mma_hl(av, hi, lo, kpf[rc]);
+      Frag<T> uf;
+      param_perm_frag<T, R>(uf, UK, 16 * jd + l16, rc, g);
+      mma(ak, uf, dxf[rc]);
+    }
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dko + 16 * jd + 4 * g) = kvalid ? make_float4(ak[0], ak[1], ak[2], ak[3]) : zero;
+    *reinterpret_cast<float4*>(dvo + 16 * jd + 4 * g) = kvalid ? make_float4(av[0], av[1], av[2], av[3]) : zero;
+  }
+}
+
+// ------------------------------------------------------------- launcher
+template <typename T, int D, int R>
+static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_t st) {
+  hipError_t e;
+  k_bwd_q<T, D, R><<<dim3(a.nchunk, s.B * s.H), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_bwd_fin<T, D, R><<<dim3(s.B * s.H, R / 8), 256, 0, st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  k_bwd_k<T, D, R><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t bwd_linear_by_shape(const Shape& s, const BwdArgs& a, hipStream_t st) {
+  if (s.d == 64) {
+    if (s.rank == 16) return bwd_launch_linear<T, 64, 16>(s, a, st);
+    if (s.rank == 32) return bwd_launch_linear<T, 64, 32>(s, a, st);
+    return bwd_launch_linear<T, 64, 64>(s, a, st);
+  }
+  if (s.rank == 16) return bwd_launch_linear<T, 128, 16>(s, a, st);
+  if (s.rank == 32) return bwd_launch_linear<T, 128, 32>(s, a, st);
+  return bwd_launch_linear<T, 128, 64>(s, a, st);
+}
+
+// CSC of the mask, then the sparse dQ and dK/dV kernels.  csc_cnt: [BH*T]
+// scratch; col_ptr [BH*T + 1]; row_idx capacity `cap`.
+template <typename T>
+static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_t* col_ptr, int32_t* row_idx,
+                             long cap, hipStream_t st) {
+  hipError_t e;
+  const int rows = s.B * s.H * s.T;
+  k_zero_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
+  k_csc_pass<false><<<(rows + 255) / 256, 256, 0, st>>>(rows, s.T, a.row_ptr, a.col_idx, csc_cnt, nullptr,
+                                                        nullptr, cap);
+  k_csc_scan<<<1, 1024, 0, st>>>(rows, csc_cnt, col_ptr);
+  k_zero_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
+  k_csc_pass<true><<<(rows + 255) / 256, 256, 0, st>>>(rows, s.T, a.row_ptr, a.col_idx, csc_cnt, col_ptr,
+                                                       row_idx, cap);
+  k_csc_sort<<<(rows + 255) / 256, 256, 0, st>>>(rows, col_ptr, row_idx, cap);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.csc_cap = cap;
+  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
+  if (s.d == 64) {
+    k_bwd_dq<T, 64><<<grid, 256, 0, st>>>(a);
+    k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);
+  } else {
+    k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);
+    k_bwd_dkv<T, 128><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const Shape& s, const BwdArgs& a, int32_t* csc_cnt, int32_t* col_ptr, int32_t* row_idx,
+                          long cap, bool linear_part, hipStream_t st);
+
+}  // namespace hsa

@@ -165,6 +165,30 @@ __device__ __forceinline__ float elem(const Chunk8<fp8_t>& c, int e) {
   }
 }
 
+// Position of key `key` (0..63) of a tile staged transposed for a
+// contraction over keys: within each 32-key chunk, key 16h + 4g + i sits at
+// 8g + 4h + i, so that lane group g reads its eight slots as one run.
+__device__ __forceinline__ int vt_pos_a(int key) {
+  int c = key >> 5, kk = key & 31;
+  int h = kk >> 4, g = (kk >> 2) & 3, i = kk & 3;
+  return 32 * c + 8 * g + 4 * h + i;
+}
+
+__device__ __forceinline__ void st4o(bf16_t* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ void st4o(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void st4v(bf16_t* dst, float a, float b, float c, float d) { st4o(dst, a, b, c, d); }
+__device__ __forceinline__ void st4v(float* dst, float a, float b, float c, float d) { st4o(dst, a, b, c, d); }
+
+__device__ __forceinline__ void lds_row(bf16_t* dst, const Chunk8<bf16_t>& c) { *reinterpret_cast<u32x4*>(dst) = c.w; }
+__device__ __forceinline__ void lds_row(float* dst, const Chunk8<float>& c) {
+  reinterpret_cast<float4*>(dst)[0] = c.a;
+  reinterpret_cast<float4*>(dst)[1] = c.b;
+}
+
 // ---------------------------------------------------------------------------
 // wave utilities
 // ---------------------------------------------------------------------------

@@ -38,6 +38,7 @@ hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const
   a.part_s = w.part_s; a.part_z = w.part_z; a.wo = wo; a.uq = uq;
   a.sp_frag = w.sp_frag; a.z = w.z; a.uq_frag = w.uq_frag;
   if (s.compl_keys) { a.s_full = w.s_full; a.wo_frag = w.wo_frag; }
+  if (w.s_plain) { a.s_full = w.s_full; a.s_plain = w.s_plain; }  // backward pass
   if (s.dt == Dt::F32) return launch_finalize_f32(s, a, st);
   return finalize_by_shape<bf16_t>(s, a, st);
 }

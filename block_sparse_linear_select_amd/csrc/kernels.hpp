@@ -67,6 +67,21 @@ struct Scratch {
   float* tile_z = nullptr;     // [BH][T][r] per-tile feature sums
   float* s_full = nullptr;     // [BH] full state S (before W_o) as float readout fragments
   void* wo_frag = nullptr;     // [H] W_o^T as matrix-core A fragments
+  // backward pass
+  float* s_plain = nullptr;    // [BH][r][d] S (before W_o)
+  void* os = nullptr;          // [BH][N_pad][d] sparse-branch output, output type
+  float* lse = nullptr;        // [BH][N_pad]
+  float* dsum = nullptr;       // [BH][N_pad] dO . O_s
+  float* part_ds = nullptr;    // [BH][chunks][r][d]
+  float* part_dz = nullptr;    // [BH][chunks][r]
+  float* ds_plain = nullptr;   // [BH][r][d]
+  float* ds_frag = nullptr;    // [BH] dS^T as float readout fragments
+  float* dz = nullptr;         // [BH][r]
+  void* uk_frag = nullptr;     // [H] U_k^T as A fragments
+  int32_t* csc_cnt = nullptr;  // [BH*T]
+  int32_t* col_ptr = nullptr;  // [BH*T + 1]
+  int32_t* row_idx = nullptr;  // [BH*T*kmax]
+  long csc_cap = 0;
 };
 
 // Workspace planning: byte offsets of each region for a given call.
@@ -76,10 +91,12 @@ struct Plan {
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
   size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
   size_t off_tile_s = 0, off_tile_z = 0, off_s_full = 0, off_wo = 0;
-  bool select = false, csr_internal = false, linear = false, vt = false, compl_keys = false;
+  size_t off_s_plain = 0, off_os = 0, off_lse = 0, off_dsum = 0, off_part_ds = 0, off_part_dz = 0;
+  size_t off_ds_plain = 0, off_ds_frag = 0, off_dz = 0, off_uk = 0, off_csc_cnt = 0, off_col_ptr = 0, off_row_idx = 0;
+  bool select = false, csr_internal = false, linear = false, vt = false, compl_keys = false, backward = false;
 };
 
-Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt);
+Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt, bool backward = false);
 Scratch bind_plan(const Plan& p, void* ws);
 
 // Launchers: each enqueues its kernels on `st` and returns hipSuccess or the
@@ -97,6 +114,13 @@ hipError_t launch_attend(const Shape& s, const void* q, const void* k, const voi
                          const float* qs, const float* ks, const float* vs,
                          const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,
                          const Scratch& w, void* o, float* lse, hipStream_t st);
+// Backward pass pieces (float32 gradients): part 1 = the linear branch (its dq,
+// dk, dv written, D written), part 2 = the transposed mask and the sparse
+// branch (dq, dk, dv added to).
+hipError_t launch_backward(const Shape& s, const void* q, const void* k, const void* v, const void* dout,
+                           const void* uq, const void* uk, const void* wo, const int32_t* row_ptr,
+                           const int32_t* col_idx, const Scratch& w, float* dq, float* dk, float* dv, int part,
+                           hipStream_t st);
 // The complement variant's O_l W_o: added to o (which holds O_s) when `add`,
 // else written to o.
 hipError_t launch_compl(const Shape& s, const void* q, const float* qs, const int32_t* row_ptr,

@@ -514,6 +514,7 @@ struct FinalArgs {
   float* z;
   void* uq_frag;
   float* s_full;   // optional: [BH] S itself (before W_o) as float readout A fragments
+  float* s_plain;  // optional: [BH][r][d] S itself (before W_o)
   void* wo_frag;   // optional: [H] W_o^T as A fragments
 };
 
@@ -560,6 +561,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
     a.z[(size_t)bh * R + tid] = s;
   }
   __syncthreads();
+  if (a.s_plain) {
+    for (int e = tid; e < kFinRows * D; e += 256) a.s_plain[((size_t)bh * R + r0) * D + e] = S[e];
+  }
   if (a.s_full) {
     constexpr int NFE = (D / 16) * NRC * 512;
     float* sf = a.s_full + (size_t)bh * NFE;

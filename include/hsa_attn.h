@@ -106,7 +106,8 @@ enum { /* which call a workspace size is asked for */
   HSA_ATTN_CALL_SPARSE = 1,
   HSA_ATTN_CALL_LINEAR = 2,
   HSA_ATTN_CALL_HYBRID = 3,
-  HSA_ATTN_CALL_LINEAR_COMPLEMENT = 4
+  HSA_ATTN_CALL_LINEAR_COMPLEMENT = 4,
+  HSA_ATTN_CALL_BACKWARD = 5
 };
 
 typedef struct hsa_attn_desc {
@@ -156,7 +157,9 @@ enum {
   HSA_ATTN_KERNEL_QUANT = 6,     /* per-row FP8 quantisation of activations */
   HSA_ATTN_KERNEL_PROJ = 7,      /* W8A8 FP8 QKV projection with fused output quantisation */
   HSA_ATTN_KERNEL_COMPL = 8,     /* linear branch over the complement of the kept tiles */
-  HSA_ATTN_KERNEL_KINDS = 9
+  HSA_ATTN_KERNEL_BWD_LINEAR = 9,  /* backward: linear branch (query side, sums, key side) */
+  HSA_ATTN_KERNEL_BWD_SPARSE = 10, /* backward: transposed mask, sparse dQ and dK/dV */
+  HSA_ATTN_KERNEL_KINDS = 11
 };
 int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
@@ -236,6 +239,31 @@ int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     const int32_t* row_ptr_in, const int32_t* col_idx_in,
                     int32_t* row_ptr_out, int32_t* col_idx_out,
                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of the hybrid (all-keys linear branch) on the forward's mask:
+ * the gradients of L with respect to Q, K and V given dL/dO = d_o, with the
+ * tile selection held fixed (it is piecewise constant in the inputs).  The
+ * forward's linear state and the sparse branch's output and log-sum-exp are
+ * recomputed from q, k, v, so nothing of the forward call is needed besides
+ * its mask.  Sparse branch: P = softmax(scale q k^T) over the kept keys,
+ * dS = P * (dO v^T - D) with D_i = dO_i . O_s,i; dq += scale dS k,
+ * dk += scale dS^T q, dv += P^T dO.  Linear branch: the chain rule through
+ * O_l = num / den (see hsa_linear_attn), S and z.
+ *   q, k, v: [B, H, N_pad, d] float32 or bf16 (HSA_ATTN_ERR_DTYPE for FP8);
+ *   U_q, U_k, W_o as for the forward; row_ptr / col_idx: the forward's CSR
+ *   with at most topk + force_diag entries per row (longer rows give
+ *   unspecified gradients); d_o: [B, H, N_pad, d] in the input type (rows
+ *   >= N are ignored).
+ *   d_q, d_k, d_v: float32 [B, H, N_pad, d], written in full (rows >= N zero).
+ *   desc->linear_keys must be HSA_ATTN_LINEAR_ALL_KEYS (HSA_ATTN_ERR_SHAPE
+ *   otherwise).  Workspace: HSA_ATTN_CALL_BACKWARD.
+ */
+int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                             const void* U_q, const void* U_k, const void* W_o,
+                             const int32_t* row_ptr, const int32_t* col_idx, const void* d_o,
+                             float* d_q, float* d_k, float* d_v,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * W8A8 FP8 projections in front of the attention (SparkDiffusion news

@@ -1,0 +1,114 @@
+"""GPU parity of the backward pass (dQ, dK, dV on a fixed mask) against the
+fp64 oracle, through the C ABI.
+
+Each case: the oracle's own mask, a seeded upstream gradient (pad rows hold
+garbage the library must ignore), and relative L2 error over the valid rows
+of all heads, per gradient: the whole hybrid, the sparse branch alone (W_o = 0
+makes the linear branch's gradient vanish) and the linear branch alone (the
+difference of the two GPU results, whose sparse parts are computed
+identically).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_linear_select_amd import binding as B
+from oracle import rola as R
+from tests import helpers as Hp
+from workloads.gen import to_fp64, upstream_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+# bf16: the recomputed probabilities, dS and the operands of every product are
+# rounded to bf16 (relative 2^-9 each) and D comes from the bf16-rounded O_s;
+# float32: accumulation order and the hardware exp2 only.
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+NAMES = ["tiny_f32", "bf16_ragged", "bf16_r64", "bf16_d64_r16", "bf16_aligned_diag", "f32_d128_r64",
+         "bf16_dense_all_tiles", "bf16_long_rows", "bf16_many_heads"]
+
+
+def _run(cfg, d, rp, ci, g, wo=None):
+    return B.hybrid_attn_backward(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"] if wo is None else wo,
+                                  rp, ci, g)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_backward_on_oracle_mask(name):
+    print(f"\n[case {name}]", flush=True)
+    inp = Hp.gen(name)
+    w = inp.w
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rows = {bh: Hp.oracle_mask_head(inp, *bh)[1] for bh in heads}
+    rp, ci = Hp.csr_tensors([rows[bh] for bh in heads], DEV)
+    g = upstream_grad(w, seed=w.seed + 7, pad_value=3.0)
+    gd = g.to(DEV)
+    full = _run(cfg, d, rp, ci, gd)
+    sparse = _run(cfg, d, rp, ci, gd, wo=torch.zeros_like(d["wo"]))
+    again = _run(cfg, d, rp, ci, gd)
+    torch.cuda.synchronize()
+    for x, y in zip(full, again):
+        assert torch.equal(x, y)  # bitwise reproducible
+    full = [t.cpu().numpy() for t in full]
+    sparse = [t.cpu().numpy() for t in sparse]
+    errs = {k: [Hp.RelL2() for _ in range(3)] for k in ("hybrid", "sparse", "linear")}
+    for b, h in heads:
+        q, k, v = Hp.head_arrays(inp, b, h)
+        uq, uk, wo = Hp.params(inp, h)
+        gh = to_fp64(g[b, h])
+        gh[w.N:] = 0.0
+        ref_s = R.sparse_backward(q, k, v, w.N, rows[(b, h)], w.softmax_scale, gh)
+        pos = R.token_positions(w.grid, w.N)
+        ref_l = R.linear_backward(q, k, v, w.N, uq, uk, pos, w.rope_base, gh @ wo.T)
+        for t in range(3):
+            errs["hybrid"][t].add(full[t][b, h, :w.N], (ref_s[t] + ref_l[t])[:w.N])
+            errs["sparse"][t].add(sparse[t][b, h, :w.N], ref_s[t][:w.N])
+            errs["linear"][t].add((full[t] - sparse[t])[b, h, :w.N], ref_l[t][:w.N])
+            assert np.all(full[t][b, h, w.N:] == 0)
+    for key, e in errs.items():
+        print(f"  {key}: dQ {e[0].value:.2e}  dK {e[1].value:.2e}  dV {e[2].value:.2e}", flush=True)
+    for key, e in errs.items():
+        for t in range(3):
+            assert e[t].value <= TOL[w.dtype], (key, t, e[t].value)
+
+
+def test_backward_workspace_contents_do_not_matter(monkeypatch):
+    w = Hp.CASES["bf16_ragged"]
+    inp = Hp.gen(w)
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rp, ci = Hp.csr_tensors([Hp.oracle_mask_head(inp, *bh)[1] for bh in heads], DEV)
+    gd = upstream_grad(w, seed=5).to(DEV)
+
+    def run(fill):
+        monkeypatch.setattr(B, "_workspace", lambda c, call, dev: torch.full(
+            (max(B.workspace_size(c, call), 256),), fill, dtype=torch.uint8, device=dev))
+        out = _run(cfg, d, rp, ci, gd)
+        torch.cuda.synchronize()
+        return [t.clone() for t in out]
+
+    for x, y in zip(run(0), run(255)):
+        assert torch.equal(x, y)
+
+
+def test_backward_rejects_fp8_and_the_complement_variant():
+    import dataclasses
+    w = Hp.CASES["fp8_ragged"]
+    inp = Hp.gen(w)
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    rp = torch.zeros(cfg.B * cfg.H * cfg.T + 1, dtype=torch.int32, device=DEV)
+    ci = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(B.HsaError):
+        B.hybrid_attn_backward(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], rp, ci, d["q"])
+    w2 = Hp.CASES["bf16_ragged"]
+    inp2 = Hp.gen(w2)
+    d2 = Hp.to_device(inp2, DEV)
+    cfg2 = dataclasses.replace(B.Config.from_workload(w2), linear_keys="complement")
+    rp2 = torch.zeros(cfg2.B * cfg2.H * cfg2.T + 1, dtype=torch.int32, device=DEV)
+    with pytest.raises(B.HsaError):
+        B.hybrid_attn_backward(cfg2, d2["q"], d2["k"], d2["v"], d2["uq"], d2["uk"], d2["wo"], rp2, ci, d2["q"])

@@ -285,3 +285,15 @@ def fp8_codes(t: torch.Tensor) -> np.ndarray:
     """The raw E4M3FN byte codes of a float8_e4m3fn tensor, as uint8."""
     assert t.dtype == torch.float8_e4m3fn
     return t.view(torch.uint8).numpy()
+
+
+def upstream_grad(w: Workload, seed: int, pad_value: float = 0.0) -> torch.Tensor:
+    """An upstream gradient dL/dO for the backward pass: N(0, 1) from
+    PCG64(seed) in float32, stored in the workload's input type (bf16 RNE, or
+    float32), shape [B, H, N_pad, d].  Rows past N hold `pad_value` (the
+    library ignores them)."""
+    assert w.dtype in ("f32", "bf16"), "the backward pass takes float32 or bf16 inputs"
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = torch.from_numpy(rng.standard_normal((w.B, w.H, w.N_pad, w.d)).astype(np.float32))
+    x[:, :, w.N:] = pad_value
+    return x.to(torch.float32 if w.dtype == "f32" else torch.bfloat16)

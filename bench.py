@@ -177,6 +177,48 @@ def bench_compl(w, cfg, d, sc, args, dev):
     return {"ms_per_call": ms, "kernels_ms": kern, "compl_kernel": compl_figures(w, kern["compl"])}
 
 
+def bench_backward(w, cfg, d, args, dev):
+    """Backward calls (dQ, dK, dV float32 for a seeded dO) on the mask the
+    hybrid call selects, timed like the forward.  The sparse part recomputes
+    P and dP per kept tile pair and forms dS, dQ, dK, dV: 5 products of
+    2*64*64*d FLOP per pair (QK^T twice, dO V^T twice, dS K, dS^T Q and P^T dO,
+    i.e. 7 products, as the dQ and dK/dV kernels each recompute QK^T and dO V^T)."""
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+    from workloads.gen import upstream_grad
+
+    sel = B.HybridPlan(cfg, dev, export_mask=True)
+    sel.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"])
+    g = upstream_grad(w, seed=w.seed + 7).to(dev)
+    run = lambda: B.hybrid_attn_backward(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sel.row_ptr,
+                                         sel.col_idx, g)
+    for _ in range(max(1, args.warmup // 2)):
+        run()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 2)
+    B.timing_enable(steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt = B.timing_read()
+    B.timing_enable(0)
+    kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    log(f"  {steps} backward calls: {ms:.3f} ms/call (sparse part {kern['bwd_sparse']:.3f} ms)")
+    pairs = w.B * w.H * w.T * w.topk
+    flops = 7 * 2.0 * 64 * 64 * w.d * pairs
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else 157.3
+    ach = flops / (kern["bwd_sparse"] * 1e-3) / 1e12
+    return {"ms_per_call": ms, "kernels_ms": kern, "steps": steps,
+            "sparse_roofline": {"bound": "mfma", "kernel": "k_bwd_dq + k_bwd_dkv (+ transposed mask)",
+                                "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                                "flop": flops}}
+
+
 def compl_figures(w, cms):
     """Bytes of the complement kernel per call: the per-row state sums read
     min(k, T - k) tile states per row (before the reuse that four rows per
@@ -214,6 +256,8 @@ def main():
     ap.add_argument("--no-compl", action="store_true",
                     help="skip the fourth measurement: hybrid calls whose linear branch sums over the complement "
                          "of each row's kept tiles")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the fifth measurement: the backward pass (dQ, dK, dV) on the selected mask")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
                          "MiB each (reference for HBM byte counters)")
@@ -330,6 +374,8 @@ def main():
                              "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
     if not args.no_proj and w.d == 128:
         out["qkv_proj"] = bench_proj(w, args, dev)
+    if not args.no_bwd and w.dtype != "fp8" and args.linear_keys == "all":
+        out["backward"] = bench_backward(w, cfg, d, args, dev)
     if args.linear_keys == "complement":
         out["compl_kernel"] = compl_figures(w, kern["compl"])
     elif not args.no_compl:

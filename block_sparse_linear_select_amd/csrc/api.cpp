@@ -87,6 +87,7 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     p.off_csc_cnt = take(rows * sizeof(int32_t));
     p.off_col_ptr = take((rows + 1) * sizeof(int32_t));
     p.off_row_idx = take(rows * s.kmax * sizeof(int32_t));
+    p.off_csc_bits = take(rows * (size_t)((s.T + 31) / 32) * sizeof(uint32_t));
   }
   p.total = off;
   return p;
@@ -136,6 +137,7 @@ Scratch bind_plan(const Plan& p, void* ws) {
     w.csc_cnt = reinterpret_cast<int32_t*>(b + p.off_csc_cnt);
     w.col_ptr = reinterpret_cast<int32_t*>(b + p.off_col_ptr);
     w.row_idx = reinterpret_cast<int32_t*>(b + p.off_row_idx);
+    w.csc_bits = reinterpret_cast<uint32_t*>(b + p.off_csc_bits);
   }
   return w;
 }

@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 #include "readout.hpp"
 
 namespace hsa {
@@ -147,28 +148,69 @@ __device__ __forceinline__ float2 rope_cs(const float2* rope, int gt, int gh, in
   return rope[gt * ht + gh * hh + x * hwp + (jp - ht - hh)];
 }
 
+// bf16 A fragment of the transpose of a row-major LDS tile (row stride STR
+// elements), read with transposing LDS reads: fragment row = tile column
+// 16 jd + l16; slot s of lane group g = tile row 32 c + 16 (s / 4) + 4 g + s % 4.
+// Within each 16-lane group, ds_read_b64_tr_b16 gives output lane i, element t
+// the element i % 4 of the 8 bytes addressed by source lane 4 t + i / 4, so
+// source lane 4 t + j addresses tile row 32 c + 16 hh + 4 g + t, columns
+// 16 jd + 4 j .. + 3.
+template <int STR>
+__device__ __forceinline__ void tr_frag(Frag<bf16_t>& f, const bf16_t* tile, int jd, int c, int l16, int g) {
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const bf16_t* src = tile + (32 * c + 16 * hh + 4 * g + (l16 >> 2)) * STR + 16 * jd + 4 * (l16 & 3);
+    const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+    const uint2 u = __builtin_bit_cast(uint2, t);
+    f.w[2 * hh] = u.x;
+    f.w[2 * hh + 1] = u.y;
+  }
+}
+
 // ------------------------------------------------- transposed mask (CSC)
 static __global__ void k_zero_i32(int n, int32_t* __restrict__ p) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 
-// one thread per CSR row (b, h, a): count (FILL = false) or place (true) its entries
-template <bool FILL>
-__global__ __launch_bounds__(256) void k_csc_pass(int rows, int T, const int32_t* __restrict__ row_ptr,
-                                                  const int32_t* __restrict__ col_idx, int32_t* __restrict__ cnt,
-                                                  const int32_t* __restrict__ col_ptr, int32_t* __restrict__ row_idx,
-                                                  long cap) {
+// The transposed mask through a bit matrix per (b, h): bit (b, a) is set when
+// row a keeps tile b (repeated entries set it once).  Counting and listing the
+// set bits of each column in index order gives the CSC rows ascending, with
+// no sort and independent of the order the bits were set in.
+// one thread per CSR row (b, h, a)
+static __global__ __launch_bounds__(256) void k_csc_bits(int rows, int T, int W, const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx, uint32_t* __restrict__ bits) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
   const int bh = r / T, a = r - bh * T;
   for (int j = row_ptr[r]; j < row_ptr[r + 1]; ++j) {
     const int b = col_idx[j];
-    if (b < 0 || b >= T) continue;
-    const int slot = atomicAdd(&cnt[bh * T + b], 1);
-    if constexpr (FILL) {
-      const long pos = (long)col_ptr[bh * T + b] + slot;
-      if (pos < cap) row_idx[pos] = a;
+    if (b >= 0 && b < T) atomicOr(&bits[((size_t)bh * T + b) * W + (a >> 5)], 1u << (a & 31));
+  }
+}
+
+// one thread per column (b, h, tile): LIST = false counts its bits, true lists them
+template <bool LIST>
+__global__ __launch_bounds__(256) void k_csc_cols(int cols, int W, const uint32_t* __restrict__ bits,
+                                                  int32_t* __restrict__ cnt, const int32_t* __restrict__ col_ptr,
+                                                  int32_t* __restrict__ row_idx, long cap) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  const uint32_t* row = bits + (size_t)c * W;
+  if constexpr (!LIST) {
+    int n = 0;
+    for (int i = 0; i < W; ++i) n += __popc(row[i]);
+    cnt[c] = n;
+  } else {
+    long pos = col_ptr[c];
+    for (int i = 0; i < W; ++i) {
+      uint32_t m = row[i];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        if (pos < cap) row_idx[pos] = 32 * i + bit;
+        ++pos;
+      }
     }
   }
 }
@@ -198,24 +240,6 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
   if (threadIdx.x == 0) ptr[n] = carry;
 }
 
-// one thread per column: insertion sort of its query tiles (the fill order
-// depends on atomics; the sorted lists do not)
-static __global__ __launch_bounds__(256) void k_csc_sort(int cols, const int32_t* __restrict__ col_ptr,
-                                                          int32_t* __restrict__ row_idx, long cap) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
-  const long lo = col_ptr[c], hi = min((long)col_ptr[c + 1], cap);
-  for (long i = lo + 1; i < hi; ++i) {
-    const int x = row_idx[i];
-    long j = i - 1;
-    while (j >= lo && row_idx[j] > x) {
-      row_idx[j + 1] = row_idx[j];
-      --j;
-    }
-    row_idx[j + 1] = x;
-  }
-}
-
 // --------------------------------------------------------- sparse: dQ
 // One block per query tile (4 waves x 16 queries), over its CSR row; K, V and
 // K^T (keys permuted for the dS contraction) staged in LDS, the next tile
@@ -224,9 +248,10 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
   constexpr int CPR = D / 8, NVU = 16 * CPR;   // threads staging 4 keys x 8 dims each
   constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
+  constexpr bool TR = sizeof(T) == 2;  // bf16: K^T fragments by transposing reads of Ks
   __shared__ __align__(16) T Ks[64 * KSTR];
   __shared__ __align__(16) T Vs[64 * KSTR];
-  __shared__ __align__(16) T Kt[D * VSTR];
+  __shared__ __align__(16) T Kt[TR ? 8 : D * VSTR];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
@@ -288,9 +313,11 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
         lds_row(&Ks[(4 * kg + ii) * KSTR + c8 * 8], kc[ii]);
         lds_row(&Vs[(4 * kg + ii) * KSTR + c8 * 8], vc[ii]);
       }
+      if constexpr (!TR) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        st4v(&Kt[(c8 * 8 + e) * VSTR + p0], elem(kc[0], e), elem(kc[1], e), elem(kc[2], e), elem(kc[3], e));
+        for (int e = 0; e < 8; ++e)
+          st4v(&Kt[(c8 * 8 + e) * VSTR + p0], elem(kc[0], e), elem(kc[1], e), elem(kc[2], e), elem(kc[3], e));
+      }
     }
     __syncthreads();
     if (j + 1 < end) load_tile(a.col_idx[j + 1]);
@@ -326,7 +353,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         Frag<T> ktf;
-        load8(ktf, &Kt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        if constexpr (TR) tr_frag<KSTR>(ktf, Ks, jd, c, l16, g);
+        else load8(ktf, &Kt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
         mma(acc[jd], ktf, dsf[c]);
       }
   }
@@ -349,10 +377,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
   constexpr int CPR = D / 8, NVU = 16 * CPR;
   constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
+  constexpr bool TR = sizeof(T) == 2;  // bf16: Q^T, dO^T fragments by transposing reads
   __shared__ __align__(16) T Qs[64 * KSTR];
   __shared__ __align__(16) T Gs[64 * KSTR];
-  __shared__ __align__(16) T Qt[D * VSTR];
-  __shared__ __align__(16) T Gt[D * VSTR];
+  __shared__ __align__(16) T Qt[TR ? 8 : D * VSTR];
+  __shared__ __align__(16) T Gt[TR ? 8 : D * VSTR];
   __shared__ float ls[64];
   __shared__ float dsm[64];
 
@@ -421,10 +450,12 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
         lds_row(&Qs[(4 * kg + ii) * KSTR + c8 * 8], qc[ii]);
         lds_row(&Gs[(4 * kg + ii) * KSTR + c8 * 8], gc[ii]);
       }
+      if constexpr (!TR) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        st4v(&Qt[(c8 * 8 + e) * VSTR + p0], elem(qc[0], e), elem(qc[1], e), elem(qc[2], e), elem(qc[3], e));
-        st4v(&Gt[(c8 * 8 + e) * VSTR + p0], elem(gc[0], e), elem(gc[1], e), elem(gc[2], e), elem(gc[3], e));
+        for (int e = 0; e < 8; ++e) {
+          st4v(&Qt[(c8 * 8 + e) * VSTR + p0], elem(qc[0], e), elem(qc[1], e), elem(qc[2], e), elem(qc[3], e));
+          st4v(&Gt[(c8 * 8 + e) * VSTR + p0], elem(gc[0], e), elem(gc[1], e), elem(gc[2], e), elem(gc[3], e));
+        }
       }
     }
     if (tid < 64) {
@@ -468,8 +499,13 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         Frag<T> gtf, qtf;
-        load8(gtf, &Gt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
-        load8(qtf, &Qt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        if constexpr (TR) {
+          tr_frag<KSTR>(gtf, Gs, jd, c, l16, g);
+          tr_frag<KSTR>(qtf, Qs, jd, c, l16, g);
+        } else {
+          load8(gtf, &Gt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+          load8(qtf, &Qt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        }
         mma(accv[jd], gtf, pf[c]);
         mma(acck[jd], qtf, dsf[c]);
       }
@@ -913,17 +949,15 @@ static hipError_t bwd_linear_by_shape(const Shape& s, const BwdArgs& a, hipStrea
 // scratch; col_ptr [BH*T + 1]; row_idx capacity `cap`.
 template <typename T>
 static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_t* col_ptr, int32_t* row_idx,
-                             long cap, hipStream_t st) {
+                             uint32_t* bits, long cap, hipStream_t st) {
   hipError_t e;
-  const int rows = s.B * s.H * s.T;
-  k_zero_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
-  k_csc_pass<false><<<(rows + 255) / 256, 256, 0, st>>>(rows, s.T, a.row_ptr, a.col_idx, csc_cnt, nullptr,
-                                                        nullptr, cap);
+  const int rows = s.B * s.H * s.T, W = (s.T + 31) / 32;
+  const long nbits = (long)rows * W;
+  k_zero_i32<<<(int)((nbits + 255) / 256), 256, 0, st>>>((int)nbits, reinterpret_cast<int32_t*>(bits));
+  k_csc_bits<<<(rows + 255) / 256, 256, 0, st>>>(rows, s.T, W, a.row_ptr, a.col_idx, bits);
+  k_csc_cols<false><<<(rows + 255) / 256, 256, 0, st>>>(rows, W, bits, csc_cnt, nullptr, nullptr, cap);
   k_csc_scan<<<1, 1024, 0, st>>>(rows, csc_cnt, col_ptr);
-  k_zero_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
-  k_csc_pass<true><<<(rows + 255) / 256, 256, 0, st>>>(rows, s.T, a.row_ptr, a.col_idx, csc_cnt, col_ptr,
-                                                       row_idx, cap);
-  k_csc_sort<<<(rows + 255) / 256, 256, 0, st>>>(rows, col_ptr, row_idx, cap);
+  k_csc_cols<true><<<(rows + 255) / 256, 256, 0, st>>>(rows, W, bits, nullptr, col_ptr, row_idx, cap);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.col_ptr = col_ptr;
   a.row_idx = row_idx;
@@ -940,6 +974,6 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
 }
 
 hipError_t launch_bwd_f32(const Shape& s, const BwdArgs& a, int32_t* csc_cnt, int32_t* col_ptr, int32_t* row_idx,
-                          long cap, bool linear_part, hipStream_t st);
+                          uint32_t* bits, long cap, bool linear_part, hipStream_t st);
 
 }  // namespace hsa

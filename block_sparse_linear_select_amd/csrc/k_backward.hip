@@ -21,9 +21,10 @@ hipError_t launch_backward(const Shape& s, const void* q, const void* k, const v
   a.part_ds = w.part_ds; a.part_dz = w.part_dz; a.ds_plain = w.ds_plain; a.ds_frag = w.ds_frag; a.dz = w.dz;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.nrows = (long)s.B * s.H * s.T;
-  if (s.dt == Dt::F32) return launch_bwd_f32(s, a, w.csc_cnt, w.col_ptr, w.row_idx, w.csc_cap, part == 1, st);
+  if (s.dt == Dt::F32)
+    return launch_bwd_f32(s, a, w.csc_cnt, w.col_ptr, w.row_idx, w.csc_bits, w.csc_cap, part == 1, st);
   if (part == 1) return bwd_linear_by_shape<bf16_t>(s, a, st);
-  return bwd_sparse<bf16_t>(s, a, w.csc_cnt, w.col_ptr, w.row_idx, w.csc_cap, st);
+  return bwd_sparse<bf16_t>(s, a, w.csc_cnt, w.col_ptr, w.row_idx, w.csc_bits, w.csc_cap, st);
 }
 
 }  // namespace hsa

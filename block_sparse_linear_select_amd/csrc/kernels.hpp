@@ -81,6 +81,7 @@ struct Scratch {
   int32_t* csc_cnt = nullptr;  // [BH*T]
   int32_t* col_ptr = nullptr;  // [BH*T + 1]
   int32_t* row_idx = nullptr;  // [BH*T*kmax]
+  uint32_t* csc_bits = nullptr;  // [BH*T][ceil(T/32)] transposed mask bits
   long csc_cap = 0;
 };
 
@@ -93,6 +94,7 @@ struct Plan {
   size_t off_tile_s = 0, off_tile_z = 0, off_s_full = 0, off_wo = 0;
   size_t off_s_plain = 0, off_os = 0, off_lse = 0, off_dsum = 0, off_part_ds = 0, off_part_dz = 0;
   size_t off_ds_plain = 0, off_ds_frag = 0, off_dz = 0, off_uk = 0, off_csc_cnt = 0, off_col_ptr = 0, off_row_idx = 0;
+  size_t off_csc_bits = 0;
   bool select = false, csr_internal = false, linear = false, vt = false, compl_keys = false, backward = false;
 };
 

@@ -112,3 +112,45 @@ def test_backward_rejects_fp8_and_the_complement_variant():
     rp2 = torch.zeros(cfg2.B * cfg2.H * cfg2.T + 1, dtype=torch.int32, device=DEV)
     with pytest.raises(B.HsaError):
         B.hybrid_attn_backward(cfg2, d2["q"], d2["k"], d2["v"], d2["uq"], d2["uk"], d2["wo"], rp2, ci, d2["q"])
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_sampled():
+    """720P bf16 (40 heads, 75600 tokens) on the mask the library selects:
+    dQ of sampled query tiles and dK, dV of sampled key tiles of three heads
+    against the oracle, which evaluates only the rows that reach them."""
+    from workloads import generate, make_workload
+    w = make_workload("wan14b_720p_bf16")
+    print("\n[wan14b_720p_bf16] generating", flush=True)
+    inp = generate(w)
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    rp, ci = B.block_select(cfg, d["q"], d["k"])
+    g = upstream_grad(w, seed=11)
+    dq, dk, dv = B.hybrid_attn_backward(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], rp, ci, g.to(DEV))
+    torch.cuda.synchronize()
+    rows = Hp.split_csr(rp, ci, w.H, w.T)
+    rng = np.random.default_rng(3)
+    tiles = sorted({0, w.T // 2, w.T - 1, *rng.integers(0, w.T, 2).tolist()})
+    pos = R.token_positions(w.grid, w.N)
+    errs = [Hp.RelL2() for _ in range(3)]
+    for h in (0, w.H // 2, w.H - 1):
+        q, k, v = Hp.head_arrays(inp, 0, h)
+        uq, uk, wo = Hp.params(inp, h)
+        gh = to_fp64(g[0, h])
+        ref_l = R.linear_backward(q, k, v, w.N, uq, uk, pos, w.rope_base, gh @ wo.T)
+        for a in tiles:
+            lo, hi = 64 * a, min(64 * a + 64, w.N)
+            only = [rows[h][x] if x == a else np.zeros(0, np.int64) for x in range(w.T)]
+            ref_q = R.sparse_backward(q, k, v, w.N, only, w.softmax_scale, gh)[0]
+            errs[0].add(dq[0, h, lo:hi].cpu().numpy(), (ref_q + ref_l[0])[lo:hi])
+            keepers = [x for x in range(w.T) if a in set(rows[h][x].tolist())]
+            col = [rows[h][x] if x in keepers else np.zeros(0, np.int64) for x in range(w.T)]
+            _, ref_k, ref_v = R.sparse_backward(q, k, v, w.N, col, w.softmax_scale, gh)
+            errs[1].add(dk[0, h, lo:hi].cpu().numpy(), (ref_k + ref_l[1])[lo:hi])
+            errs[2].add(dv[0, h, lo:hi].cpu().numpy(), (ref_v + ref_l[2])[lo:hi])
+        for t in (dq, dk, dv):
+            assert torch.all(t[0, h, w.N:] == 0)
+    print(f"  sampled rel L2: dQ {errs[0].value:.2e}  dK {errs[1].value:.2e}  dV {errs[2].value:.2e}", flush=True)
+    for e in errs:
+        assert e.value <= TOL["bf16"]

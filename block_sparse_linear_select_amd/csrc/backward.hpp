@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
 // queries, contracted over queries on the matrix cores) and dz.  One partial
 // dS, dz per block.
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
   constexpr int NFE = NDB * NRC * 512;
   constexpr int GST = D + 4, QST = R + 4;       // LDS row strides (floats)
@@ -631,39 +631,50 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
                                           : f32x4{0.f, 0.f, 0.f, 0.f};
       pack_rows(qpf[rc], lo, hi, 1.f);
     }
-    // num^T = S^T q'^T and gW^T = W_o dO^T (rows d, query columns)
-    f32x4 num[NDB], gw[NDB];
+    // num^T = S^T q'^T (rows d, query columns), then O_l = num / den
+    f32x4 ol[NDB];
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
-      num[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gw[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ol[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
         float x[8];
         load8f(x, SF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
         Frag<T> hi, lo;
         split8(x, hi, lo);
-        mma_hl(num[jd], hi, lo, qpf[rc]);
+        mma_hl(ol[jd], hi, lo, qpf[rc]);
       }
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        Frag<T> wf;
-        load8(wf, WO + (size_t)(16 * jd + l16) * D + 32 * c + 8 * g);
-        mma(gw[jd], wf, gf[c]);
-      }
+      ol[jd] *= invden;
     }
+    // gW^T = W_o dO^T, two d blocks at a time: gW . O_l, dnum = gW / den as B
+    // fragments (chunks of 32 d) and in LDS for the dS product
+    const int ql = 16 * w + l16;
     float gwol = 0.f;
+    Frag<T> gnf[D / 32];
 #pragma unroll
-    for (int jd = 0; jd < NDB; ++jd)
+    for (int c = 0; c < D / 32; ++c) {
+      f32x4 gw[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gwol = fmaf(gw[jd][i], num[jd][i] * invden, gwol);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int jd = 2 * c + hh;
+        gw[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc) {
+          Frag<T> wf;
+          load8(wf, WO + (size_t)(16 * jd + l16) * D + 32 * cc + 8 * g);
+          mma(gw[hh], wf, gf[cc]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gwol = fmaf(gw[hh][i], ol[jd][i], gwol);
+        *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
+            make_float4(gw[hh][0] * invden, gw[hh][1] * invden, gw[hh][2] * invden, gw[hh][3] * invden);
+      }
+      pack_rows(gnf[c], gw[0], gw[1], invden);
+    }
     gwol = group4_sum(gwol);
     const float gden = -gwol * invden;
     if (g == 0 && qvalid) a.dsum[(size_t)bh * a.N_pad + qrow] = gos;
-    // dnum = gW / den as B fragments (chunks of 32 d); dq' = S dnum
-    Frag<T> gnf[D / 32];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) pack_rows(gnf[c], gw[2 * c], gw[2 * c + 1], invden);
+    // dq' = S dnum
     f32x4 dqp[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -721,11 +732,6 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dzl[rb][i] = fmaf(gden, fq[rb][i], dzl[rb][i]);
-    const int ql = 16 * w + l16;
-#pragma unroll
-    for (int jd = 0; jd < NDB; ++jd)
-      *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
-          make_float4(gw[jd][0] * invden, gw[jd][1] * invden, gw[jd][2] * invden, gw[jd][3] * invden);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =

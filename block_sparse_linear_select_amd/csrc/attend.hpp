@@ -249,36 +249,6 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 // ds_read_b64_tr_b16: within each 16-lane group, output lane i, element t is
 // element (i mod 4) of the 8 bytes addressed by source lane 4t + i/4.
 // ---------------------------------------------------------------------------
-// Swizzles of a staged tile with RG 16-byte granules per row (RB = 16 RG
-// bytes): rows sharing a 256-byte bank set get distinct granule positions
-// (K) or distinct granule pairs (V).
-template <int RG> __device__ __forceinline__ int swz_k(int row) { return (row / (16 / RG)) & (RG - 1); }
-template <int RG> __device__ __forceinline__ int swz_v(int row) { return 2 * ((row / (16 / RG)) & (RG / 2 - 1)); }
-
-// One wave's share of the LDS-direct loads of a 64-row tile (RB bytes per
-// row): load i of wave w fills LDS bytes [1024 (NI w + i), +1024).
-// off[i] = the lane's byte offset within the tile of the granule it moves.
-template <int RB, bool V>
-__device__ __forceinline__ void dma_offsets(int w, int lane, int* off) {
-  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / 2;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int lin = 1024 * (NI * w + i) + 16 * lane;
-    const int row = lin / RB, pos = (lin % RB) / 16;
-    const int gr = pos ^ (V ? swz_v<RG>(row) : swz_k<RG>(row));
-    off[i] = row * RB + 16 * gr;
-  }
-}
-template <int RB>
-__device__ __forceinline__ void dma_tile(const i32x4_t& rs, int col, const int* off, uint8_t* dst, int w) {
-  constexpr int NI = 64 * RB / 1024 / 2;
-  const int base = col * 64 * RB;  // out-of-range columns fall outside the buffer and load zeros
-  static_for<0, NI>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    lds_dma16<1024 * i>(rs, dst + 1024 * NI * w, base + off[i]);
-  });
-}
-
 template <int D, int R, bool SPARSE, bool LINEAR>
 __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;  // bytes and granules per row

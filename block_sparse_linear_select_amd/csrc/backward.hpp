@@ -369,6 +369,167 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
   }
 }
 
+// bf16 sparse dQ: one block per query tile = 2 waves x 32 queries (each K,
+// V or K^T fragment read from LDS feeds two matrix-core steps).  K and V
+// tiles go global -> LDS by LDS-direct loads into XOR-swizzled tiles (row
+// reads), K once more in the transposing-read layout (K^T fragments for
+// dq += scale dS K); the next K and V load during the dq step, the next K^T
+// copy during the scores step.
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
+  constexpr int RB = 2 * D, RG = RB / 16;
+  constexpr int NQB = 2, NDB = D / 16;
+  constexpr int NI = 64 * RB / 1024 / 2;   // LDS-direct loads per wave per tile
+  __shared__ __align__(16) uint8_t Ks[64 * RB];
+  __shared__ __align__(16) uint8_t Vs[64 * RB];
+  __shared__ __align__(16) uint8_t Kv[64 * RB];
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), qa = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + base;
+  const bf16_t* G = reinterpret_cast<const bf16_t*>(a.dout) + base;
+  const int nbytes = a.N * RB;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Q, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void*)G, 0, nbytes, kBufferFlags);
+  const i32x4_t krs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.k) + base, nbytes);
+  const i32x4_t vrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.v) + base, nbytes);
+
+  int qrow[NQB];
+  bool qvalid[NQB];
+  float lse2[NQB], dd[NQB];
+  Frag<bf16_t> qf[NQB][D / 32], gf[NQB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    qrow[qb] = qa * 64 + 32 * w + 16 * qb + l16;
+    qvalid[qb] = qrow[qb] < a.N;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
+      qf[qb][c].w = __builtin_amdgcn_raw_buffer_load_b128(qrs, (qrow[qb] * D + 32 * c + 8 * g) * 2, 0, 0);
+      gf[qb][c].w = __builtin_amdgcn_raw_buffer_load_b128(grs, (qrow[qb] * D + 32 * c + 8 * g) * 2, 0, 0);
+    }
+    lse2[qb] = qvalid[qb] ? a.lse[(size_t)bh * a.N_pad + qrow[qb]] * kLog2e : 0.f;
+    dd[qb] = qvalid[qb] ? a.dsum[(size_t)bh * a.N_pad + qrow[qb]] : 0.f;
+  }
+  f32x4 acc[NQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) acc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (a.N < 0) { Ks[tid] = 0; Vs[tid] = 0; Kv[tid] = 0; }  // (the tiles are written by LDS-direct loads only)
+  const int beg = a.row_ptr[(size_t)bh * a.T + qa], end = a.row_ptr[(size_t)bh * a.T + qa + 1];
+  const float c2 = a.scale * kLog2e;
+  int koff[NI], voff[NI];
+  dma_offsets<RB, false>(w, lane, koff);
+  dma_offsets<RB, true>(w, lane, voff);
+  const int fk = swz_k<RG>(l16);
+  const int kaddr = l16 * RB + 16 * (g ^ fk);
+  const int rowl = 4 * g + (l16 >> 2);
+  const int vaddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);
+  int colv = beg + lane < end ? a.col_idx[beg + lane] : 0;
+  int col = __builtin_amdgcn_readlane(colv, 0);
+  int ncol = __builtin_amdgcn_readlane(colv, 1);
+  if (beg < end) {
+    dma_tile<RB>(krs, col, koff, Ks, w);
+    dma_tile<RB>(vrs, col, koff, Vs, w);
+    dma_tile<RB>(krs, col, voff, Kv, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's K and V shares have landed
+    __syncthreads();
+  }
+  for (int j = beg; j < end; ++j) {
+    const bool more = j + 1 < end;
+    const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
+    Frag<bf16_t> dsf[NQB][2];
+    if (kvalid > 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {  // key blocks 2c, 2c + 1 -> chunk c of dS^T
+        f32x4 s[NQB][2], dp[NQB][2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int kb = 2 * c + h2;
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            s[qb][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[qb][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int cc = 0; cc < D / 32; ++cc) {
+            Frag<bf16_t> kf, vf;
+            kf.w = *reinterpret_cast<const u32x4*>(&Ks[(kaddr ^ (64 * cc)) + 16 * RB * kb]);
+            vf.w = *reinterpret_cast<const u32x4*>(&Vs[(kaddr ^ (64 * cc)) + 16 * RB * kb]);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+              mma(s[qb][h2], kf, qf[qb][cc]);
+              mma(dp[qb][h2], vf, gf[qb][cc]);
+            }
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = 16 * (2 * c + h2) + 4 * g + i;
+              const float p = key < kvalid ? __builtin_amdgcn_exp2f(fmaf(s[qb][h2][i], c2, -lse2[qb])) : 0.f;
+              s[qb][h2][i] = p * (dp[qb][h2][i] - dd[qb]) * a.scale;
+            }
+          pack_rows(dsf[qb][c], s[qb][0], s[qb][1], 1.f);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's K^T share has landed
+    lds_barrier();                              // K^T visible; both waves are done with K and V
+    if (more) {
+      dma_tile<RB>(krs, ncol, koff, Ks, w);
+      dma_tile<RB>(vrs, ncol, koff, Vs, w);
+    }
+    if (kvalid > 0) {
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd) {
+        const int va = vaddr ^ (32 * jd);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<bf16_t> ktf;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Kv[va + (32 * c + 16 * hh) * RB]));
+            const uint2 u = __builtin_bit_cast(uint2, t);
+            ktf.w[2 * hh] = u.x;
+            ktf.w[2 * hh + 1] = u.y;
+          }
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) mma(acc[qb][jd], ktf, dsf[qb][c]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K and V has landed
+    lds_barrier();                              // next K, V visible; both waves are done with K^T
+    if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
+      colv = j + 2 + lane < end ? a.col_idx[j + 2 + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    if (more) dma_tile<RB>(krs, ncol, voff, Kv, w);
+    col = ncol;
+    ncol = __builtin_amdgcn_readlane(colv, (j + 2 - beg) & 63);
+  }
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    if (!qvalid[qb]) continue;
+    float* out = a.dq + base + (size_t)qrow[qb] * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float4 o = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
+      o.x += acc[qb][jd][0]; o.y += acc[qb][jd][1]; o.z += acc[qb][jd][2]; o.w += acc[qb][jd][3];
+      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = o;
+    }
+  }
+}
+
 // ------------------------------------------------------- sparse: dK, dV
 // One block per key tile (4 waves x 16 keys), over the query tiles that keep
 // it (CSC, ascending); Q, dO, their transposes (queries permuted) and the
@@ -926,6 +1087,194 @@ __global__ __launch_bounds__(256) void k_bwd_k(BwdArgs a) {
   }
 }
 
+// bf16 sparse dK, dV: one block per key tile = 2 waves x 32 keys, over the
+// query tiles that keep it (CSC).  Q and dO tiles go global -> LDS by
+// LDS-direct loads: row-read copies for S = Q K^T and dP = dO V^T, and
+// transposing-read copies for dk += scale dS^T Q and dv += P^T dO; the next
+// row-read copies load during the dk/dv step, the next transposing-read copies
+// during the S/dP step.  lse and D of the four query rows a lane holds come
+// with float4 loads.
+template <int D>
+__global__ __launch_bounds__(128) void k_bwd_dkv_bf16(BwdArgs a) {
+  constexpr int RB = 2 * D, RG = RB / 16;
+  constexpr int NKB = 2, NDB = D / 16;
+  constexpr int NI = 64 * RB / 1024 / 2;
+  __shared__ __align__(16) uint8_t Qs[64 * RB];
+  __shared__ __align__(16) uint8_t Gs[64 * RB];
+  __shared__ __align__(16) uint8_t Qv[64 * RB];
+  __shared__ __align__(16) uint8_t Gv[64 * RB];
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + base;
+  const int nbytes = a.N * RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
+  const i32x4_t qrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.q) + base, nbytes);
+  const i32x4_t grs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.dout) + base, nbytes);
+  const float* LSE = a.lse + (size_t)bh * a.N_pad;
+  const float* DS = a.dsum + (size_t)bh * a.N_pad;
+
+  int krow[NKB];
+  bool kvalid[NKB];
+  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
+    kvalid[kb] = krow[kb] < a.N;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
+      kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+      vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+    }
+  }
+  f32x4 acck[NKB][NDB], accv[NKB][NDB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      acck[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accv[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  if (a.N < 0) { Qs[tid] = 0; Gs[tid] = 0; Qv[tid] = 0; Gv[tid] = 0; }
+  const int beg = a.col_ptr[(size_t)bh * a.T + kt];
+  const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
+  const float c2 = a.scale * kLog2e;
+  int roff[NI], toff[NI];
+  dma_offsets<RB, false>(w, lane, roff);
+  dma_offsets<RB, true>(w, lane, toff);
+  const int fk = swz_k<RG>(l16);
+  const int raddr = l16 * RB + 16 * (g ^ fk);
+  const int rowl = 4 * g + (l16 >> 2);
+  const int taddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);
+  int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
+  int row = __builtin_amdgcn_readlane(rowv, 0);
+  int nrow = __builtin_amdgcn_readlane(rowv, 1);
+  if (beg < end) {
+    dma_tile<RB>(qrs, row, roff, Qs, w);
+    dma_tile<RB>(grs, row, roff, Gs, w);
+    dma_tile<RB>(qrs, row, toff, Qv, w);
+    dma_tile<RB>(grs, row, toff, Gv, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));  // this wave's row-read shares have landed
+    __syncthreads();
+  }
+  for (int j = beg; j < end; ++j) {
+    const bool more = j + 1 < end;
+    // lse (log2 units) and D of query rows 16 qb + 4 g + i; rows >= N get P = 0
+    float4 lq[4], dq4[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int q0 = row * 64 + 16 * qb + 4 * g;
+      lq[qb] = *reinterpret_cast<const float4*>(LSE + q0);
+      dq4[qb] = *reinterpret_cast<const float4*>(DS + q0);
+    }
+    Frag<bf16_t> pf[NKB][2], dsf[NKB][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
+      f32x4 s[2][NKB], dp[2][NKB];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qb = 2 * c + h2;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc) {
+          Frag<bf16_t> qfr, gfr;
+          qfr.w = *reinterpret_cast<const u32x4*>(&Qs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+          gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            mma(s[h2][kb], qfr, kf[kb][cc]);
+            mma(dp[h2][kb], gfr, vf[kb][cc]);
+          }
+        }
+        const float4 l4 = lq[qb], d4 = dq4[qb];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
+            // (lse and D of rows >= N are never written: not read into the result)
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e)) : 0.f;
+            s[h2][kb][i] = p;
+            dp[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        pack_rows(pf[kb][c], s[0][kb], s[1][kb], 1.f);
+        pack_rows(dsf[kb][c], dp[0][kb], dp[1][kb], 1.f);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's transposing-read shares have landed
+    lds_barrier();                              // both waves are done with the row-read copies
+    if (more) {
+      dma_tile<RB>(qrs, nrow, roff, Qs, w);
+      dma_tile<RB>(grs, nrow, roff, Gs, w);
+    }
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      const int ta = taddr ^ (32 * jd);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<bf16_t> gtf, qtf;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const s16x4_t tg = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Gv[ta + (32 * c + 16 * hh) * RB]));
+          const s16x4_t tq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Qv[ta + (32 * c + 16 * hh) * RB]));
+          const uint2 ug = __builtin_bit_cast(uint2, tg), uq = __builtin_bit_cast(uint2, tq);
+          gtf.w[2 * hh] = ug.x;
+          gtf.w[2 * hh + 1] = ug.y;
+          qtf.w[2 * hh] = uq.x;
+          qtf.w[2 * hh + 1] = uq.y;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          mma(accv[kb][jd], gtf, pf[kb][c]);
+          mma(acck[kb][jd], qtf, dsf[kb][c]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next row-read copies has landed
+    lds_barrier();                              // both waves are done with the transposing-read copies
+    if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
+      rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    if (more) {
+      dma_tile<RB>(qrs, nrow, toff, Qv, w);
+      dma_tile<RB>(grs, nrow, toff, Gv, w);
+    }
+    row = nrow;
+    nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
+  }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (!kvalid[kb]) continue;
+    float* ok = a.dk + base + (size_t)krow[kb] * D;
+    float* ov = a.dv + base + (size_t)krow[kb] * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float4 x = *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g);
+      x.x += acck[kb][jd][0]; x.y += acck[kb][jd][1]; x.z += acck[kb][jd][2]; x.w += acck[kb][jd][3];
+      *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g) = x;
+      float4 y = *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g);
+      y.x += accv[kb][jd][0]; y.y += accv[kb][jd][1]; y.z += accv[kb][jd][2]; y.w += accv[kb][jd][3];
+      *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g) = y;
+    }
+  }
+}
+
 // ------------------------------------------------------------- launcher
 template <typename T, int D, int R>
 static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_t st) {
@@ -969,12 +1318,19 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   a.row_idx = row_idx;
   a.csc_cap = cap;
   const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
-  if (s.d == 64) {
-    k_bwd_dq<T, 64><<<grid, 256, 0, st>>>(a);
-    k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);
+  if constexpr (sizeof(T) == 2) {
+    if (s.d == 64) k_bwd_dq_bf16<64><<<grid, 128, 0, st>>>(a);
+    else k_bwd_dq_bf16<128><<<grid, 128, 0, st>>>(a);
   } else {
-    k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);
-    k_bwd_dkv<T, 128><<<grid, 256, 0, st>>>(a);
+    if (s.d == 64) k_bwd_dq<T, 64><<<grid, 256, 0, st>>>(a);
+    else k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (s.d == 64) k_bwd_dkv_bf16<64><<<grid, 128, 0, st>>>(a);
+    else k_bwd_dkv_bf16<128><<<grid, 128, 0, st>>>(a);
+  } else {
+    if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);
+    else k_bwd_dkv<T, 128><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -1087,22 +1087,23 @@ __global__ __launch_bounds__(256) void k_bwd_k(BwdArgs a) {
   }
 }
 
-// bf16 sparse dK, dV: one block per key tile = 2 waves x 32 keys, over the
-// query tiles that keep it (CSC).  Q and dO tiles go global -> LDS by
-// LDS-direct loads: row-read copies for S = Q K^T and dP = dO V^T, and
-// transposing-read copies for dk += scale dS^T Q and dv += P^T dO; the next
-// row-read copies load during the dk/dv step, the next transposing-read copies
-// during the S/dP step.  lse and D of the four query rows a lane holds come
-// with float4 loads.
-template <int D>
-__global__ __launch_bounds__(128) void k_bwd_dkv_bf16(BwdArgs a) {
+// bf16 sparse dK or dV (two launches, so that each holds half the
+// accumulators and runs at two waves per SIMD): one block per key tile = 2
+// waves x 32 keys, over the query tiles that keep it (CSC).  Q (and dO) tiles
+// go global -> LDS by LDS-direct loads: row-read copies for S = Q K^T (and
+// dP = dO V^T), a transposing-read copy for dv += P^T dO (dO) or
+// dk += scale dS^T Q (Q); the next row-read copies load during the
+// accumulation step, the next transposing-read copy during the S/dP step.
+// lse and D of the four query rows a lane holds come with float4 loads.
+template <int D, bool DK>
+__global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
   constexpr int NKB = 2, NDB = D / 16;
   constexpr int NI = 64 * RB / 1024 / 2;
+  constexpr int NROW = DK ? 2 : 1;  // row-read copies per step (Q, and dO for dK)
   __shared__ __align__(16) uint8_t Qs[64 * RB];
-  __shared__ __align__(16) uint8_t Gs[64 * RB];
-  __shared__ __align__(16) uint8_t Qv[64 * RB];
-  __shared__ __align__(16) uint8_t Gv[64 * RB];
+  __shared__ __align__(16) uint8_t Gs[DK ? 64 * RB : 16];
+  __shared__ __align__(16) uint8_t Tv[64 * RB];  // transposing-read copy: Q (dK) or dO (dV)
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
@@ -1117,12 +1118,13 @@ __global__ __launch_bounds__(128) void k_bwd_dkv_bf16(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
   const i32x4_t qrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.q) + base, nbytes);
   const i32x4_t grs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.dout) + base, nbytes);
+  const i32x4_t trs = DK ? qrs : grs;
   const float* LSE = a.lse + (size_t)bh * a.N_pad;
   const float* DS = a.dsum + (size_t)bh * a.N_pad;
 
   int krow[NKB];
   bool kvalid[NKB];
-  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][D / 32];
+  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][DK ? D / 32 : 1];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
@@ -1130,19 +1132,16 @@ __global__ __launch_bounds__(128) void k_bwd_dkv_bf16(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
       kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-      vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+      if constexpr (DK) vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
     }
   }
-  f32x4 acck[NKB][NDB], accv[NKB][NDB];
+  f32x4 acc[NKB][NDB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
-      acck[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accv[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (a.N < 0) { Qs[tid] = 0; Gs[tid] = 0; Qv[tid] = 0; Gv[tid] = 0; }
+  if (a.N < 0) { Qs[tid] = 0; Gs[tid & 15] = 0; Tv[tid] = 0; }
   const int beg = a.col_ptr[(size_t)bh * a.T + kt];
   const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
   const float c2 = a.scale * kLog2e;
@@ -1156,121 +1155,110 @@ __global__ __launch_bounds__(128) void k_bwd_dkv_bf16(BwdArgs a) {
   int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
   int row = __builtin_amdgcn_readlane(rowv, 0);
   int nrow = __builtin_amdgcn_readlane(rowv, 1);
+  auto issue_rows = [&](int r) {
+    dma_tile<RB>(qrs, r, roff, Qs, w);
+    if constexpr (DK) dma_tile<RB>(grs, r, roff, Gs, w);
+  };
   if (beg < end) {
-    dma_tile<RB>(qrs, row, roff, Qs, w);
-    dma_tile<RB>(grs, row, roff, Gs, w);
-    dma_tile<RB>(qrs, row, toff, Qv, w);
-    dma_tile<RB>(grs, row, toff, Gv, w);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));  // this wave's row-read shares have landed
+    issue_rows(row);
+    dma_tile<RB>(trs, row, toff, Tv, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's row-read shares have landed
     __syncthreads();
   }
   for (int j = beg; j < end; ++j) {
     const bool more = j + 1 < end;
-    // lse (log2 units) and D of query rows 16 qb + 4 g + i; rows >= N get P = 0
+    // lse (natural log) and D of query rows 16 qb + 4 g + i; rows >= N get P = 0
     float4 lq[4], dq4[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int q0 = row * 64 + 16 * qb + 4 * g;
       lq[qb] = *reinterpret_cast<const float4*>(LSE + q0);
-      dq4[qb] = *reinterpret_cast<const float4*>(DS + q0);
+      if constexpr (DK) dq4[qb] = *reinterpret_cast<const float4*>(DS + q0);
     }
-    Frag<bf16_t> pf[NKB][2], dsf[NKB][2];
+    Frag<bf16_t> bfr[NKB][2];  // P (dV) or scale dS (dK) as B fragments over queries
 #pragma unroll
     for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
-      f32x4 s[2][NKB], dp[2][NKB];
+      f32x4 s[2][NKB], dp[2][DK ? NKB : 1];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int qb = 2 * c + h2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (DK) dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int cc = 0; cc < D / 32; ++cc) {
-          Frag<bf16_t> qfr, gfr;
+          Frag<bf16_t> qfr;
           qfr.w = *reinterpret_cast<const u32x4*>(&Qs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-          gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            mma(s[h2][kb], qfr, kf[kb][cc]);
-            mma(dp[h2][kb], gfr, vf[kb][cc]);
+          for (int kb = 0; kb < NKB; ++kb) mma(s[h2][kb], qfr, kf[kb][cc]);
+          if constexpr (DK) {
+            Frag<bf16_t> gfr;
+            gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma(dp[h2][kb], gfr, vf[kb][cc]);
           }
         }
-        const float4 l4 = lq[qb], d4 = dq4[qb];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float4 l4 = lq[qb];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float dv4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DK) {
+          dv4[0] = dq4[qb].x; dv4[1] = dq4[qb].y; dv4[2] = dq4[qb].z; dv4[3] = dq4[qb].w;
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
             // (lse and D of rows >= N are never written: not read into the result)
+            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
             const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e)) : 0.f;
-            s[h2][kb][i] = p;
-            dp[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+            if constexpr (DK) s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+            else s[h2][kb][i] = p;
           }
       }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        pack_rows(pf[kb][c], s[0][kb], s[1][kb], 1.f);
-        pack_rows(dsf[kb][c], dp[0][kb], dp[1][kb], 1.f);
-      }
+      for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's transposing-read shares have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's transposing-read share has landed
     lds_barrier();                              // both waves are done with the row-read copies
-    if (more) {
-      dma_tile<RB>(qrs, nrow, roff, Qs, w);
-      dma_tile<RB>(grs, nrow, roff, Gs, w);
-    }
+    if (more) issue_rows(nrow);
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       const int ta = taddr ^ (32 * jd);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        Frag<bf16_t> gtf, qtf;
+        Frag<bf16_t> tf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const s16x4_t tg = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Gv[ta + (32 * c + 16 * hh) * RB]));
-          const s16x4_t tq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Qv[ta + (32 * c + 16 * hh) * RB]));
-          const uint2 ug = __builtin_bit_cast(uint2, tg), uq = __builtin_bit_cast(uint2, tq);
-          gtf.w[2 * hh] = ug.x;
-          gtf.w[2 * hh + 1] = ug.y;
-          qtf.w[2 * hh] = uq.x;
-          qtf.w[2 * hh + 1] = uq.y;
+          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Tv[ta + (32 * c + 16 * hh) * RB]));
+          const uint2 u = __builtin_bit_cast(uint2, t);
+          tf.w[2 * hh] = u.x;
+          tf.w[2 * hh + 1] = u.y;
         }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          mma(accv[kb][jd], gtf, pf[kb][c]);
-          mma(acck[kb][jd], qtf, dsf[kb][c]);
-        }
+        for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next row-read copies has landed
-    lds_barrier();                              // both waves are done with the transposing-read copies
+    lds_barrier();                              // both waves are done with the transposing-read copy
     if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
       rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    if (more) {
-      dma_tile<RB>(qrs, nrow, toff, Qv, w);
-      dma_tile<RB>(grs, nrow, toff, Gv, w);
-    }
+    if (more) dma_tile<RB>(trs, nrow, toff, Tv, w);
     row = nrow;
     nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     if (!kvalid[kb]) continue;
-    float* ok = a.dk + base + (size_t)krow[kb] * D;
-    float* ov = a.dv + base + (size_t)krow[kb] * D;
+    float* out = (DK ? a.dk : a.dv) + base + (size_t)krow[kb] * D;
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
-      float4 x = *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g);
-      x.x += acck[kb][jd][0]; x.y += acck[kb][jd][1]; x.z += acck[kb][jd][2]; x.w += acck[kb][jd][3];
-      *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g) = x;
-      float4 y = *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g);
-      y.x += accv[kb][jd][0]; y.y += accv[kb][jd][1]; y.z += accv[kb][jd][2]; y.w += accv[kb][jd][3];
-      *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g) = y;
+      float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
+      x.x += acc[kb][jd][0]; x.y += acc[kb][jd][1]; x.z += acc[kb][jd][2]; x.w += acc[kb][jd][3];
+      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = x;
     }
   }
 }
@@ -1326,8 +1314,13 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
     else k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);
   }
   if constexpr (sizeof(T) == 2) {
-    if (s.d == 64) k_bwd_dkv_bf16<64><<<grid, 128, 0, st>>>(a);
-    else k_bwd_dkv_bf16<128><<<grid, 128, 0, st>>>(a);
+    if (s.d == 64) {
+      k_bwd_dkv_bf16<64, false><<<grid, 128, 0, st>>>(a);
+      k_bwd_dkv_bf16<64, true><<<grid, 128, 0, st>>>(a);
+    } else {
+      k_bwd_dkv_bf16<128, false><<<grid, 128, 0, st>>>(a);
+      k_bwd_dkv_bf16<128, true><<<grid, 128, 0, st>>>(a);
+    }
   } else {
     if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);
     else k_bwd_dkv<T, 128><<<grid, 256, 0, st>>>(a);

@@ -8,8 +8,11 @@
 // attention does):  P = exp(scale q k^T - lse), dP = dO v^T,
 //   dS = P * (dP - D) with D_i = dO_i . O_s,i,
 //   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dO.
-// k_bwd_dq walks each query tile's CSR row, k_bwd_dkv each key tile's column
-// of the transposed mask (CSC, built by k_csc_*).
+// The dQ kernels walk each query tile's CSR row, the dK/dV kernels each key
+// tile's column of the transposed mask (CSC, built by k_csc_*).  For bf16
+// inputs the tiles are staged by LDS-direct loads into XOR-swizzled LDS
+// tiles, once for row reads and once for transposing reads (ds_read_b64_tr_b16
+// gives the transposed operands), with 32 rows per wave.
 //
 // Linear branch, O_l = num / den, num = rho(phi(q U_q)) S, den = phi(q U_q) . z:
 //   gW = dO W_o^T, dnum = gW / den, dden = -(gW . O_l) / den,
@@ -148,25 +151,6 @@ __device__ __forceinline__ float2 rope_cs(const float2* rope, int gt, int gh, in
   return rope[gt * ht + gh * hh + x * hwp + (jp - ht - hh)];
 }
 
-// bf16 A fragment of the transpose of a row-major LDS tile (row stride STR
-// elements), read with transposing LDS reads: fragment row = tile column
-// 16 jd + l16; slot s of lane group g = tile row 32 c + 16 (s / 4) + 4 g + s % 4.
-// Within each 16-lane group, ds_read_b64_tr_b16 gives output lane i, element t
-// the element i % 4 of the 8 bytes addressed by source lane 4 t + i / 4, so
-// source lane 4 t + j addresses tile row 32 c + 16 hh + 4 g + t, columns
-// 16 jd + 4 j .. + 3.
-template <int STR>
-__device__ __forceinline__ void tr_frag(Frag<bf16_t>& f, const bf16_t* tile, int jd, int c, int l16, int g) {
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const bf16_t* src = tile + (32 * c + 16 * hh + 4 * g + (l16 >> 2)) * STR + 16 * jd + 4 * (l16 & 3);
-    const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-    const uint2 u = __builtin_bit_cast(uint2, t);
-    f.w[2 * hh] = u.x;
-    f.w[2 * hh + 1] = u.y;
-  }
-}
-
 // ------------------------------------------------- transposed mask (CSC)
 static __global__ void k_zero_i32(int n, int32_t* __restrict__ p) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -241,17 +225,17 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
 }
 
 // --------------------------------------------------------- sparse: dQ
-// One block per query tile (4 waves x 16 queries), over its CSR row; K, V and
-// K^T (keys permuted for the dS contraction) staged in LDS, the next tile
-// prefetched into registers.  Adds scale * dS K to dq.
+// float32 inputs: one block per query tile (4 waves x 16 queries), over its
+// CSR row; K, V and K^T (keys permuted for the dS contraction) staged in LDS
+// through registers, the next tile prefetched into registers.  Adds
+// scale * dS K to dq.  (bf16 inputs use k_bwd_dq_bf16 below.)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
   constexpr int CPR = D / 8, NVU = 16 * CPR;   // threads staging 4 keys x 8 dims each
   constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
-  constexpr bool TR = sizeof(T) == 2;  // bf16: K^T fragments by transposing reads of Ks
   __shared__ __align__(16) T Ks[64 * KSTR];
   __shared__ __align__(16) T Vs[64 * KSTR];
-  __shared__ __align__(16) T Kt[TR ? 8 : D * VSTR];
+  __shared__ __align__(16) T Kt[D * VSTR];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
@@ -313,11 +297,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
         lds_row(&Ks[(4 * kg + ii) * KSTR + c8 * 8], kc[ii]);
         lds_row(&Vs[(4 * kg + ii) * KSTR + c8 * 8], vc[ii]);
       }
-      if constexpr (!TR) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          st4v(&Kt[(c8 * 8 + e) * VSTR + p0], elem(kc[0], e), elem(kc[1], e), elem(kc[2], e), elem(kc[3], e));
-      }
+      for (int e = 0; e < 8; ++e)
+        st4v(&Kt[(c8 * 8 + e) * VSTR + p0], elem(kc[0], e), elem(kc[1], e), elem(kc[2], e), elem(kc[3], e));
     }
     __syncthreads();
     if (j + 1 < end) load_tile(a.col_idx[j + 1]);
@@ -353,8 +335,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         Frag<T> ktf;
-        if constexpr (TR) tr_frag<KSTR>(ktf, Ks, jd, c, l16, g);
-        else load8(ktf, &Kt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        load8(ktf, &Kt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
         mma(acc[jd], ktf, dsf[c]);
       }
   }
@@ -531,18 +512,18 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
 }
 
 // ------------------------------------------------------- sparse: dK, dV
-// One block per key tile (4 waves x 16 keys), over the query tiles that keep
-// it (CSC, ascending); Q, dO, their transposes (queries permuted) and the
-// per-query lse and D staged in LDS.  Adds scale * dS^T Q to dk and P^T dO to dv.
+// float32 inputs: one block per key tile (4 waves x 16 keys), over the query
+// tiles that keep it (CSC, ascending); Q, dO, their transposes (queries
+// permuted) and the per-query lse and D staged in LDS.  Adds scale * dS^T Q
+// to dk and P^T dO to dv.  (bf16 inputs use k_bwd_dkv_bf16 below.)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
   constexpr int CPR = D / 8, NVU = 16 * CPR;
   constexpr int KSTR = D + 8, VSTR = 64 + 8, NDB = D / 16;
-  constexpr bool TR = sizeof(T) == 2;  // bf16: Q^T, dO^T fragments by transposing reads
   __shared__ __align__(16) T Qs[64 * KSTR];
   __shared__ __align__(16) T Gs[64 * KSTR];
-  __shared__ __align__(16) T Qt[TR ? 8 : D * VSTR];
-  __shared__ __align__(16) T Gt[TR ? 8 : D * VSTR];
+  __shared__ __align__(16) T Qt[D * VSTR];
+  __shared__ __align__(16) T Gt[D * VSTR];
   __shared__ float ls[64];
   __shared__ float dsm[64];
 
@@ -611,12 +592,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
         lds_row(&Qs[(4 * kg + ii) * KSTR + c8 * 8], qc[ii]);
         lds_row(&Gs[(4 * kg + ii) * KSTR + c8 * 8], gc[ii]);
       }
-      if constexpr (!TR) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          st4v(&Qt[(c8 * 8 + e) * VSTR + p0], elem(qc[0], e), elem(qc[1], e), elem(qc[2], e), elem(qc[3], e));
-          st4v(&Gt[(c8 * 8 + e) * VSTR + p0], elem(gc[0], e), elem(gc[1], e), elem(gc[2], e), elem(gc[3], e));
-        }
+      for (int e = 0; e < 8; ++e) {
+        st4v(&Qt[(c8 * 8 + e) * VSTR + p0], elem(qc[0], e), elem(qc[1], e), elem(qc[2], e), elem(qc[3], e));
+        st4v(&Gt[(c8 * 8 + e) * VSTR + p0], elem(gc[0], e), elem(gc[1], e), elem(gc[2], e), elem(gc[3], e));
       }
     }
     if (tid < 64) {
@@ -660,13 +639,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         Frag<T> gtf, qtf;
-        if constexpr (TR) {
-          tr_frag<KSTR>(gtf, Gs, jd, c, l16, g);
-          tr_frag<KSTR>(qtf, Qs, jd, c, l16, g);
-        } else {
-          load8(gtf, &Gt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
-          load8(qtf, &Qt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
-        }
+        load8(gtf, &Gt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
+        load8(qtf, &Qt[(16 * jd + l16) * VSTR + 32 * c + 8 * g]);
         mma(accv[jd], gtf, pf[c]);
         mma(acck[jd], qtf, dsf[c]);
       }

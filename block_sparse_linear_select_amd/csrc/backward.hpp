@@ -678,7 +678,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   __shared__ __align__(16) float QP[64 * QST];
   __shared__ float zred[4][R];
 
-  const int chunk = blockIdx.x, bh = blockIdx.y;
+  // XCD-aware order: the hardware hands block i to XCD i % 8; all chunks of
+  // (b, h) run on XCD bh % 8, so each XCD's L2 holds the per-head operand
+  // fragments (~128 KB) of a few heads only.
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (jx / a.nchunk), chunk = jx % a.nchunk;
+  if (bh >= (int)(a.nrows / a.T)) return;
   const int h = bh % a.H;
   const int t0 = chunk * a.tpc, t1 = min(a.T, t0 + a.tpc);
   if (t0 >= t1) return;
@@ -1241,7 +1246,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
 template <typename T, int D, int R>
 static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_t st) {
   hipError_t e;
-  k_bwd_q<T, D, R><<<dim3(a.nchunk, s.B * s.H), 256, 0, st>>>(a);
+  k_bwd_q<T, D, R><<<8 * a.nchunk * ((s.B * s.H + 7) / 8), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_bwd_fin<T, D, R><<<dim3(s.B * s.H, R / 8), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

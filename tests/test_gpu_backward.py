@@ -154,3 +154,43 @@ def test_backward_full_size_sampled():
     print(f"  sampled rel L2: dQ {errs[0].value:.2e}  dK {errs[1].value:.2e}  dV {errs[2].value:.2e}", flush=True)
     for e in errs:
         assert e.value <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_d64_r16"])
+def test_backward_edge_rows(name):
+    """A row keeping no tile (its sparse gradients vanish), a row keeping every
+    tile, rows with entries outside [0, T) (skipped, as the forward skips
+    them), on the GPU against the oracle given the same mask without them.
+    The descriptor's topk is T, so that every row is within the backward's
+    capacity of topk + force_diag entries per row."""
+    w = Hp.CASES[name]
+    inp = Hp.gen(w)
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w.with_(topk=w.T, force_diag=False))
+    T = w.T
+    rng = np.random.default_rng(9)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    clean, dirty = {}, {}
+    for bh in heads:
+        rows = [np.sort(rng.choice(T, size=min(3, T), replace=False)) for _ in range(T)]
+        rows[0] = np.zeros(0, np.int64)
+        rows[1] = np.arange(T)
+        clean[bh] = rows
+        dr = [r.copy() for r in rows]
+        dr[2] = np.concatenate([[-2], dr[2], [T, T + 3]])
+        dr[0] = np.array([-1, T])
+        dirty[bh] = dr
+    rp, ci = Hp.csr_tensors([dirty[bh] for bh in heads], DEV)
+    g = upstream_grad(w, seed=w.seed + 9)
+    grads = [t.cpu().numpy() for t in _run(cfg, d, rp, ci, g.to(DEV))]
+    errs = [Hp.RelL2() for _ in range(3)]
+    for b, h in heads:
+        q, k, v = Hp.head_arrays(inp, b, h)
+        uq, uk, wo = Hp.params(inp, h)
+        ref = R.hybrid_backward(q, k, v, w.N, w.grid, uq, uk, wo, clean[(b, h)], w.softmax_scale, w.rope_base,
+                                to_fp64(g[b, h]))
+        for t in range(3):
+            errs[t].add(grads[t][b, h, :w.N], ref[t][:w.N])
+    print(f"  dQ {errs[0].value:.2e}  dK {errs[1].value:.2e}  dV {errs[2].value:.2e}", flush=True)
+    for e in errs:
+        assert e.value <= TOL[w.dtype]

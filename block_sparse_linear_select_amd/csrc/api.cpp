@@ -86,7 +86,7 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     p.off_uk = take((size_t)s.H * nrb * (s.d / 32) * 512 * elt);
     p.off_csc_cnt = take(rows * sizeof(int32_t));
     p.off_col_ptr = take((rows + 1) * sizeof(int32_t));
-    p.off_row_idx = take(rows * s.kmax * sizeof(int32_t));
+    p.off_row_idx = take(rows * (size_t)s.T * sizeof(int32_t));  // any mask: at most T rows per column
     p.off_csc_bits = take(rows * (size_t)((s.T + 31) / 32) * sizeof(uint32_t));
   }
   p.total = off;
@@ -549,7 +549,7 @@ HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, c
   Plan p = make_plan(s, false, false, true, false, true);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
-  w.csc_cap = (long)s.B * s.H * s.T * s.kmax;
+  w.csc_cap = (long)s.B * s.H * s.T * s.T;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the forward state (S, z) and the sparse branch's output and log-sum-exp, recomputed
   if ((rc = run_linear_state(s, q, k, v, nullptr, nullptr, nullptr, U_q, U_k, W_o, false, w, st))) return rc;

@@ -80,7 +80,7 @@ struct Scratch {
   void* uk_frag = nullptr;     // [H] U_k^T as A fragments
   int32_t* csc_cnt = nullptr;  // [BH*T]
   int32_t* col_ptr = nullptr;  // [BH*T + 1]
-  int32_t* row_idx = nullptr;  // [BH*T*kmax]
+  int32_t* row_idx = nullptr;  // [BH*T*T]
   uint32_t* csc_bits = nullptr;  // [BH*T][ceil(T/32)] transposed mask bits
   long csc_cap = 0;
 };

@@ -252,9 +252,9 @@ int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
  * O_l = num / den (see hsa_linear_attn), S and z.
  *   q, k, v: [B, H, N_pad, d] float32 or bf16 (HSA_ATTN_ERR_DTYPE for FP8);
  *   U_q, U_k, W_o as for the forward; row_ptr / col_idx: the forward's CSR
- *   with at most topk + force_diag entries per row (longer rows give
- *   unspecified gradients); d_o: [B, H, N_pad, d] in the input type (rows
- *   >= N are ignored).
+ *   (entries outside [0, T) are skipped; rows with repeated entries are
+ *   outside this call's domain); d_o: [B, H, N_pad, d] in the input type
+ *   (rows >= N are ignored).
  *   d_q, d_k, d_v: float32 [B, H, N_pad, d], written in full (rows >= N zero).
  *   desc->linear_keys must be HSA_ATTN_LINEAR_ALL_KEYS (HSA_ATTN_ERR_SHAPE
  *   otherwise).  Workspace: HSA_ATTN_CALL_BACKWARD.

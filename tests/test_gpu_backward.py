@@ -161,12 +161,11 @@ def test_backward_edge_rows(name):
     """A row keeping no tile (its sparse gradients vanish), a row keeping every
     tile, rows with entries outside [0, T) (skipped, as the forward skips
     them), on the GPU against the oracle given the same mask without them.
-    The descriptor's topk is T, so that every row is within the backward's
-    capacity of topk + force_diag entries per row."""
+    The full row holds more entries than the descriptor's topk."""
     w = Hp.CASES[name]
     inp = Hp.gen(w)
     d = Hp.to_device(inp, DEV)
-    cfg = B.Config.from_workload(w.with_(topk=w.T, force_diag=False))
+    cfg = B.Config.from_workload(w)
     T = w.T
     rng = np.random.default_rng(9)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]

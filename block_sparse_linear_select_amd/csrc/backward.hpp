@@ -962,13 +962,15 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdArgs a) {
 }
 
 // ------------------------------------------------------ linear: key side
-// One block per key tile (4 waves x 16 keys): x_k, phi_k, k', then
+// One block per key tile, 2 waves x 32 keys (two 16-key column blocks per
+// wave, so every operand fragment fetched serves both): x_k, phi_k, k', then
 // dk' = dS v, dv = dS^T k' and dk = ((dz + rho^T dk') * phi'(x_k)) U_k^T,
-// written to dk and dv (pad rows 0; the sparse kernel adds to them).
+// written to dk and dv (pad rows 0; the sparse kernels add to them).
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void k_bwd_k(BwdArgs a) {
+__global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
   constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
   constexpr int NFE = NDB * NRC * 512;
+  constexpr int NKB = 2;
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
   const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
@@ -983,86 +985,109 @@ __global__ __launch_bounds__(256) void k_bwd_k(BwdArgs a) {
   const float* DSF = a.ds_frag + (size_t)bh * NFE;
   const float* DSP = a.ds_plain + (size_t)bh * R * D;
   const float* DZ = a.dz + (size_t)bh * R;
-  const int krow = kt * 64 + 16 * w + l16;
-  const bool kvalid = krow < a.N;
-  Frag<T> kf[D / 32], vf[D / 32];
+  int krow[NKB];
+  bool kvalid[NKB];
+  Frag<T> kf[NKB][D / 32], vf[NKB][D / 32];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    if (kvalid) {
-      load8(kf[c], K + (size_t)krow * D + 32 * c + 8 * g);
-      load8(vf[c], V + (size_t)krow * D + 32 * c + 8 * g);
-    } else {
-      kf[c].zero();
-      vf[c].zero();
+  for (int kb = 0; kb < NKB; ++kb) {
+    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
+    kvalid[kb] = krow[kb] < a.N;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (kvalid[kb]) {
+        load8(kf[kb][c], K + (size_t)krow[kb] * D + 32 * c + 8 * g);
+        load8(vf[kb][c], V + (size_t)krow[kb] * D + 32 * c + 8 * g);
+      } else {
+        kf[kb][c].zero();
+        vf[kb][c].zero();
+      }
     }
   }
-  f32x4 xk[NRB], dkp[NRB];
+  f32x4 xk[NKB][NRB], dkp[NKB][NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    xk[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dkp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      xk[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dkp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       Frag<T> uf;
       load8(uf, UKF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
-      mma(xk[rb], uf, kf[c]);
       float x[8];
       load8f(x, DSP + (size_t)(16 * rb + l16) * D + 32 * c + 8 * g);
       Frag<T> hi, lo;
       split8(x, hi, lo);
-      mma_hl(dkp[rb], hi, lo, vf[c]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        mma(xk[kb][rb], uf, kf[kb][c]);
+        mma_hl(dkp[kb][rb], hi, lo, vf[kb][c]);
+      }
     }
   }
-  const int tok = kvalid ? krow : 0;
-  float fk[NRB][4], kp[NRB][4], dx[NRB][4];
+  Frag<T> kpf[NKB][NRC], dxf[NKB][NRC];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int tok = kvalid[kb] ? krow[kb] : 0;
+    float kp[NRB][4], dx[NRB][4];
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int m = 16 * rb + 4 * g + 2 * pr;
-      const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
-      const float e0 = xk[rb][2 * pr], e1 = xk[rb][2 * pr + 1];
-      const float f0 = elu1(e0), f1 = elu1(e1);
-      fk[rb][2 * pr] = f0;
-      fk[rb][2 * pr + 1] = f1;
-      kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
-      kp[rb][2 * pr + 1] = f0 * cs.y + f1 * cs.x;
-      const float x0 = dkp[rb][2 * pr], x1 = dkp[rb][2 * pr + 1];
-      const float d0 = DZ[m] + (x0 * cs.x + x1 * cs.y);
-      const float d1 = DZ[m + 1] + (-x0 * cs.y + x1 * cs.x);
-      dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : f0);
-      dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : f1);
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int m = 16 * rb + 4 * g + 2 * pr;
+        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
+        const float e0 = xk[kb][rb][2 * pr], e1 = xk[kb][rb][2 * pr + 1];
+        const float f0 = elu1(e0), f1 = elu1(e1);
+        kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
+        kp[rb][2 * pr + 1] = f0 * cs.y + f1 * cs.x;
+        const float x0 = dkp[kb][rb][2 * pr], x1 = dkp[kb][rb][2 * pr + 1];
+        const float d0 = DZ[m] + (x0 * cs.x + x1 * cs.y);
+        const float d1 = DZ[m + 1] + (-x0 * cs.y + x1 * cs.x);
+        dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : f0);
+        dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : f1);
+      }
+#pragma unroll
+    for (int rc = 0; rc < NRC; ++rc) {
+      const bool two = 2 * rc + 1 < NRB;
+      const int b1 = two ? 2 * rc + 1 : 2 * rc;
+      const float keep = two ? 1.f : 0.f;
+      pack_rows(kpf[kb][rc], f32x4{kp[2 * rc][0], kp[2 * rc][1], kp[2 * rc][2], kp[2 * rc][3]},
+                f32x4{keep * kp[b1][0], keep * kp[b1][1], keep * kp[b1][2], keep * kp[b1][3]}, 1.f);
+      pack_rows(dxf[kb][rc], f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]},
+                f32x4{keep * dx[b1][0], keep * dx[b1][1], keep * dx[b1][2], keep * dx[b1][3]}, 1.f);
     }
-  Frag<T> kpf[NRC], dxf[NRC];
-#pragma unroll
-  for (int rc = 0; rc < NRC; ++rc) {
-    const bool two = 2 * rc + 1 < NRB;
-    const int b1 = two ? 2 * rc + 1 : 2 * rc;
-    const float keep = two ? 1.f : 0.f;
-    pack_rows(kpf[rc], f32x4{kp[2 * rc][0], kp[2 * rc][1], kp[2 * rc][2], kp[2 * rc][3]},
-              f32x4{keep * kp[b1][0], keep * kp[b1][1], keep * kp[b1][2], keep * kp[b1][3]}, 1.f);
-    pack_rows(dxf[rc], f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]},
-              f32x4{keep * dx[b1][0], keep * dx[b1][1], keep * dx[b1][2], keep * dx[b1][3]}, 1.f);
   }
-  float* dko = a.dk + base + (size_t)krow * D;
-  float* dvo = a.dv + base + (size_t)krow * D;
 #pragma unroll
   for (int jd = 0; jd < NDB; ++jd) {
-    f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f}, ak = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 av[NKB], ak[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      av[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ak[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int rc = 0; rc < NRC; ++rc) {
       float x[8];
       load8f(x, DSF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
       Frag<T> hi, lo;
       split8(x, hi, lo);
-      mma_hl(av, hi, lo, kpf[rc]);
       Frag<T> uf;
       param_perm_frag<T, R>(uf, UK, 16 * jd + l16, rc, g);
-      mma(ak, uf, dxf[rc]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        mma_hl(av[kb], hi, lo, kpf[kb][rc]);
+        mma(ak[kb], uf, dxf[kb][rc]);
+      }
     }
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(dko + 16 * jd + 4 * g) = kvalid ? make_float4(ak[0], ak[1], ak[2], ak[3]) : zero;
-    *reinterpret_cast<float4*>(dvo + 16 * jd + 4 * g) = kvalid ? make_float4(av[0], av[1], av[2], av[3]) : zero;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float* dko = a.dk + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
+      float* dvo = a.dv + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
+      *reinterpret_cast<float4*>(dko) = kvalid[kb] ? make_float4(ak[kb][0], ak[kb][1], ak[kb][2], ak[kb][3]) : zero;
+      *reinterpret_cast<float4*>(dvo) = kvalid[kb] ? make_float4(av[kb][0], av[kb][1], av[kb][2], av[kb][3]) : zero;
+    }
   }
 }
 
@@ -1251,7 +1276,7 @@ static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_
   k_bwd_fin<T, D, R><<<dim3(s.B * s.H, R / 8), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
-  k_bwd_k<T, D, R><<<grid, 256, 0, st>>>(a);
+  k_bwd_k<T, D, R><<<grid, 128, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -151,6 +151,39 @@ __device__ __forceinline__ float2 rope_cs(const float2* rope, int gt, int gh, in
   return rope[gt * ht + gh * hh + x * hwp + (jp - ht - hh)];
 }
 
+// ------------------------------------------------- staging for the sparse kernels
+// Swizzle of a staged tile read both ways: by 16-byte row reads over 16
+// consecutive rows (operand fragments) and by transposing 8-byte reads over
+// aligned groups of 8 rows, each row giving one 32-byte granule pair.  With
+// rr the row's 256-byte bank-set index (RG 16-byte granules per row),
+// granule g sits at g ^ f(rr), f = 2 (rr mod RG/2) + (rr div RG/2) mod 2:
+// over 16 rows f takes every value, so a row read hits 16 distinct granule
+// positions, and over each group of 8 rows f / 2 takes distinct values, so a
+// transposing read hits distinct granule pairs.
+template <int RG> __device__ __forceinline__ int swz_kt(int row) {
+  const int rr = row / (16 / RG);
+  return 2 * (rr & (RG / 2 - 1)) + ((rr / (RG / 2)) & 1);
+}
+// dma_offsets with that swizzle.
+template <int RB>
+__device__ __forceinline__ void dma_offsets_kt(int w, int lane, int* off) {
+  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int lin = 1024 * (NI * w + i) + 16 * lane;
+    const int row = lin / RB, pos = (lin % RB) / 16;
+    off[i] = row * RB + 16 * (pos ^ swz_kt<RG>(row));
+  }
+}
+// One 4-byte-per-lane LDS-direct load (lane l writes 4 bytes at lds_dst +
+// 4 l), issued like lds_dma16 and counted by the kernel's own vmcnt waits.
+__device__ __forceinline__ void lds_dma4(const i32x4_t& rs, const void* lds_dst, int voff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t)(lds_dst);
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(voff), "s"(m0v), "s"(rs) : "memory");
+}
+
 // ------------------------------------------------- transposed mask (CSC)
 static __global__ void k_zero_i32(int n, int32_t* __restrict__ p) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -352,18 +385,17 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
 
 // bf16 sparse dQ: one block per query tile = 2 waves x 32 queries (each K,
 // V or K^T fragment read from LDS feeds two matrix-core steps).  K and V
-// tiles go global -> LDS by LDS-direct loads into XOR-swizzled tiles (row
-// reads), K once more in the transposing-read layout (K^T fragments for
-// dq += scale dS K); the next K and V load during the dq step, the next K^T
-// copy during the scores step.
+// tiles go global -> LDS by LDS-direct loads into XOR-swizzled tiles; the K
+// tile, double-buffered, is read both by rows (S = Q K^T) and transposed
+// (dq += scale dS K), so each key tile is staged once.  The next K tile loads
+// during the scores step, the next V tile during the dq step.
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
   constexpr int NQB = 2, NDB = D / 16;
   constexpr int NI = 64 * RB / 1024 / 2;   // LDS-direct loads per wave per tile
-  __shared__ __align__(16) uint8_t Ks[64 * RB];
+  __shared__ __align__(16) uint8_t Kb[2][64 * RB];
   __shared__ __align__(16) uint8_t Vs[64 * RB];
-  __shared__ __align__(16) uint8_t Kv[64 * RB];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
@@ -401,28 +433,30 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[qb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (a.N < 0) { Ks[tid] = 0; Vs[tid] = 0; Kv[tid] = 0; }  // (the tiles are written by LDS-direct loads only)
+  if (a.N < 0) { Kb[0][tid] = 0; Kb[1][tid] = 0; Vs[tid] = 0; }  // (the tiles are written by LDS-direct loads only)
   const int beg = a.row_ptr[(size_t)bh * a.T + qa], end = a.row_ptr[(size_t)bh * a.T + qa + 1];
   const float c2 = a.scale * kLog2e;
   int koff[NI], voff[NI];
-  dma_offsets<RB, false>(w, lane, koff);
-  dma_offsets<RB, true>(w, lane, voff);
-  const int fk = swz_k<RG>(l16);
-  const int kaddr = l16 * RB + 16 * (g ^ fk);
+  dma_offsets_kt<RB>(w, lane, koff);
+  dma_offsets<RB, false>(w, lane, voff);
+  const int kaddr = l16 * RB + 16 * (g ^ swz_kt<RG>(l16));
+  const int vaddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
   const int rowl = 4 * g + (l16 >> 2);
-  const int vaddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);
+  const int taddr = rowl * RB + 16 * (((l16 >> 1) & 1) ^ swz_kt<RG>(rowl)) + 8 * (l16 & 1);
   int colv = beg + lane < end ? a.col_idx[beg + lane] : 0;
   int col = __builtin_amdgcn_readlane(colv, 0);
   int ncol = __builtin_amdgcn_readlane(colv, 1);
   if (beg < end) {
-    dma_tile<RB>(krs, col, koff, Ks, w);
-    dma_tile<RB>(vrs, col, koff, Vs, w);
-    dma_tile<RB>(krs, col, voff, Kv, w);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's K and V shares have landed
+    dma_tile<RB>(krs, col, koff, Kb[0], w);
+    dma_tile<RB>(vrs, col, voff, Vs, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   for (int j = beg; j < end; ++j) {
+    const int cur = (j - beg) & 1;
     const bool more = j + 1 < end;
+    if (more) dma_tile<RB>(krs, ncol, koff, Kb[cur ^ 1], w);  // that buffer was last read by the previous dq step
+    const uint8_t* Kc = Kb[cur];
     const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
     Frag<bf16_t> dsf[NQB][2];
     if (kvalid > 0) {
@@ -440,8 +474,8 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
 #pragma unroll
           for (int cc = 0; cc < D / 32; ++cc) {
             Frag<bf16_t> kf, vf;
-            kf.w = *reinterpret_cast<const u32x4*>(&Ks[(kaddr ^ (64 * cc)) + 16 * RB * kb]);
-            vf.w = *reinterpret_cast<const u32x4*>(&Vs[(kaddr ^ (64 * cc)) + 16 * RB * kb]);
+            kf.w = *reinterpret_cast<const u32x4*>(&Kc[(kaddr ^ (64 * cc)) + 16 * RB * kb]);
+            vf.w = *reinterpret_cast<const u32x4*>(&Vs[(vaddr ^ (64 * cc)) + 16 * RB * kb]);
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
               mma(s[qb][h2], kf, qf[qb][cc]);
@@ -463,22 +497,18 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's K^T share has landed
-    lds_barrier();                              // K^T visible; both waves are done with K and V
-    if (more) {
-      dma_tile<RB>(krs, ncol, koff, Ks, w);
-      dma_tile<RB>(vrs, ncol, koff, Vs, w);
-    }
+    lds_barrier();  // both waves are done with V
+    if (more) dma_tile<RB>(vrs, ncol, voff, Vs, w);
     if (kvalid > 0) {
 #pragma unroll
       for (int jd = 0; jd < NDB; ++jd) {
-        const int va = vaddr ^ (32 * jd);
+        const int ta = taddr ^ (32 * jd);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           Frag<bf16_t> ktf;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Kv[va + (32 * c + 16 * hh) * RB]));
+            const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Kc[ta + (32 * c + 16 * hh) * RB]));
             const uint2 u = __builtin_bit_cast(uint2, t);
             ktf.w[2 * hh] = u.x;
             ktf.w[2 * hh + 1] = u.y;
@@ -488,13 +518,12 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next K and V has landed
-    lds_barrier();                              // next K, V visible; both waves are done with K^T
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next K and V have landed
+    lds_barrier();                              // next K, V visible; both waves are done with this K
     if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
       colv = j + 2 + lane < end ? a.col_idx[j + 2 + lane] : 0;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    if (more) dma_tile<RB>(krs, ncol, voff, Kv, w);
     col = ncol;
     ncol = __builtin_amdgcn_readlane(colv, (j + 2 - beg) & 63);
   }
@@ -1091,23 +1120,23 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
   }
 }
 
-// bf16 sparse dK or dV (two launches, so that each holds half the
-// accumulators and runs at two waves per SIMD): one block per key tile = 2
-// waves x 32 keys, over the query tiles that keep it (CSC).  Q (and dO) tiles
-// go global -> LDS by LDS-direct loads: row-read copies for S = Q K^T (and
-// dP = dO V^T), a transposing-read copy for dv += P^T dO (dO) or
-// dk += scale dS^T Q (Q); the next row-read copies load during the
-// accumulation step, the next transposing-read copy during the S/dP step.
-// lse and D of the four query rows a lane holds come with float4 loads.
-template <int D, bool DK>
-__global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
+// bf16 sparse dV and dK (two launches, so that each holds half the
+// accumulators): one block per key tile = 2 waves x 32 keys, over the query
+// tiles that keep it (CSC).  Query-side tiles go global -> LDS by LDS-direct
+// loads, and so do the lse (and D) of the staged query tile, so that the loop
+// issues no other global loads: a global load issued behind an LDS-direct
+// load would, when its value is first used, wait for that load as well.
+//
+// dV: Q (row reads, S = Q K^T) and dO (transposing reads, dv += P^T dO); the
+// next Q loads during the dv step, the next dO during the S step.
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_bwd_dv_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
   constexpr int NKB = 2, NDB = D / 16;
   constexpr int NI = 64 * RB / 1024 / 2;
-  constexpr int NROW = DK ? 2 : 1;  // row-read copies per step (Q, and dO for dK)
   __shared__ __align__(16) uint8_t Qs[64 * RB];
-  __shared__ __align__(16) uint8_t Gs[DK ? 64 * RB : 16];
-  __shared__ __align__(16) uint8_t Tv[64 * RB];  // transposing-read copy: Q (dK) or dO (dV)
+  __shared__ __align__(16) uint8_t Tv[64 * RB];
+  __shared__ __align__(16) float Ls[64];
 
   const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
   if (L < 0) return;
@@ -1116,28 +1145,22 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + base;
   const int nbytes = a.N * RB;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
   const i32x4_t qrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.q) + base, nbytes);
   const i32x4_t grs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.dout) + base, nbytes);
-  const i32x4_t trs = DK ? qrs : grs;
-  const float* LSE = a.lse + (size_t)bh * a.N_pad;
-  const float* DS = a.dsum + (size_t)bh * a.N_pad;
+  const i32x4_t lrs = make_rsrc_regs(a.lse + (size_t)bh * a.N_pad, a.N * 4);  // rows >= N read as 0
 
   int krow[NKB];
   bool kvalid[NKB];
-  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][DK ? D / 32 : 1];
+  Frag<bf16_t> kf[NKB][D / 32];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
     kvalid[kb] = krow[kb] < a.N;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
+    for (int c = 0; c < D / 32; ++c)  // rows >= N read as zeros
       kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-      if constexpr (DK) vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-    }
   }
   f32x4 acc[NKB][NDB];
 #pragma unroll
@@ -1145,88 +1168,63 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (a.N < 0) { Qs[tid] = 0; Gs[tid & 15] = 0; Tv[tid] = 0; }
+  if (a.N < 0) { Qs[tid] = 0; Tv[tid] = 0; Ls[tid & 63] = 0.f; }
   const int beg = a.col_ptr[(size_t)bh * a.T + kt];
   const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
   const float c2 = a.scale * kLog2e;
   int roff[NI], toff[NI];
   dma_offsets<RB, false>(w, lane, roff);
   dma_offsets<RB, true>(w, lane, toff);
-  const int fk = swz_k<RG>(l16);
-  const int raddr = l16 * RB + 16 * (g ^ fk);
+  const int raddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
   const int rowl = 4 * g + (l16 >> 2);
   const int taddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);
   int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
   int row = __builtin_amdgcn_readlane(rowv, 0);
   int nrow = __builtin_amdgcn_readlane(rowv, 1);
-  auto issue_rows = [&](int r) {
+  auto issue_q = [&](int r) {
     dma_tile<RB>(qrs, r, roff, Qs, w);
-    if constexpr (DK) dma_tile<RB>(grs, r, roff, Gs, w);
+    if (w == 0) lds_dma4(lrs, Ls, r * 256 + 4 * lane);
   };
   if (beg < end) {
-    issue_rows(row);
-    dma_tile<RB>(trs, row, toff, Tv, w);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));  // this wave's row-read shares have landed
+    issue_q(row);
+    dma_tile<RB>(grs, row, toff, Tv, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   for (int j = beg; j < end; ++j) {
     const bool more = j + 1 < end;
-    // lse (natural log) and D of query rows 16 qb + 4 g + i; rows >= N get P = 0
-    float4 lq[4], dq4[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int q0 = row * 64 + 16 * qb + 4 * g;
-      lq[qb] = *reinterpret_cast<const float4*>(LSE + q0);
-      if constexpr (DK) dq4[qb] = *reinterpret_cast<const float4*>(DS + q0);
-    }
-    Frag<bf16_t> bfr[NKB][2];  // P (dV) or scale dS (dK) as B fragments over queries
+    Frag<bf16_t> bfr[NKB][2];  // P as B fragments over queries
 #pragma unroll
     for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
-      f32x4 s[2][NKB], dp[2][DK ? NKB : 1];
+      f32x4 s[2][NKB];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int qb = 2 * c + h2;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (DK) dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int kb = 0; kb < NKB; ++kb) s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < D / 32; ++cc) {
           Frag<bf16_t> qfr;
           qfr.w = *reinterpret_cast<const u32x4*>(&Qs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) mma(s[h2][kb], qfr, kf[kb][cc]);
-          if constexpr (DK) {
-            Frag<bf16_t> gfr;
-            gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) mma(dp[h2][kb], gfr, vf[kb][cc]);
-          }
         }
-        const float4 l4 = lq[qb];
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[16 * qb + 4 * g]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        float dv4[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DK) {
-          dv4[0] = dq4[qb].x; dv4[1] = dq4[qb].y; dv4[2] = dq4[qb].z; dv4[3] = dq4[qb].w;
-        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // (lse and D of rows >= N are never written: not read into the result)
-            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e)) : 0.f;
-            if constexpr (DK) s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
-            else s[h2][kb][i] = p;
+            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;  // query rows >= N take no part
+            s[h2][kb][i] = ok ? __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e)) : 0.f;
           }
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's transposing-read share has landed
-    lds_barrier();                              // both waves are done with the row-read copies
-    if (more) issue_rows(nrow);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the dO tile has landed
+    lds_barrier();                              // dO visible; both waves are done with Q and lse
+    if (more) issue_q(nrow);
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       const int ta = taddr ^ (32 * jd);
@@ -1244,20 +1242,178 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dkv_bf16(BwdArgs a) {
         for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the next row-read copies has landed
-    lds_barrier();                              // both waves are done with the transposing-read copy
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q and lse have landed
+    lds_barrier();                              // next Q visible; both waves are done with dO
     if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
       rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    if (more) dma_tile<RB>(trs, nrow, toff, Tv, w);
+    if (more) dma_tile<RB>(grs, nrow, toff, Tv, w);
     row = nrow;
     nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     if (!kvalid[kb]) continue;
-    float* out = (DK ? a.dk : a.dv) + base + (size_t)krow[kb] * D;
+    float* out = a.dv + base + (size_t)krow[kb] * D;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
+      x.x += acc[kb][jd][0]; x.y += acc[kb][jd][1]; x.z += acc[kb][jd][2]; x.w += acc[kb][jd][3];
+      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = x;
+    }
+  }
+}
+
+// dK: Q, double-buffered and read both by rows (S = Q K^T) and transposed
+// (dk += scale dS^T Q), so each query tile is staged once, and dO (row
+// reads, dP = dO V^T); lse and D come with Q.  The next Q loads during the
+// S/dP step, the next dO during the dk step.
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
+  constexpr int RB = 2 * D, RG = RB / 16;
+  constexpr int NKB = 2, NDB = D / 16;
+  constexpr int NI = 64 * RB / 1024 / 2;
+  __shared__ __align__(16) uint8_t Qb[2][64 * RB];
+  __shared__ __align__(16) uint8_t Gs[64 * RB];
+  __shared__ __align__(16) float Ls[2][2][64];  // [buffer][lse, D][query]
+
+  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
+  if (L < 0) return;
+  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)bh * a.N_pad * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + base;
+  const int nbytes = a.N * RB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)V, 0, nbytes, kBufferFlags);
+  const i32x4_t qrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.q) + base, nbytes);
+  const i32x4_t grs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.dout) + base, nbytes);
+  // wave 0 stages lse, wave 1 stages D (rows >= N read as 0)
+  const i32x4_t srs = make_rsrc_regs(w == 0 ? (const float*)a.lse + (size_t)bh * a.N_pad
+                                            : (const float*)a.dsum + (size_t)bh * a.N_pad, a.N * 4);
+
+  int krow[NKB];
+  bool kvalid[NKB];
+  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
+    kvalid[kb] = krow[kb] < a.N;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
+      kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+      vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+    }
+  }
+  f32x4 acc[NKB][NDB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (a.N < 0) { Qb[0][tid] = 0; Qb[1][tid] = 0; Gs[tid] = 0; Ls[0][0][tid & 63] = 0.f; }
+  const int beg = a.col_ptr[(size_t)bh * a.T + kt];
+  const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
+  const float c2 = a.scale * kLog2e;
+  int qoff[NI], goff[NI];
+  dma_offsets_kt<RB>(w, lane, qoff);
+  dma_offsets<RB, false>(w, lane, goff);
+  const int qaddr = l16 * RB + 16 * (g ^ swz_kt<RG>(l16));
+  const int gaddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
+  const int rowl = 4 * g + (l16 >> 2);
+  const int taddr = rowl * RB + 16 * (((l16 >> 1) & 1) ^ swz_kt<RG>(rowl)) + 8 * (l16 & 1);
+  int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
+  int row = __builtin_amdgcn_readlane(rowv, 0);
+  int nrow = __builtin_amdgcn_readlane(rowv, 1);
+  auto issue_q = [&](int r, int buf) {
+    dma_tile<RB>(qrs, r, qoff, Qb[buf], w);
+    lds_dma4(srs, Ls[buf][w], r * 256 + 4 * lane);
+  };
+  if (beg < end) {
+    issue_q(row, 0);
+    dma_tile<RB>(grs, row, goff, Gs, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+  }
+  for (int j = beg; j < end; ++j) {
+    const int cur = (j - beg) & 1;
+    const bool more = j + 1 < end;
+    if (more) issue_q(nrow, cur ^ 1);  // that buffer was last read by the previous dk step
+    const uint8_t* Qc = Qb[cur];
+    Frag<bf16_t> bfr[NKB][2];  // scale dS as B fragments over queries
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
+      f32x4 s[2][NKB], dp[2][NKB];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qb = 2 * c + h2;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc) {
+          Frag<bf16_t> qfr, gfr;
+          qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(qaddr ^ (64 * cc)) + 16 * RB * qb]);
+          gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(gaddr ^ (64 * cc)) + 16 * RB * qb]);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            mma(s[h2][kb], qfr, kf[kb][cc]);
+            mma(dp[h2][kb], gfr, vf[kb][cc]);
+          }
+        }
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;  // query rows >= N take no part
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+            s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
+    }
+    lds_barrier();  // both waves are done with dO
+    if (more) dma_tile<RB>(grs, nrow, goff, Gs, w);
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      const int ta = taddr ^ (32 * jd);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<bf16_t> tf;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Qc[ta + (32 * c + 16 * hh) * RB]));
+          const uint2 u = __builtin_bit_cast(uint2, t);
+          tf.w[2 * hh] = u.x;
+          tf.w[2 * hh + 1] = u.y;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q, lse, D and dO have landed
+    lds_barrier();                              // they are visible; both waves are done with this Q
+    if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
+      rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    row = nrow;
+    nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
+  }
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (!kvalid[kb]) continue;
+    float* out = a.dk + base + (size_t)krow[kb] * D;
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
@@ -1319,11 +1475,11 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   }
   if constexpr (sizeof(T) == 2) {
     if (s.d == 64) {
-      k_bwd_dkv_bf16<64, false><<<grid, 128, 0, st>>>(a);
-      k_bwd_dkv_bf16<64, true><<<grid, 128, 0, st>>>(a);
+      k_bwd_dv_bf16<64><<<grid, 128, 0, st>>>(a);
+      k_bwd_dk_bf16<64><<<grid, 128, 0, st>>>(a);
     } else {
-      k_bwd_dkv_bf16<128, false><<<grid, 128, 0, st>>>(a);
-      k_bwd_dkv_bf16<128, true><<<grid, 128, 0, st>>>(a);
+      k_bwd_dv_bf16<128><<<grid, 128, 0, st>>>(a);
+      k_bwd_dk_bf16<128><<<grid, 128, 0, st>>>(a);
     }
   } else {
     if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);

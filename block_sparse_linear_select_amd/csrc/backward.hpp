@@ -55,6 +55,7 @@ struct BwdArgs {
   const int32_t* col_ptr;  // its transpose (CSC): query tiles per key tile, ascending
   const int32_t* row_idx;
   long csc_cap;            // entries row_idx holds
+  const int32_t* col_order; // [BH*T] key tiles in the order the dK / dV blocks take them
   const void* os;          // [BH][N_pad][d] O_s in the output type
   const float* lse;        // [BH][N_pad] natural-log log-sum-exp of the sparse branch
   float* dsum;             // [BH][N_pad] D_i
@@ -255,6 +256,61 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
     __syncthreads();
   }
   if (threadIdx.x == 0) ptr[n] = carry;
+}
+
+// Order in which the dK / dV kernels take the key tiles: within each window
+// of `hw` consecutive heads, by decreasing column length (the query tiles
+// that keep the tile), so that the longest columns start first and the
+// shortest fill the end of the launch; consecutive entries go to different
+// XCDs.  Column lengths run from 0 to several times the mean, and in head
+// order a long column that starts late decides when the launch ends.  A
+// counting sort: the order among equal lengths is arbitrary, and no result
+// depends on it (each column is handled by one block wherever it stands).
+// One block per window; dynamic LDS of kOrderLds(T) bytes.
+constexpr int kOrderHeads = 1;
+inline size_t kOrderLds(int T) { return (size_t)(T + 1 + 1024) * sizeof(int); }
+static __global__ __launch_bounds__(1024) void k_csc_order(int T, int BH, int hw, const int32_t* __restrict__ col_ptr,
+                                                           long cap, int32_t* __restrict__ order) {
+  extern __shared__ int sh_order[];
+  int* hist = sh_order;         // [T + 1]: bucket T - length
+  int* part = sh_order + T + 1; // [1024]
+  const int tid = threadIdx.x;
+  const int h0 = blockIdx.x * hw, nh = min(hw, BH - h0);
+  const int c0 = h0 * T, n = nh * T;
+  auto bucket = [&](int c) {
+    const long b = min((long)col_ptr[c], cap), e = min((long)col_ptr[c + 1], cap);
+    return T - (int)max(0L, min(e - b, (long)T));
+  };
+  for (int i = tid; i <= T; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&hist[bucket(c0 + i)], 1);
+  __syncthreads();
+  // exclusive scan of hist: a segment per thread, then a scan of the segment sums
+  const int seg = (T + 1 + 1023) / 1024;
+  const int lo = min(T + 1, tid * seg), hi = min(T + 1, lo + seg);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += hist[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int x = hist[i];
+    hist[i] = run;
+    run += x;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) order[c0 + atomicAdd(&hist[bucket(c0 + i)], 1)] = c0 + i;
+}
+// Plain order (head-major), where T is too large for the sort's LDS.
+static __global__ void k_iota_i32(int n, int32_t* __restrict__ p) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = i;
 }
 
 // --------------------------------------------------------- sparse: dQ
@@ -1138,8 +1194,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dv_bf16(BwdArgs a) {
   __shared__ __align__(16) uint8_t Tv[64 * RB];
   __shared__ __align__(16) float Ls[64];
 
-  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
-  if (L < 0) return;
+  const int L = uniform(a.col_order[blockIdx.x]);
   const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -1278,8 +1333,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
   __shared__ __align__(16) uint8_t Gs[64 * RB];
   __shared__ __align__(16) float Ls[2][2][64];  // [buffer][lse, D][query]
 
-  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
-  if (L < 0) return;
+  const int L = uniform(a.col_order[blockIdx.x]);
   const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -1461,10 +1515,17 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   k_csc_cols<false><<<(rows + 255) / 256, 256, 0, st>>>(rows, W, bits, csc_cnt, nullptr, nullptr, cap);
   k_csc_scan<<<1, 1024, 0, st>>>(rows, csc_cnt, col_ptr);
   k_csc_cols<true><<<(rows + 255) / 256, 256, 0, st>>>(rows, W, bits, nullptr, col_ptr, row_idx, cap);
+  // the counts are no longer needed: their buffer takes the dK / dV order
+  if (kOrderLds(s.T) <= 65536)
+    k_csc_order<<<(s.B * s.H + kOrderHeads - 1) / kOrderHeads, 1024, kOrderLds(s.T), st>>>(s.T, s.B * s.H, kOrderHeads,
+                                                                                         col_ptr, cap, csc_cnt);
+  else
+    k_iota_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   a.col_ptr = col_ptr;
   a.row_idx = row_idx;
   a.csc_cap = cap;
+  a.col_order = csc_cnt;
   const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
   if constexpr (sizeof(T) == 2) {
     if (s.d == 64) k_bwd_dq_bf16<64><<<grid, 128, 0, st>>>(a);
@@ -1475,11 +1536,11 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   }
   if constexpr (sizeof(T) == 2) {
     if (s.d == 64) {
-      k_bwd_dv_bf16<64><<<grid, 128, 0, st>>>(a);
-      k_bwd_dk_bf16<64><<<grid, 128, 0, st>>>(a);
+      k_bwd_dv_bf16<64><<<rows, 128, 0, st>>>(a);
+      k_bwd_dk_bf16<64><<<rows, 128, 0, st>>>(a);
     } else {
-      k_bwd_dv_bf16<128><<<grid, 128, 0, st>>>(a);
-      k_bwd_dk_bf16<128><<<grid, 128, 0, st>>>(a);
+      k_bwd_dv_bf16<128><<<rows, 128, 0, st>>>(a);
+      k_bwd_dk_bf16<128><<<rows, 128, 0, st>>>(a);
     }
   } else {
     if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);

@@ -815,66 +815,53 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
       }
     }
     gos = group4_sum(gos);
-    // x_q^T = U_q^T q^T; phi; den; q' = rope(phi)
-    f32x4 xq[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      xq[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        Frag<T> uf;
-        load8(uf, UQF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
-        mma(xq[rb], uf, qf[c]);
-      }
-    }
+    // x_q^T = U_q^T q^T; phi; den; q' = rope(phi) (x_q itself is not kept: phi'(x) is 1 where
+    // phi > 1 and phi elsewhere)
+    const int ql = 16 * w + l16;
     const int tok = qvalid ? qrow : 0;
-    float fq[NRB][4], qp[NRB][4];
+    float fq[NRB][4];
     float den = 0.f;
+    Frag<T> qpf[NRC];
+    {
+      float qp[NRB][4];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 xq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fq[rb][i] = elu1(xq[rb][i]);
-        den = fmaf(fq[rb][i], Z[16 * rb + 4 * g + i], den);
+        for (int c = 0; c < D / 32; ++c) {
+          Frag<T> uf;
+          load8(uf, UQF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+          mma(xq, uf, qf[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fq[rb][i] = elu1(xq[i]);
+          den = fmaf(fq[rb][i], Z[16 * rb + 4 * g + i], den);
+        }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, (16 * rb + 4 * g) / 2 + pr);
+          const float x0 = fq[rb][2 * pr], x1 = fq[rb][2 * pr + 1];
+          qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
+          qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+        }
+        // q' of the tile's queries for the dS product (the previous tile's product is done)
+        *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =
+            make_float4(qp[rb][0], qp[rb][1], qp[rb][2], qp[rb][3]);
       }
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, (16 * rb + 4 * g) / 2 + pr);
-        const float x0 = fq[rb][2 * pr], x1 = fq[rb][2 * pr + 1];
-        qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
-        qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+      for (int rc = 0; rc < NRC; ++rc) {
+        const f32x4 lo = f32x4{qp[2 * rc][0], qp[2 * rc][1], qp[2 * rc][2], qp[2 * rc][3]};
+        const f32x4 hi = (2 * rc + 1 < NRB) ? f32x4{qp[2 * rc + 1][0], qp[2 * rc + 1][1], qp[2 * rc + 1][2],
+                                                    qp[2 * rc + 1][3]}
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        pack_rows(qpf[rc], lo, hi, 1.f);
       }
     }
     den = group4_sum(den);
     const float invden = 1.f / den;
-    Frag<T> qpf[NRC];
-#pragma unroll
-    for (int rc = 0; rc < NRC; ++rc) {
-      const f32x4 lo = f32x4{qp[2 * rc][0], qp[2 * rc][1], qp[2 * rc][2], qp[2 * rc][3]};
-      const f32x4 hi = (2 * rc + 1 < NRB) ? f32x4{qp[2 * rc + 1][0], qp[2 * rc + 1][1], qp[2 * rc + 1][2],
-                                                  qp[2 * rc + 1][3]}
-                                          : f32x4{0.f, 0.f, 0.f, 0.f};
-      pack_rows(qpf[rc], lo, hi, 1.f);
-    }
-    // num^T = S^T q'^T (rows d, query columns), then O_l = num / den
-    f32x4 ol[NDB];
-#pragma unroll
-    for (int jd = 0; jd < NDB; ++jd) {
-      ol[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int rc = 0; rc < NRC; ++rc) {
-        float x[8];
-        load8f(x, SF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-        Frag<T> hi, lo;
-        split8(x, hi, lo);
-        mma_hl(ol[jd], hi, lo, qpf[rc]);
-      }
-      ol[jd] *= invden;
-    }
-    // gW^T = W_o dO^T, two d blocks at a time: gW . O_l, dnum = gW / den as B
-    // fragments (chunks of 32 d) and in LDS for the dS product
-    const int ql = 16 * w + l16;
-    float gwol = 0.f;
+    // gW^T = W_o dO^T, two d blocks at a time: dnum = gW / den as B fragments
+    // (chunks of 32 d) and in LDS for the dS product
     Frag<T> gnf[D / 32];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -889,15 +876,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
           load8(wf, WO + (size_t)(16 * jd + l16) * D + 32 * cc + 8 * g);
           mma(gw[hh], wf, gf[cc]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gwol = fmaf(gw[hh][i], ol[jd][i], gwol);
         *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
             make_float4(gw[hh][0] * invden, gw[hh][1] * invden, gw[hh][2] * invden, gw[hh][3] * invden);
       }
       pack_rows(gnf[c], gw[0], gw[1], invden);
     }
+    // num^T = S^T q'^T (rows d, query columns); gW . O_l = dnum . num, with this
+    // lane's dnum read back from LDS (its own writes)
+    float gwol = 0.f;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd) {
+      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rc = 0; rc < NRC; ++rc) {
+        float x[8];
+        load8f(x, SF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        Frag<T> hi, lo;
+        split8(x, hi, lo);
+        mma_hl(num, hi, lo, qpf[rc]);
+      }
+      const float4 gn = *reinterpret_cast<const float4*>(&GN[ql * GST + 16 * jd + 4 * g]);
+      gwol = fmaf(gn.x, num[0], gwol);
+      gwol = fmaf(gn.y, num[1], gwol);
+      gwol = fmaf(gn.z, num[2], gwol);
+      gwol = fmaf(gn.w, num[3], gwol);
+    }
     gwol = group4_sum(gwol);
-    const float gden = -gwol * invden;
+    const float gden = -gwol * invden;  // d den = -(gW . O_l) / den
     if (g == 0 && qvalid) a.dsum[(size_t)bh * a.N_pad + qrow] = gos;
     // dq' = S dnum
     f32x4 dqp[NRB];
@@ -926,9 +931,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
         const float x0 = dqp[rb][2 * pr], x1 = dqp[rb][2 * pr + 1];
         const float d0 = fmaf(gden, Z[m], x0 * cs.x + x1 * cs.y);
         const float d1 = fmaf(gden, Z[m + 1], -x0 * cs.y + x1 * cs.x);
-        const float e0 = xq[rb][2 * pr], e1 = xq[rb][2 * pr + 1];
-        dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : fq[rb][2 * pr]);
-        dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : fq[rb][2 * pr + 1]);
+        const float f0 = fq[rb][2 * pr], f1 = fq[rb][2 * pr + 1];
+        dx[rb][2 * pr] = d0 * (f0 > 1.f ? 1.f : f0);
+        dx[rb][2 * pr + 1] = d1 * (f1 > 1.f ? 1.f : f1);
       }
     Frag<T> dxf[NRC];
 #pragma unroll
@@ -952,15 +957,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
       *reinterpret_cast<float4*>(dqo + 16 * jd + 4 * g) =
           qvalid ? make_float4(acc[0], acc[1], acc[2], acc[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // contributions to dz and dS
+    // contributions to dz
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dzl[rb][i] = fmaf(gden, fq[rb][i], dzl[rb][i]);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =
-          make_float4(qp[rb][0], qp[rb][1], qp[rb][2], qp[rb][3]);
     __syncthreads();
     // dS^T (d x r) += dnum^T q' over the tile's 64 queries
 #pragma unroll

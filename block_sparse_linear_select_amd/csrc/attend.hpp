@@ -227,6 +227,14 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 }
 
 
+// Row maxima of raw scores.  fmaxf on values the compiler cannot prove
+// canonical (matrix-core results) costs one extra canonicalizing v_max per
+// input under IEEE mode; the IEEE 754-2019 maximum lowers to v_maximum3_f32
+// with none.  The two differ only for NaN and signed zero, and a score is
+// never NaN (masked keys are -inf, where both agree).
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float smax4(const f32x4& v) { return smax(smax(v[0], v[1]), smax(v[2], v[3])); }
+
 // ---------------------------------------------------------------------------
 // bf16 query-tile kernel.  One block = one (b, h, query tile) = 2 waves of 32
 // queries; each wave keeps its queries as two 16-column B-fragment sets, so
@@ -371,10 +379,7 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
         bool raise = false;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
-#pragma unroll
-          for (int kb = 1; kb < 4; ++kb)
-            mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+          const float mx = smax(smax(smax4(s[qb][0]), smax4(s[qb][1])), smax(smax4(s[qb][2]), smax4(s[qb][3])));
           mloc[qb] = mx * c2;
           raise |= mloc[qb] > m[qb] + 8.f;
         }
@@ -696,13 +701,11 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
           float mt[2];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 4 * t; kb < 4 * t + 4; ++kb)
-              mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+            const float mx = smax(smax(smax4(s[qb][4 * t]), smax4(s[qb][4 * t + 1])),
+                                  smax(smax4(s[qb][4 * t + 2]), smax4(s[qb][4 * t + 3])));
             mt[t] = kv[t] > 0 ? mx * ck[t] : -INFINITY;
           }
-          mloc[qb] = fmaxf(mt[0], mt[1]);
+          mloc[qb] = smax(mt[0], mt[1]);
           raise |= mloc[qb] > m[qb] + 8.f;
         }
         if (__ballot(raise)) {

@@ -596,6 +596,18 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
     for (int o = 32; o >= 1; o >>= 1) svref = fmaxf(svref, __shfl_xor(svref, o, 64));
     svref = uniform_f(svref);
     const float c0 = sq * a.scale_log2;
+    // per entry of the index block (one per lane): valid keys, exp2 multiplier,
+    // log2 and inverse of s_v / s_v,ref; the steps read them with readlane
+    int kvv;
+    float ckv, lrv, irv;
+    auto derive = [&]() {
+      const bool ok = colv >= 0 && colv < a.T;
+      kvv = ok ? min(64, a.N - colv * 64) : 0;
+      ckv = ok ? c0 * skv : 1.f;  // a missing tile's scores are all -inf: any positive multiplier
+      lrv = ok ? __log2f(svv / svref) : 0.f;  // P' = P * s_v / s_v,ref
+      irv = ok ? svref / svv : 0.f;
+    };
+    derive();
     float m[NQB] = {-INFINITY, -INFINITY};
     f32x4 acc_l[NQB];  // rows 0 and 1 (lane group 0): sums of P' over tile 0 and tile 1 of each pair
 #pragma unroll
@@ -654,14 +666,11 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
       float ck[2], lr[2], ir[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {  // a pair never straddles a block of 64 indices
-        const int col = t == 0 ? c0i : c1i;
-        const bool ok = col >= 0 && col < a.T;
-        kv[t] = ok ? min(64, a.N - col * 64) : 0;
-        const float svf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(svv), (j + t - beg) & 63));
-        const float skf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(skv), (j + t - beg) & 63));
-        ck[t] = ok ? c0 * skf : 1.f;  // a missing tile's scores are all -inf: any positive multiplier
-        lr[t] = ok ? __log2f(svf / svref) : 0.f;   // P' = P * s_v / s_v,ref
-        ir[t] = ok ? svref / svf : 0.f;
+        const int e = (j + t - beg) & 63;
+        kv[t] = __builtin_amdgcn_readlane(kvv, e);
+        ck[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ckv), e));
+        lr[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrv), e));
+        ir[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(irv), e));
       }
       if (((j - beg) & 63) == 62 && more) {  // the next pair starts a new block of 64 indices
         // (only rows longer than 64 entries get here; waits for the loads in flight)
@@ -670,6 +679,7 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
         svv = (colv >= 0 && colv < a.T) ? SV[colv] : 0.f;
         skv = (colv >= 0 && colv < a.T) ? SK[colv] : 0.f;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        derive();
       }
       const int n0 = more ? col_at(j + 2) : -1, n1 = more ? col_at(j + 3) : -1;
       const bool work = kv[0] + kv[1] > 0;

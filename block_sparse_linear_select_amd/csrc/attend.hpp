@@ -736,19 +736,24 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const float b0 = lr[0] - m[qb], b1 = lr[1] - m[qb];
-          float part[2] = {0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
             const float mul = kb < 4 ? ck[0] : ck[1], add = kb < 4 ? b0 : b1;
-            float pv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], mul, add));
-            if (__builtin_expect(want_lse, 0)) part[kb >> 2] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-            wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+            for (int i = 0; i < 4; ++i) s[qb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], mul, add));
+          }
+          if (__builtin_expect(want_lse, 0)) {  // one branch for the step, not one per key block
+            float part[2] = {0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) part[kb >> 2] += (s[qb][kb][0] + s[qb][kb][1]) + (s[qb][kb][2] + s[qb][kb][3]);
+            lex[qb] += part[0] * ir[0] + part[1] * ir[1];  // per-lane partial sums of P'; ir undoes the V-scale ratio
+          }
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][kb][0], s[qb][kb][1], 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][kb][2], s[qb][kb][3], wd, true);
             pf[qb][kb] = wd;
           }
-          lex[qb] += part[0] * ir[0] + part[1] * ir[1];  // per-lane partial sums of P'; ir undoes the V-scale ratio
           const f32x4 r = mma_fp8(onesf, pf[qb], f32x4{0.f, 0.f, 0.f, 0.f});
           lsum[qb] += r[0] * ir[0] + r[1] * ir[1];  // meaningful in lane group 0
         }

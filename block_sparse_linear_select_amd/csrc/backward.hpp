@@ -1267,13 +1267,11 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dv_bf16(BwdArgs a) {
         }
         const float4 l4 = *reinterpret_cast<const float4*>(&Ls[16 * qb + 4 * g]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        // query rows >= N: Q, dO and lse read as zeros, so P = 1 meets a zero dO row
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;  // query rows >= N take no part
-            s[h2][kb][i] = ok ? __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e)) : 0.f;
-          }
+          for (int i = 0; i < 4; ++i) s[h2][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
@@ -1429,7 +1427,10 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;  // query rows >= N take no part
+            // query rows >= N read as zeros (Q, dO, lse, D) and would give P = 1 times dP - D = 0;
+            // the guard keeps the exp of those rows out (evaluated per element, it also keeps
+            // fewer values live: without it this kernel spills at d = 128)
+            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
             const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
             s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
           }

@@ -258,54 +258,45 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
   if (threadIdx.x == 0) ptr[n] = carry;
 }
 
-// Order in which the dK / dV kernels take the key tiles: within each window
-// of `hw` consecutive heads, by decreasing column length (the query tiles
-// that keep the tile), so that the longest columns start first and the
-// shortest fill the end of the launch; consecutive entries go to different
-// XCDs.  Column lengths run from 0 to several times the mean, and in head
-// order a long column that starts late decides when the launch ends.  A
-// counting sort: the order among equal lengths is arbitrary, and no result
-// depends on it (each column is handled by one block wherever it stands).
-// One block per window; dynamic LDS of kOrderLds(T) bytes.
-constexpr int kOrderHeads = 1;
-inline size_t kOrderLds(int T) { return (size_t)(T + 1 + 1024) * sizeof(int); }
-static __global__ __launch_bounds__(1024) void k_csc_order(int T, int BH, int hw, const int32_t* __restrict__ col_ptr,
-                                                           long cap, int32_t* __restrict__ order) {
-  extern __shared__ int sh_order[];
-  int* hist = sh_order;         // [T + 1]: bucket T - length
-  int* part = sh_order + T + 1; // [1024]
+// Order in which the dK / dV kernels take the key tiles of each head: by
+// decreasing column length (the query tiles that keep the tile), then by tile
+// index.  Column lengths run from 0 to several times the mean, and in index
+// order a long column that starts late decides when the launch ends.
+// Consecutive entries go to different XCDs.  No result depends on the order
+// (each column is handled by one block wherever it stands).  One block per
+// (b, h): a bitonic sort of (T - length) << 16 | tile keys in LDS, for
+// T <= kOrderMaxT.
+constexpr int kOrderMaxT = 2048;
+static __global__ __launch_bounds__(1024) void k_csc_order(int T, const int32_t* __restrict__ col_ptr, long cap,
+                                                           int32_t* __restrict__ order) {
+  __shared__ uint32_t key[kOrderMaxT];
   const int tid = threadIdx.x;
-  const int h0 = blockIdx.x * hw, nh = min(hw, BH - h0);
-  const int c0 = h0 * T, n = nh * T;
-  auto bucket = [&](int c) {
-    const long b = min((long)col_ptr[c], cap), e = min((long)col_ptr[c + 1], cap);
-    return T - (int)max(0L, min(e - b, (long)T));
-  };
-  for (int i = tid; i <= T; i += 1024) hist[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += 1024) atomicAdd(&hist[bucket(c0 + i)], 1);
-  __syncthreads();
-  // exclusive scan of hist: a segment per thread, then a scan of the segment sums
-  const int seg = (T + 1 + 1023) / 1024;
-  const int lo = min(T + 1, tid * seg), hi = min(T + 1, lo + seg);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += hist[i];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int i = lo; i < hi; ++i) {
-    const int x = hist[i];
-    hist[i] = run;
-    run += x;
+  const int c0 = blockIdx.x * T;
+  for (int i = tid; i < kOrderMaxT; i += 1024) {
+    uint32_t k = 0xFFFFFFFFu;  // past T: sorts last
+    if (i < T) {
+      const long b = min((long)col_ptr[c0 + i], cap), e = min((long)col_ptr[c0 + i + 1], cap);
+      const int len = (int)max(0L, min(e - b, (long)T));
+      k = (uint32_t)(T - len) << 16 | (uint32_t)i;
+    }
+    key[i] = k;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) order[c0 + atomicAdd(&hist[bucket(c0 + i)], 1)] = c0 + i;
+  for (int k = 2; k <= kOrderMaxT; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < kOrderMaxT; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t x = key[i], y = key[l];
+          if ((x > y) == ((i & k) == 0)) {
+            key[i] = y;
+            key[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < T; i += 1024) order[c0 + i] = c0 + (int)(key[i] & 0xFFFFu);
 }
 // Plain order (head-major), where T is too large for the sort's LDS.
 static __global__ void k_iota_i32(int n, int32_t* __restrict__ p) {
@@ -1518,9 +1509,8 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   k_csc_scan<<<1, 1024, 0, st>>>(rows, csc_cnt, col_ptr);
   k_csc_cols<true><<<(rows + 255) / 256, 256, 0, st>>>(rows, W, bits, nullptr, col_ptr, row_idx, cap);
   // the counts are no longer needed: their buffer takes the dK / dV order
-  if (kOrderLds(s.T) <= 65536)
-    k_csc_order<<<(s.B * s.H + kOrderHeads - 1) / kOrderHeads, 1024, kOrderLds(s.T), st>>>(s.T, s.B * s.H, kOrderHeads,
-                                                                                         col_ptr, cap, csc_cnt);
+  if (s.T <= kOrderMaxT)
+    k_csc_order<<<s.B * s.H, 1024, 0, st>>>(s.T, col_ptr, cap, csc_cnt);
   else
     k_iota_i32<<<(rows + 255) / 256, 256, 0, st>>>(rows, csc_cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;

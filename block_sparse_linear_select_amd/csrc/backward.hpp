@@ -258,14 +258,19 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
   if (threadIdx.x == 0) ptr[n] = carry;
 }
 
-// Order in which the dK / dV kernels take the key tiles of each head: by
-// decreasing column length (the query tiles that keep the tile), then by tile
-// index.  Column lengths run from 0 to several times the mean, and in index
-// order a long column that starts late decides when the launch ends.
-// Consecutive entries go to different XCDs.  No result depends on the order
-// (each column is handled by one block wherever it stands).  One block per
-// (b, h): a bitonic sort of (T - length) << 16 | tile keys in LDS, for
-// T <= kOrderMaxT.
+// Order in which the dK / dV kernels take the key tiles of each head.  The
+// tiles are sorted by column length (the query tiles that keep the tile) in
+// buckets of 2^kOrderShift lengths, longest first, then by tile index: column
+// lengths run from 0 to several times the mean, and in index order a long
+// column that starts late decides when the launch ends.  The sorted list is
+// then dealt to the XCDs (block p runs on XCD p mod 8) in runs of kOrderRun
+// consecutive entries, snaking, so that each XCD's L2 sees runs of
+// neighbouring key tiles, which share many of their query tiles, while every
+// XCD still draws from the whole list.  No result depends on the order (each column is
+// handled by one block wherever it stands).  One block per (b, h): a bitonic
+// sort of (bucket << 16 | tile) keys in LDS, for T <= kOrderMaxT.
+constexpr int kOrderShift = 6;
+constexpr int kOrderRun = 32;
 constexpr int kOrderMaxT = 2048;
 static __global__ __launch_bounds__(1024) void k_csc_order(int T, const int32_t* __restrict__ col_ptr, long cap,
                                                            int32_t* __restrict__ order) {
@@ -277,7 +282,7 @@ static __global__ __launch_bounds__(1024) void k_csc_order(int T, const int32_t*
     if (i < T) {
       const long b = min((long)col_ptr[c0 + i], cap), e = min((long)col_ptr[c0 + i + 1], cap);
       const int len = (int)max(0L, min(e - b, (long)T));
-      k = (uint32_t)(T - len) << 16 | (uint32_t)i;
+      k = ((uint32_t)(T - len) >> kOrderShift) << 16 | (uint32_t)i;
     }
     key[i] = k;
   }
@@ -296,7 +301,20 @@ static __global__ __launch_bounds__(1024) void k_csc_order(int T, const int32_t*
       }
       __syncthreads();
     }
-  for (int i = tid; i < T; i += 1024) order[c0 + i] = c0 + (int)(key[i] & 0xFFFFu);
+  // dispatch position p -> sorted position: within each group of 8 kOrderRun
+  // entries, XCD x takes run x, the XCDs in reverse order every other group
+  // (so that no XCD always takes the longest run of a group); the last
+  // partial group stays in place
+  constexpr int G = 8 * kOrderRun;
+  const int full = T / G * G;
+  for (int p = tid; p < T; p += 1024) {
+    int q = p;
+    if (p < full) {
+      const int x = p & 7, j = p >> 3, grp = j / kOrderRun;
+      q = G * grp + kOrderRun * ((grp & 1) ? 7 - x : x) + j % kOrderRun;
+    }
+    order[c0 + p] = c0 + (int)(key[q] & 0xFFFFu);
+  }
 }
 // Plain order (head-major), where T is too large for the sort's LDS.
 static __global__ void k_iota_i32(int n, int32_t* __restrict__ p) {

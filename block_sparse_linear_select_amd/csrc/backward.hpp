@@ -1432,17 +1432,28 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
         const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        // query rows >= N read as zeros (Q, dO, lse, D), so P = 1 meets dP - D = 0: only
+        // the ragged last tile is guarded (a per-element guard compiles to a branch per
+        // element); the barrier keeps the exps of the two halves from piling up live
+        if (row * 64 + 64 <= a.N) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // query rows >= N read as zeros (Q, dO, lse, D) and would give P = 1 times dP - D = 0;
-            // the guard keeps the exp of those rows out (evaluated per element, it also keeps
-            // fewer values live: without it this kernel spills at d = 128)
-            const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-            s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
-          }
+            for (int i = 0; i < 4; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+              s[h2][kb][i] = p * (dp[h2][kb][i] - dv4[i]) * a.scale;
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+              s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);

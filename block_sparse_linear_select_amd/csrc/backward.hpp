@@ -550,14 +550,23 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
         }
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
+          if (D == 128 && kvalid == 64) {  // keys past N exist only in the ragged last tile (d = 64 keeps one
+                                            // form: the second would cost it a wave per SIMD)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2)
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = 16 * (2 * c + h2) + 4 * g + i;
-              const float p = key < kvalid ? __builtin_amdgcn_exp2f(fmaf(s[qb][h2][i], c2, -lse2[qb])) : 0.f;
-              s[qb][h2][i] = p * (dp[qb][h2][i] - dd[qb]) * a.scale;
-            }
+              for (int i = 0; i < 4; ++i)
+                s[qb][h2][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][h2][i], c2, -lse2[qb])) * (dp[qb][h2][i] - dd[qb]) * a.scale;
+          } else {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = 16 * (2 * c + h2) + 4 * g + i;
+                const float p = key < kvalid ? __builtin_amdgcn_exp2f(fmaf(s[qb][h2][i], c2, -lse2[qb])) : 0.f;
+                s[qb][h2][i] = p * (dp[qb][h2][i] - dd[qb]) * a.scale;
+              }
+          }
           pack_rows(dsf[qb][c], s[qb][0], s[qb][1], 1.f);
         }
       }

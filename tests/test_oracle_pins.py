@@ -244,6 +244,76 @@ def test_p5_duplicated_tiles_force_exact_ties():
         assert list(top1) == [0]
 
 
+# ---------------------------------------------------------------- O1 positions
+def test_o1_token_positions_by_hand():
+    """Frame-major raster on a grid whose three extents all differ (G_t, G_h,
+    G_w) = (3, 5, 7): token i sits at frame i // 35, row (i // 7) mod 5, column
+    i mod 7.  Coordinates written out by hand for tokens on every boundary, so
+    that swapped h and w fields, or a row taken as i // G_h, fail."""
+    pos = R.token_positions((3, 5, 7), 105)
+    by_hand = {
+        0: (0, 0, 0), 1: (0, 0, 1), 6: (0, 0, 6),       # first row of frame 0
+        7: (0, 1, 0), 10: (0, 1, 3), 13: (0, 1, 6),     # second row
+        34: (0, 4, 6),                                  # last token of frame 0
+        35: (1, 0, 0), 36: (1, 0, 1), 43: (1, 1, 1),    # frame 1
+        69: (1, 4, 6), 70: (2, 0, 0), 104: (2, 4, 6),   # last token
+    }
+    for i, p in by_hand.items():
+        assert tuple(int(x) for x in pos[i]) == p, f"token {i}"
+    # every coordinate in range and every (t, h, w) exactly once
+    assert pos[:, 0].max() == 2 and pos[:, 1].max() == 4 and pos[:, 2].max() == 6
+    assert len({tuple(p) for p in pos.tolist()}) == 105
+
+
+def test_o1_positions_of_the_720p_latent_grid_by_hand():
+    """On the 21 x 45 x 80 latent grid one frame holds 3600 tokens; token 3600
+    starts frame 1, token 80 starts row 1, token 75599 is (20, 44, 79)."""
+    pos = R.token_positions((21, 45, 80), 75600)
+    assert tuple(pos[3600]) == (1, 0, 0)
+    assert tuple(pos[80]) == (0, 1, 0)
+    assert tuple(pos[3600 + 2 * 80 + 5]) == (1, 2, 5)
+    assert tuple(pos[75599]) == (20, 44, 79)
+
+
+# ---------------------------------------------------------------- O3 orientation
+def test_o3_pooled_scores_by_hand_are_query_rows_key_columns():
+    """sigma[a, b] = qbar_a . kbar_b with query tiles as rows: a 2 x 2 case
+    worked out by hand, whose transpose differs."""
+    qbar = np.array([[1.0, 0.0], [0.0, 2.0]])
+    kbar = np.array([[3.0, 1.0], [5.0, 7.0]])
+    sc = R.pooled_scores(qbar, kbar)
+    assert sc.tolist() == [[3.0, 5.0], [2.0, 14.0]]   # transposed would be [[3, 2], [5, 14]]
+
+
+def test_o3_asymmetric_scores_against_explicit_loops():
+    rng = np.random.default_rng(33)
+    qbar, kbar = rng.standard_normal((5, 6)), rng.standard_normal((5, 6))
+    sc = R.pooled_scores(qbar, kbar)
+    for a in range(5):
+        for b in range(5):
+            assert abs(sc[a, b] - sum(qbar[a, e] * kbar[b, e] for e in range(6))) <= 1e-14
+    assert np.abs(sc - sc.T).max() > 0.1   # the case is asymmetric
+
+
+def test_o3_o4_top1_of_the_hybrid_follows_the_query_rows():
+    """Three tiles whose rows are constant: query tile a holds basis vector e_a,
+    key tile b holds e_(b+1 mod 3).  Query tile 0 then matches key tile 2,
+    tile 1 key tile 0, tile 2 key tile 1; read with the grid transposed (or the
+    arguments swapped) the answer would be [1], [2], [0]."""
+    d, r, n = 4, 16, 192
+    q = np.zeros((n, d))
+    k = np.zeros((n, d))
+    for a in range(3):
+        q[64 * a:64 * a + 64, a] = 1.0
+        k[64 * a:64 * a + 64, (a + 1) % 3] = 1.0
+    v = np.random.default_rng(3).standard_normal((n, d))
+    uq = uk = np.zeros((d, r))
+    out = R.hybrid_head(q, k, v, n, (1, 3, 64), uq, uk, np.zeros((d, d)), topk=1, force_diag=False,
+                        scale=0.5, base=10000.0)
+    assert [list(x) for x in out["rows"]] == [[2], [0], [1]]
+    assert out["scores"][0, 2] == 1.0 and out["scores"][2, 0] == 0.0
+
+
 # ---------------------------------------------------------------- P6 pooling
 def test_p6_pooling_closed_forms():
     d = 8

@@ -156,6 +156,12 @@ static int check_desc(const hsa_attn_desc* d, Shape& s, bool need_rank, bool nee
     return fail(HSA_ATTN_ERR_SHAPE, "grid %dx%dx%d out of range (t < 2048, h and w < 1024)", d->grid_t, d->grid_h, d->grid_w);
   if ((long long)d->grid_t * d->grid_h * d->grid_w != d->N)
     return fail(HSA_ATTN_ERR_SHAPE, "grid %dx%dx%d does not hold N=%d tokens", d->grid_t, d->grid_h, d->grid_w, d->N);
+  // The kernels address one (b, h) slice with 32-bit byte offsets and buffer
+  // sizes; the widest tensor a call touches per slice is float32 (backward
+  // gradients, float32 inputs), so N_pad * d * 4 bytes must stay below 2^31.
+  if ((long long)d->N_pad * d->d * 4 >= (1ll << 31))
+    return fail(HSA_ATTN_ERR_SHAPE, "N_pad=%d x d=%d: one (b, h) slice of float32 must stay below 2^31 bytes",
+                d->N_pad, d->d);
   const int T = d->N_pad / 64;
   if (need_select && T > 2048) return fail(HSA_ATTN_ERR_SHAPE, "T=%d tiles per row: selection supports at most 2048", T);
   if (need_select && (d->topk < 1 || d->topk > T)) return fail(HSA_ATTN_ERR_SHAPE, "topk=%d must be in [1, T=%d]", d->topk, T);

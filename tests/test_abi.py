@@ -139,3 +139,15 @@ def test_complement_variant_arguments():
     big = _cfg(linear_keys="complement", grid=(65, 64, 64), N=65 * 64 * 64, N_pad=65 * 64 * 64)
     assert _ws(big, B.CALL_LINEAR_COMPLEMENT)[0] == -2 and b"4096" in L.hsa_attn_last_error()
     assert _ws(_cfg(grid=(65, 64, 64), N=65 * 64 * 64, N_pad=65 * 64 * 64, topk=3), B.CALL_LINEAR)[0] == 0
+
+
+def test_slices_beyond_32_bit_offsets_are_rejected():
+    """One (b, h) slice is addressed with 32-bit byte offsets: N_pad * d * 4
+    must stay below 2^31 for every call, also those that select nothing."""
+    n = (1 << 22)  # 4,194,304 tokens: 2^22 * 128 * 4 = 2^31 bytes
+    grid = (1024, 64, 64)
+    for call in (B.CALL_SPARSE, B.CALL_LINEAR, B.CALL_BACKWARD):
+        rc, _ = _ws(_cfg(grid=grid, N=n, N_pad=n, topk=3), call)
+        assert rc == -2 and b"2^31" in B.lib().hsa_attn_last_error(), call
+    rc, _ = _ws(_cfg(grid=(1023, 64, 64), N=1023 * 64 * 64, N_pad=1023 * 64 * 64, topk=3), B.CALL_LINEAR)
+    assert rc == 0

@@ -29,6 +29,76 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def executed_flops(nnz_tiles, d, tile=64):
+    """Matrix-core work of the sparse branch: Q K^T and P V over every kept
+    (query tile, key tile) pair, 2 * 64 * 64 * d FLOP each."""
+    return 4.0 * tile * tile * d * nnz_tiles
+
+
+def dense_equivalent_flops(n, d, heads, batch=1):
+    """The same two products over every (query, key) pair of N valid tokens."""
+    return 4.0 * n * n * d * heads * batch
+
+
+def host_cores():
+    """CPUs this process may run on, the CPU model and the BLAS thread count."""
+    cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"), default=1)
+    except Exception:
+        blas = 1
+    return cpus, model, blas
+
+
+def time_calls(run, steps, warmup, stream):
+    """Whole-call times from HIP events recorded on the launch stream before and
+    after every call (the library's per-kernel timing is off meanwhile).
+    Returns (mean ms over the timed window, per-call ms)."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return ev[0][0].elapsed_time(ev[-1][1]) / steps, per
+
+
+def kernel_split(run, steps):
+    """Average milliseconds per launch of every kernel kind over `steps` more
+    calls, from the HIP events the library records on the launch stream."""
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+    B.timing_enable(steps)
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    kt = B.timing_read()
+    B.timing_enable(0)
+    return {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+
+
+def percentiles(per):
+    import numpy as np
+    return {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
+            "min": float(min(per)), "max": float(max(per))}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -78,11 +148,7 @@ def cpu_baseline(w, inp, heads):
     """The fp64 oracle on `heads` whole heads of the workload, in the metric's unit."""
     from oracle import rola as R
     from workloads.gen import to_fp64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
-    except Exception:
-        threads = 1
+    cpus, model, blas = host_cores()
     t_total = 0.0
     for h in heads:
         args = (*head_fp64(w, inp, h), w.N, w.grid, to_fp64(inp.uq[h]), to_fp64(inp.uk[h]), to_fp64(inp.wo[h]))
@@ -90,12 +156,13 @@ def cpu_baseline(w, inp, heads):
         R.hybrid_head(*args, topk=w.topk, force_diag=w.force_diag, scale=w.softmax_scale, base=w.rope_base)
         t_total += time.perf_counter() - t0
         log(f"  oracle head {h}: {t_total:.1f} s so far")
-    flops = R.dense_equivalent_flops(w.N, w.d, len(heads), 1)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(threads),
+    flops = dense_equivalent_flops(w.N, w.d, len(heads), 1)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(min(cpus, blas)),
             "kind": "oracle",
             "sample": f"{len(heads)} of {w.H} heads of the workload, every query tile, full hybrid in fp64 "
                       f"({t_total:.1f} s; {t_total / len(heads) * w.H * w.B:.0f} s per whole call extrapolated)",
-            "seconds_per_call_extrapolated": t_total / len(heads) * w.H * w.B}
+            "seconds_per_call_extrapolated": t_total / len(heads) * w.H * w.B,
+            "cpus_available": cpus, "blas_threads": blas, "cpu_model": model}
 
 
 def bench_proj(w, args, dev):
@@ -118,22 +185,9 @@ def bench_proj(w, args, dev):
         xc, xs = B.quantize_rows_fp8(x)
         return B.qkv_proj_fp8(xc, xs, wq, sw, w.B, w.N_pad, w.H, w.d)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    B.timing_enable(args.steps)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    kt = B.timing_read()
-    B.timing_enable(0)
-    q_ms = kt["quant"][0] / kt["quant"][1]
-    p_ms = kt["proj"][0] / kt["proj"][1]
+    ms, per = time_calls(step, args.steps, args.warmup, torch.cuda.current_stream())
+    kern = kernel_split(step, args.steps)
+    q_ms, p_ms = kern["quant"], kern["proj"]
     flops = 2.0 * M * C * 3 * C
     log(f"  {args.steps} projection steps: {ms:.3f} ms/step (quant {q_ms:.3f}, proj {p_ms:.3f})")
     achieved = flops / (p_ms * 1e-3) / 1e12
@@ -158,23 +212,11 @@ def bench_compl(w, cfg, d, sc, args, dev):
     plan = B.HybridPlan(ccfg, dev)
     run = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
                            sc["v_scale"], check=False)
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    B.timing_enable(args.steps)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    kt = B.timing_read()
-    B.timing_enable(0)
-    kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    ms, per = time_calls(run, args.steps, args.warmup, torch.cuda.current_stream())
+    kern = kernel_split(run, args.steps)
     log(f"  {args.steps} calls, complement keys: {ms:.3f} ms/call (complement kernel {kern['compl']:.3f} ms)")
-    return {"ms_per_call": ms, "kernels_ms": kern, "compl_kernel": compl_figures(w, kern["compl"])}
+    return {"ms_per_call": ms, **{"ms_" + k: v for k, v in percentiles(per).items()}, "kernels_ms": kern,
+            "compl_kernel": compl_figures(w, kern["compl"])}
 
 
 def bench_backward(w, cfg, d, args, dev):
@@ -193,28 +235,16 @@ def bench_backward(w, cfg, d, args, dev):
     g = upstream_grad(w, seed=w.seed + 7).to(dev)
     run = lambda: B.hybrid_attn_backward(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sel.row_ptr,
                                          sel.col_idx, g)
-    for _ in range(max(1, args.warmup // 2)):
-        run()
-    torch.cuda.synchronize()
     steps = max(1, args.steps // 2)
-    B.timing_enable(steps)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    kt = B.timing_read()
-    B.timing_enable(0)
-    kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    ms, per = time_calls(run, steps, max(1, args.warmup // 2), torch.cuda.current_stream())
+    kern = kernel_split(run, steps)
     log(f"  {steps} backward calls: {ms:.3f} ms/call (sparse part {kern['bwd_sparse']:.3f} ms)")
     pairs = w.B * w.H * w.T * w.topk
     flops = 5 * 2.0 * 64 * 64 * w.d * pairs
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else 157.3
     ach = flops / (kern["bwd_sparse"] * 1e-3) / 1e12
-    return {"ms_per_call": ms, "kernels_ms": kern, "steps": steps,
+    return {"ms_per_call": ms, **{"ms_" + k: v for k, v in percentiles(per).items()}, "kernels_ms": kern,
+            "steps": steps,
             "sparse_roofline": {"bound": "mfma", "kernel": "k_bwd_dq + k_bwd_dv + k_bwd_dk (+ transposed mask)",
                                 "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                                 "flop": flops, "executed_flop": flops * 8 / 5}}
@@ -238,13 +268,77 @@ def compl_figures(w, cms):
             "hbm_frac_min": hbm / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def call_figures(w, ms, per, kern, nnz, linear_keys="all"):
+    """The JSON fields of one timed workload: whole-call figures, the roofline
+    of the attend kernel (executed FLOP over its average launch) and the
+    linear state pass against HBM."""
+    exec_flops = executed_flops(nnz, w.d)
+    dense_flops = dense_equivalent_flops(w.N, w.d, w.H, w.B)
+    attend_ms = kern["attend"]
+    elt = 1 if w.dtype == "fp8" else (4 if w.dtype == "f32" else 2)
+    peak = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
+    achieved = exec_flops / (attend_ms * 1e-3) / 1e12
+    kv_bytes = 2.0 * w.B * w.H * w.N * w.d * elt          # K and V, the linear key/value state's input
+    stream_ms = kern["stream"]
+    pct = percentiles(per)
+    return {
+        "value": dense_flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent, 4*N^2*d*H per call)",
+        "ms_per_step": ms,
+        "ms_per_call": {"mean": ms, **pct},
+        "executed_tflops": exec_flops / (ms * 1e-3) / 1e12,
+        "kept_tile_pairs": nnz,
+        "roofline": {"bound": "mfma", "kernel": "k_attend (block-sparse flash" + (
+                         " + linear readout)" if linear_keys == "all" else ")"),
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "flop_per_launch": exec_flops, "ms_per_launch": attend_ms,
+                     "traffic": measured_traffic(w.name) if linear_keys == "all" else None},
+        "kernels_ms": kern,
+        "linear_state": {"kernel": "k_stream (key/value state)", "ms": stream_ms,
+                         "kv_bytes": kv_bytes, "kv_GBps": kv_bytes / (stream_ms * 1e-3) / 1e9,
+                         "kv_frac_hbm": kv_bytes / (stream_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+
+
+def bench_second_workload(name, args, dev):
+    """Another workload of the same shape (the FP8 one), timed the same way:
+    whole calls with p50/p95, the kernel split, and its roofline."""
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+    from workloads import make_workload, generate
+    w = make_workload(name)
+    cfg = B.Config.from_workload(w)
+    t0 = time.time()
+    inp = generate(w)
+    log(f"  {name} generated in {time.time() - t0:.1f} s")
+    d = {k: getattr(inp, k).to(dev) for k in ("q", "k", "v", "uq", "uk", "wo")}
+    sc = {k: (None if getattr(inp, k) is None else getattr(inp, k).to(dev)) for k in ("q_scale", "k_scale", "v_scale")}
+    del inp
+    plan = B.HybridPlan(cfg, dev)
+    run = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
+                           sc["v_scale"], check=False)
+    ms, per = time_calls(run, args.steps, args.warmup, torch.cuda.current_stream())
+    kern = kernel_split(run, args.steps)
+    sel = B.HybridPlan(cfg, dev, export_mask=True)
+    sel.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"], sc["v_scale"])
+    torch.cuda.synchronize()
+    cols = sel.col_idx[: int(sel.row_ptr[-1].item())]
+    nnz = int(((cols >= 0) & (cols < w.T)).sum().item())
+    log(f"  {args.steps} {name} calls: {ms:.3f} ms/call (attend {kern['attend']:.3f} ms)")
+    res = {"workload": name, "dtype": w.dtype}
+    res.update(call_figures(w, ms, per, kern, nnz))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan14b_720p_bf16")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads the oracle baseline runs (0 skips it)")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads the oracle baseline runs (0 skips it)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 leg: the same 720P shape with E4M3 inputs, timed like the main workload")
     ap.add_argument("--no-reuse", action="store_true",
                     help="skip the second measurement: calls that reuse one selected mask (no pooling, "
                          "scores or top-k), as across denoising steps")
@@ -271,7 +365,6 @@ def main():
     import torch
     from block_sparse_linear_select_amd import binding as B
     from workloads import make_workload, generate
-    from oracle import rola as R
 
     w = make_workload(args.workload)
     cfg = B.Config.from_workload(w)
@@ -298,81 +391,38 @@ def main():
         torch.cuda.synchronize()
         log(f"  calibration: 3 x neg over {args.calibrate_copy} MiB float32 (read and write {n * 4} bytes each)")
         del x, y
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    B.timing_enable(args.steps)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    kt = B.timing_read()
-    B.timing_enable(0)
-    log(f"  {args.steps} calls: {ms:.3f} ms/call")
+    ms, per = time_calls(run, args.steps, args.warmup, stream)
+    log(f"  {args.steps} calls: {ms:.3f} ms/call mean, p50 {percentiles(per)['p50']:.3f} ms")
+    kern = kernel_split(run, args.steps)
 
-    nnz = w.B * w.H * w.T * w.topk  # exactly k tiles per row without a forced diagonal
-    exec_flops = R.executed_flops(nnz, w.d)
-    dense_flops = R.dense_equivalent_flops(w.N, w.d, w.H, w.B)
-    kern = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
-    attend_ms = kern["attend"]
-    elt = 1 if w.dtype == "fp8" else (4 if w.dtype == "f32" else 2)
-    peak = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
-    achieved = exec_flops / (attend_ms * 1e-3) / 1e12
-    kv_bytes = 2.0 * w.B * w.H * w.N * w.d * elt          # K and V, the linear key/value state's input
-    qkv_bytes = 1.5 * kv_bytes                           # the streaming pass also pools Q
-    stream_ms = kern["stream"]
-
-    out = {
-        "metric": "hybrid attn ms/call + effective TFLOP/s at N=75600,H=40; % MFMA/HBM peak",
-        "value": dense_flops / (ms * 1e-3) / 1e12,
-        "unit": "TFLOP/s (dense-equivalent, 4*N^2*d*H per call)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_pad": w.N_pad, "d": w.d,
-                   "grid": list(w.grid), "tile": 64, "topk": w.topk, "tiles_per_row": w.T,
-                   "density": w.topk / w.T, "rank": w.rank, "linear_keys": args.linear_keys,
-                   "parallelism": "single GPU"},
-        "executed_tflops": exec_flops / (ms * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "k_attend (block-sparse flash" + (
-                         " + linear readout)" if args.linear_keys == "all" else ")"),
-                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(w.name) if args.linear_keys == "all" else None},
-        "kernels_ms": kern,
-        "linear_state": {"kernel": "k_stream (pooling + key/value state)", "ms": stream_ms,
-                         "kv_bytes": kv_bytes, "kv_GBps": kv_bytes / (stream_ms * 1e-3) / 1e9,
-                         "kv_frac_hbm": kv_bytes / (stream_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "qkv_GBps": qkv_bytes / (stream_ms * 1e-3) / 1e9},
-    }
+    # kept tile pairs, counted on the mask this workload selects
+    sel = B.HybridPlan(cfg, dev, export_mask=True)
+    sel.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"], sc["v_scale"])
+    torch.cuda.synchronize()
+    cols = sel.col_idx[: int(sel.row_ptr[-1].item())]
+    nnz = int(((cols >= 0) & (cols < w.T)).sum().item())
+    out = {"metric": "hybrid attn ms/call + effective TFLOP/s at N=75600,H=40; % MFMA/HBM peak",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_pad": w.N_pad, "d": w.d,
+                      "grid": list(w.grid), "tile": 64, "topk": w.topk, "tiles_per_row": w.T,
+                      "density": nnz / (w.B * w.H * w.T * w.T), "rank": w.rank, "linear_keys": args.linear_keys,
+                      "parallelism": "single GPU"}}
+    out.update(call_figures(w, ms, per, kern, nnz, args.linear_keys))
     if not args.no_reuse:
         # Mask reuse: select once, then run the hybrid call on that CSR (the
         # streaming pass then computes the linear state only).  Same inputs,
         # same launch configuration; timed the same way.
-        sel = B.HybridPlan(cfg, dev, export_mask=True)
-        sel.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"], sc["v_scale"])
         reuse = lambda: plan.run(d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], sc["q_scale"], sc["k_scale"],
                                  sc["v_scale"], row_ptr=sel.row_ptr, col_idx=sel.col_idx, check=False)
-        for _ in range(args.warmup):
-            reuse()
-        torch.cuda.synchronize()
-        B.timing_enable(args.steps)
-        e0.record(stream)
-        for _ in range(args.steps):
-            reuse()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_r = e0.elapsed_time(e1) / args.steps
-        kt_r = B.timing_read()
-        B.timing_enable(0)
+        ms_r, per_r = time_calls(reuse, args.steps, args.warmup, stream)
+        kern_r = kernel_split(reuse, args.steps)
         log(f"  {args.steps} calls on a reused mask: {ms_r:.3f} ms/call")
-        out["mask_reuse"] = {"ms_per_call": ms_r, "value": dense_flops / (ms_r * 1e-3) / 1e12,
-                             "kernels_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in kt_r.items()}}
+        out["mask_reuse"] = {"ms_per_call": ms_r, **{"ms_" + k: v for k, v in percentiles(per_r).items()},
+                             "value": dense_equivalent_flops(w.N, w.d, w.H, w.B) / (ms_r * 1e-3) / 1e12,
+                             "kernels_ms": kern_r}
     if not args.no_proj and w.d == 128:
         out["qkv_proj"] = bench_proj(w, args, dev)
     if not args.no_bwd and w.dtype != "fp8" and args.linear_keys == "all":
@@ -381,6 +431,11 @@ def main():
         out["compl_kernel"] = compl_figures(w, kern["compl"])
     elif not args.no_compl:
         out["linear_complement"] = bench_compl(w, cfg, d, sc, args, dev)
+    if not args.no_fp8 and w.dtype == "bf16" and w.name == "wan14b_720p_bf16":
+        # the same shape with FP8 E4M3 inputs (per-tile scales), as its own leg
+        del plan, sel
+        torch.cuda.empty_cache()
+        out["fp8"] = bench_second_workload("wan14b_720p_fp8", args, dev)
     if args.cpu_heads > 0:
         log(f"oracle baseline on {args.cpu_heads} heads")
         heads = list(range(min(args.cpu_heads, w.H)))

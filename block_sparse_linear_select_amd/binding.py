@@ -26,7 +26,7 @@ EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version"
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
             "hsa_hybrid_attn", "hsa_hybrid_attn_backward",
             "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
-KERNEL_KINDS = ["rope", "stream", "finalize", "scores", "topk", "attend", "quant", "proj", "compl", "bwd_linear",
+KERNEL_KINDS = ["rope", "stream", "finalize", "select", "unused4", "attend", "quant", "proj", "compl", "bwd_linear",
                 "bwd_sparse"]
 LINEAR_KEYS = {"all": 0, "complement": 1}
 

@@ -40,7 +40,8 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
   if (select) {
     p.off_qmean = take(bh * s.d * s.T * sizeof(double));
     p.off_kmean = take(bh * s.d * s.T * sizeof(double));
-    p.off_scores = take(bh * (size_t)s.T * s.T * sizeof(double));
+    p.off_khi = take(bh * s.d * s.T * sizeof(uint16_t));
+    p.off_klo = take(bh * s.d * s.T * sizeof(uint16_t));
     if (s.force_diag) {
       p.off_sel_tmp = take(rows * (s.topk + 1) * sizeof(int32_t));
       p.off_sel_cnt = take(rows * sizeof(int32_t));
@@ -99,7 +100,8 @@ Scratch bind_plan(const Plan& p, void* ws) {
   if (p.select) {
     w.qmean = reinterpret_cast<double*>(b + p.off_qmean);
     w.kmean = reinterpret_cast<double*>(b + p.off_kmean);
-    w.scores = reinterpret_cast<double*>(b + p.off_scores);
+    w.khi = reinterpret_cast<uint16_t*>(b + p.off_khi);
+    w.klo = reinterpret_cast<uint16_t*>(b + p.off_klo);
     w.sel_tmp = reinterpret_cast<int32_t*>(b + p.off_sel_tmp);
     w.sel_cnt = reinterpret_cast<int32_t*>(b + p.off_sel_cnt);
   }
@@ -340,13 +342,13 @@ HSA_API int hsa_block_select(const hsa_attn_desc* desc, const void* q, const voi
   Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = timed(HSA_ATTN_KERNEL_STREAM, st, [&] {
-    return launch_stream_pass(s, q, k, nullptr, q_scale, k_scale, nullptr, nullptr, true, false, w, qbar_out,
-                              kbar_out, st);
+    return launch_stream_pass(s, nullptr, k, nullptr, nullptr, k_scale, nullptr, nullptr, true, false, w, kbar_out,
+                              st);
   });
-  if (e != hipSuccess) return hip_fail(e, "tile pooling");
-  e = timed(HSA_ATTN_KERNEL_SCORES, st, [&] { return launch_scores(s, w, st); });
-  if (e != hipSuccess) return hip_fail(e, "pooled scores");
-  e = timed(HSA_ATTN_KERNEL_TOPK, st, [&] { return launch_topk(s, w, row_ptr, col_idx, st); });
+  if (e != hipSuccess) return hip_fail(e, "key tile pooling");
+  e = timed(HSA_ATTN_KERNEL_SELECT, st, [&] {
+    return launch_select(s, q, q_scale, w, row_ptr, col_idx, qbar_out, st);
+  });
   if (e != hipSuccess) return hip_fail(e, "tile selection");
   return HSA_ATTN_OK;
 }
@@ -386,7 +388,7 @@ static int run_linear_state(const Shape& s, const void* q, const void* k, const 
   hipError_t e = timed(HSA_ATTN_KERNEL_ROPE, st, [&] { return launch_rope_table(s, w.rope, st); });
   if (e != hipSuccess) return hip_fail(e, "rope table");
   e = timed(HSA_ATTN_KERNEL_STREAM, st, [&] {
-    return launch_stream_pass(s, q, k, v, qs, ks, vs, uk, pool, true, w, nullptr, nullptr, st);
+    return launch_stream_pass(s, q, k, v, qs, ks, vs, uk, pool, true, w, nullptr, st);
   });
   if (e != hipSuccess) return hip_fail(e, "streaming pass");
   e = timed(HSA_ATTN_KERNEL_FINALIZE, st, [&] { return launch_finalize(s, uq, wo, w, st); });
@@ -475,9 +477,9 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if (!given) {
     int32_t* rpo = internal ? w.row_ptr : row_ptr_out;
     int32_t* cio = internal ? w.col_idx : col_idx_out;
-    hipError_t e = timed(HSA_ATTN_KERNEL_SCORES, st, [&] { return launch_scores(s, w, st); });
-    if (e != hipSuccess) return hip_fail(e, "pooled scores");
-    e = timed(HSA_ATTN_KERNEL_TOPK, st, [&] { return launch_topk(s, w, rpo, cio, st); });
+    hipError_t e = timed(HSA_ATTN_KERNEL_SELECT, st, [&] {
+      return launch_select(s, q, q_scale, w, rpo, cio, nullptr, st);
+    });
     if (e != hipSuccess) return hip_fail(e, "tile selection");
     rp = rpo;
     ci = cio;

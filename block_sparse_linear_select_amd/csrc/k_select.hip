@@ -11,88 +11,7 @@
 
 namespace hsa {
 
-// -------------------------------------------------------------- scores
-// sigma[a][b] = qbar_a . kbar_b for one (b, h), float64 16x16x4 matrix-core
-// steps.  Block: 4 waves x 16 rows = 64 rows of a; the column means are
-// staged 32 columns at a time through double-buffered LDS, and each wave runs
-// two independent accumulator chains.  Means are stored one row per tile
-// ([T][d]): a chunk of 32 column means is one contiguous block, loaded
-// coalesced and kept in LDS with row stride d + 4 doubles (the 16 rows x 4
-// dims of an operand read then spread over all banks).
-constexpr int kScoreCols = 32;
-
-template <int D>
-__global__ __launch_bounds__(256) void k_scores(int T, const double* __restrict__ qmean,
-                                                const double* __restrict__ kmean, double* __restrict__ scores) {
-  constexpr int CS = D + 4;  // LDS row stride (doubles) of a staged column mean
-  __shared__ double kbuf[2][kScoreCols * CS];
-  const int bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const double* qb = qmean + (size_t)bh * T * D;
-  const double* kb = kmean + (size_t)bh * T * D;
-  double* out = scores + (size_t)bh * T * T;
-  const int rbase = 64 * blockIdx.x + 16 * w;
-  const int row = rbase + l16;
-  double af[D / 4];
-#pragma unroll
-  for (int s = 0; s < D / 4; ++s) af[s] = row < T ? qb[(size_t)row * D + 4 * s + g] : 0.0;
-
-  // this block's part of the columns: chunks [c_lo, c_hi) of blockIdx.z's share
-  const int nchunks_all = (T + kScoreCols - 1) / kScoreCols;
-  const int c_lo = (int)((long)nchunks_all * blockIdx.z / gridDim.z);
-  const int c_hi = (int)((long)nchunks_all * (blockIdx.z + 1) / gridDim.z);
-  // each thread stages PER doubles of a chunk: element tid + 256 i of the
-  // chunk's contiguous [32][D] block
-  constexpr int PER = D * kScoreCols / 256;
-  double pre[PER];
-  auto fetch = [&](int cc) {
-    const double* src = kb + (size_t)cc * kScoreCols * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + 256 * i;
-      pre[i] = cc * kScoreCols + e / D < T ? src[e] : 0.0;
-    }
-  };
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + 256 * i;
-      kbuf[buf][(e / D) * CS + e % D] = pre[i];
-    }
-  };
-  if (c_lo >= c_hi) return;
-  fetch(c_lo);
-  put(0);
-  __syncthreads();
-  for (int cc = c_lo; cc < c_hi; ++cc) {
-    const int buf = (cc - c_lo) & 1;
-    if (cc + 1 < c_hi) fetch(cc + 1);  // in flight while this chunk is multiplied
-    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
-    const double* kt = kbuf[buf];
-#pragma unroll
-    for (int s = 0; s < D / 4; ++s) {
-      const double b0 = kt[l16 * CS + 4 * s + g];
-      const double b1 = kt[(16 + l16) * CS + 4 * s + g];
-      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s], b1, acc1, 0, 0, 0);
-    }
-    // float64 16x16x4 accumulator: register i of lane group g holds row 4i + g
-    const int c0 = cc * kScoreCols + l16, c1 = c0 + 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = rbase + 4 * i + g;
-      if (rr < T) {
-        if (c0 < T) out[(size_t)rr * T + c0] = acc0[i];
-        if (c1 < T) out[(size_t)rr * T + c1] = acc1[i];
-      }
-    }
-    if (cc + 1 < c_hi) put(buf ^ 1);  // that buffer was last read before the previous barrier
-    __syncthreads();
-  }
-}
-
-// -------------------------------------------------------------- top-k
+// -------------------------------------------------------------- keys
 // Order-preserving 64-bit key of a float64 (larger key <=> larger value;
 // -0 is folded onto +0 so that equal values tie).
 __device__ __forceinline__ uint64_t order_key(double x) {
@@ -100,63 +19,132 @@ __device__ __forceinline__ uint64_t order_key(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
+// The same for a float32, in 32 bits.
+__device__ __forceinline__ uint32_t order_key32(float x) {
+  if (x == 0.f) x = 0.f;
+  const uint32_t u = __float_as_uint(x);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key32_value(uint32_t k) {
+  return __uint_as_float((k >> 31) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row (keys per lane: MJ <= kMaxJ)
 
-// One wave per row: radix-select the k-th largest key (8 passes of 8 bits),
-// keep every key above it and the lowest-index keys equal to it, add the
-// diagonal if forced, and write the kept tiles in ascending order.
-template <int MJ>  // keys per lane held in registers: T <= 64 * MJ
-__global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int force_diag, int direct,
-                                              const double* __restrict__ scores, int32_t* __restrict__ out_cols,
-                                              int32_t* __restrict__ out_cnt, int32_t* __restrict__ row_ptr) {
-  __shared__ uint32_t hist[4][256];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + w;
-  const bool live = row < rows;
-  const int a = live ? row % T : 0;
-  const double* src = scores + (size_t)(live ? row : 0) * T;
-  const int nj = (T + 63) / 64;
+// Wave-wide reductions and scans on DPP lane moves within 16-lane rows plus
+// four readlanes across the rows: no LDS traffic (a lane shuffle would go
+// through the LDS crossbar and its latency).  Results are wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) { return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) { return __int_as_float(dpp<CTRL>(__float_as_int(x))); }
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
-  uint64_t key[MJ];
-#pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    int b = lane + 64 * j;
-    key[j] = (j < nj && b < T && live) ? order_key(src[b]) : 0ull;
+__device__ __forceinline__ int wave_max_int(int x) {
+  x = max(x, dpp<kQuadXor1>(x));
+  x = max(x, dpp<kQuadXor2>(x));
+  x = max(x, dpp<kRowRor4>(x));
+  x = max(x, dpp<kRowRor8>(x));
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ float wave_min_f(float x) {
+  x = fminf(x, dppf<kQuadXor1>(x));
+  x = fminf(x, dppf<kQuadXor2>(x));
+  x = fminf(x, dppf<kRowRor4>(x));
+  x = fminf(x, dppf<kRowRor8>(x));
+  float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  r = fminf(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+  r = fminf(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)));
+  return fminf(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+// max over the 16 lanes of each row (every lane of the row gets it)
+__device__ __forceinline__ float row16_max_f(float x) {
+  x = fmaxf(x, dppf<kQuadXor1>(x));
+  x = fmaxf(x, dppf<kQuadXor2>(x));
+  x = fmaxf(x, dppf<kRowRor4>(x));
+  return fmaxf(x, dppf<kRowRor8>(x));
+}
+// inclusive prefix sum over lanes 0..l (row scans by shifts, then the totals
+// of the rows below)
+__device__ __forceinline__ int wave_prefix_sum(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+// float64 sum over the wave: each row summed by lane moves of both halves,
+// then the four row sums in a fixed order
+__device__ __forceinline__ double dpp_d(double x, int ctrl_sel) {
+  const int lo = __double2loint(x), hi = __double2hiint(x);
+  int l2, h2;
+  switch (ctrl_sel) {
+    case 0: l2 = dpp<kQuadXor1>(lo); h2 = dpp<kQuadXor1>(hi); break;
+    case 1: l2 = dpp<kQuadXor2>(lo); h2 = dpp<kQuadXor2>(hi); break;
+    case 2: l2 = dpp<kRowRor4>(lo); h2 = dpp<kRowRor4>(hi); break;
+    default: l2 = dpp<kRowRor8>(lo); h2 = dpp<kRowRor8>(hi); break;
   }
+  return __hiloint2double(h2, l2);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l), __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x += dpp_d(x, c);
+  return ((readlane_d(x, 0) + readlane_d(x, 16)) + readlane_d(x, 32)) + readlane_d(x, 48);
+}
 
-  // Radix select of the k-th largest key.  After each pass, `prefix` holds the
-  // bits fixed so far, `need` how many keys of that bucket are still needed.
-  // When a bucket holds exactly the keys still needed, every key >= prefix is
-  // kept and the search stops early (the usual case after two or three passes).
-  // Each wave works on its own row and its own LDS histogram, so the waves of
-  // a block never synchronise with each other.
-  uint64_t prefix = 0, mask = 0;
+// The histogram of a radix pass is private to one wave, and the LDS
+// operations of a wave complete in issue order: waiting for them and keeping
+// the compiler from moving memory operations is all the ordering needed (a
+// memory fence would also wait for the wave's outstanding global stores).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+// Top-k of one row held by one wave: key[j] of lane l belongs to column
+// l + 64 j (j < nj); key 0 marks an absent column.  Radix select of the k-th
+// largest key, 8 bits per pass; every key above it is kept and, among keys
+// equal to it, the lowest columns.  Returns the kept flags (bit j of lane l:
+// column l + 64 j).  `hw` is a 256-word LDS histogram owned by this wave.
+template <int MJ, typename K>
+__device__ uint32_t radix_topk(const K (&key)[MJ], int nj, int topk, int lane, uint32_t* hw) {
+  constexpr int BITS = 8 * sizeof(K);
+  // After each pass, `prefix` holds the bits fixed so far, `need` how many
+  // keys of that bucket are still needed.  When a bucket holds exactly the
+  // keys still needed, every key >= prefix is kept and the search stops
+  // early (the usual case after two or three passes).
+  K prefix = 0, mask = 0;
   int need = topk;
   bool done = false;
-  uint32_t* hw = hist[w];
-  // First pass (sign and top exponent bits): the scores of a row fall into a
-  // handful of these digits, so LDS atomics would serialise.  Walk the present
-  // digits from the top instead, counting each with ballots, and stop at the
-  // digit that holds the k-th key.
+  // First pass (sign and top exponent bits): the keys of a row fall into a
+  // handful of these digits, so LDS atomics would serialise.  Walk the
+  // present digits from the top instead, counting each with ballots, and stop
+  // at the digit that holds the k-th key.
   {
     uint32_t pend = 0;
 #pragma unroll
     for (int j = 0; j < MJ; ++j)
-      if (j < nj && key[j] != 0ull) pend |= 1u << j;
+      if (j < nj && key[j] != 0) pend |= 1u << j;
     int cum = 0, digit = 0, dcnt = 0;
     for (;;) {
       int dl = -1;
 #pragma unroll
       for (int j = 0; j < MJ; ++j)
-        if ((pend >> j) & 1u) dl = max(dl, (int)(key[j] >> 56));
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) dl = max(dl, __shfl_xor(dl, off, 64));
+        if ((pend >> j) & 1u) dl = max(dl, (int)(key[j] >> (BITS - 8)));
+      dl = wave_max_int(dl);
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         if (j < nj) {
-          const bool hit = ((pend >> j) & 1u) && (int)(key[j] >> 56) == dl;
+          const bool hit = ((pend >> j) & 1u) && (int)(key[j] >> (BITS - 8)) == dl;
           cnt += __popcll(__ballot(hit));
           if (hit) pend &= ~(1u << j);
         }
@@ -165,31 +153,26 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
       cum += cnt;
     }
     need -= cum;
-    prefix = (uint64_t)digit << 56;
-    mask = 255ull << 56;
+    prefix = (K)digit << (BITS - 8);
+    mask = (K)255 << (BITS - 8);
     done = dcnt == need;
   }
-  for (int shift = 48; shift >= 0 && !done; shift -= 8) {
+  for (int shift = BITS - 16; shift >= 0 && !done; shift -= 8) {
     for (int i = lane; i < 256; i += 64) hw[i] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_order();
 #pragma unroll
     for (int j = 0; j < MJ; ++j)
-      if (j < nj && (key[j] & mask) == prefix && key[j] != 0ull)
-        atomicAdd(&hw[(key[j] >> shift) & 255u], 1u);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+      if (j < nj && (key[j] & mask) == prefix && key[j] != 0)
+        atomicAdd(&hw[(uint32_t)(key[j] >> shift) & 255u], 1u);
+    wave_lds_order();
     // lane l owns digits 4l .. 4l+3; count from the top digit down
     const uint32_t h0 = hw[4 * lane], h1 = hw[4 * lane + 1], h2 = hw[4 * lane + 2], h3 = hw[4 * lane + 3];
     const uint32_t mine = h0 + h1 + h2 + h3;
-    // inclusive suffix sum over lanes (lanes above hold larger digits)
-    uint32_t suf = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
-    uint32_t cum = suf - mine;  // count in digits > 4l+3
+    // count in the digits above this lane's (lanes above hold larger digits):
+    // the total minus the inclusive prefix over lanes 0..l
+    const int pre = wave_prefix_sum((int)mine, lane);
+    const int tot = __builtin_amdgcn_readlane(pre, 63);
+    uint32_t cum = (uint32_t)(tot - pre);
     int found = -1, rest = 0, fcnt = 0;
     const uint32_t hh[4] = {h0, h1, h2, h3};
 #pragma unroll
@@ -203,55 +186,336 @@ __global__ __launch_bounds__(256) void k_topk(int T, int rows, int topk, int for
     }
     const uint64_t bal = __ballot(found >= 0);
     const int src_lane = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
-    const int digit = __shfl(found, src_lane, 64);
-    need = __shfl(rest, src_lane, 64);
-    const int bcnt = __shfl(fcnt, src_lane, 64);
-    prefix |= ((uint64_t)(digit < 0 ? 0 : digit)) << shift;
-    mask |= 255ull << shift;
+    const int digit = __builtin_amdgcn_readlane(found, src_lane);
+    need = __builtin_amdgcn_readlane(rest, src_lane);
+    const int bcnt = __builtin_amdgcn_readlane(fcnt, src_lane);
+    prefix |= ((K)(digit < 0 ? 0 : digit)) << shift;
+    mask |= (K)255 << shift;
     done = bcnt == need;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_order();
   }
   // keep key > kth, plus the `need` lowest-index keys equal to kth; an early
   // exit keeps every key >= prefix (kth = prefix - 1, no ties to break)
-  const uint64_t kth = done ? prefix - 1 : prefix;
+  const K kth = done ? prefix - 1 : prefix;
   if (done) need = 0;
-
-  // selection flags: strictly above the threshold, then ties by lowest index
-  uint32_t sel = 0;  // bit j: element j of this lane is kept
+  uint32_t sel = 0;
   int taken = 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int j = 0; j < MJ; ++j) {
     if (j < nj) {  // nj is wave-uniform; a guard instead of a break keeps key[] in registers
       const bool above = key[j] > kth;
-      const bool eq = key[j] == kth && key[j] != 0ull;
+      const bool eq = key[j] == kth && key[j] != 0;
       const uint64_t be = __ballot(eq);
       const int before = __popcll(be & lt_mask);
       if (above || (eq && taken + before < need)) sel |= 1u << j;
       taken += __popcll(be);
     }
   }
-  if (force_diag && lane == (a & 63)) sel |= 1u << (a >> 6);
+  return sel;
+}
 
-  // emit ascending
-  int base_pos = 0;
-  const size_t obase = direct ? (size_t)row * topk : (size_t)row * (topk + 1);
+// -------------------------------------------------------------- selection
+// One block = 16 consecutive query tiles of one (b, h), four waves.
+//
+//  1. Pooling: float64 sums of the valid rows of each query tile (exact for
+//     bf16 and fp8 values), divided by the valid count -> qbar (written to
+//     the workspace and, if asked, exported).
+//  2. Scores: sigma'_ab = qbar_a . kbar_b for every key tile b on the bf16
+//     matrix cores, each float64 mean split into bf16 hi + lo parts and the
+//     three products hi.hi + hi.lo + lo.hi accumulated in float32.  A fourth
+//     product |qbar_hi| . |kbar_hi| gives A_ab >= sum_e |qbar_e kbar_e| / (1 + 2^-7)^2,
+//     and |sigma' - sigma| <= 1.6e-4 A_ab bounds the error (dropped lo.lo
+//     and remainder terms: 3.05 * 2^-16; 384 float32 additions: 2.3e-5;
+//     a factor 2.2 of margin).
+//  3. Top-k: per row, the approximate top-k A' by (sigma' desc, b asc) and
+//     t' = its smallest score.  With E = the row's largest error bound,
+//     every tile with sigma' > t' + 2E is in the exact top-k, every tile with
+//     sigma' < t' - 2E is out, and only the tiles in between are ranked again
+//     by their exact float64 scores (usually none: the band is ~1e-4 of the
+//     scores, the gap at the k-th score ~1e-3).  So the kept set is exactly
+//     the one the float64 scores give, ties to the lower index.
+//  4. Emission: the kept tiles in ascending order (plus the diagonal when
+//     forced) as a CSR row.
+struct SelectArgs {
+  int T, N, N_pad, topk, force_diag, direct;
+  const void* q;        // [BH][N_pad][D] in the input type
+  const float* qs;      // fp8: [BH][T] tile scales of Q
+  const uint16_t* khi;  // [BH][T][D] bf16 hi part of the key tile means
+  const uint16_t* klo;  // [BH][T][D] bf16 lo part
+  const double* kmean;  // [BH][T][D]
+  double* qmean;        // [BH][T][D], written
+  double* qbar_out;     // optional export [BH][T][D]
+  int32_t* out_cols;    // direct: col_idx [rows][topk]; else [rows][topk + 1]
+  int32_t* out_cnt;     // [rows] when not direct
+  int32_t* row_ptr;     // [rows + 1] when direct
+  int rows;
+  int nbh;              // B * H
+};
+
+constexpr int kSelRows = 16;  // query tiles per block
+constexpr float kScoreErr = 1.6e-4f;
+
+// float64 -> bf16 bits (through float32; the bound above allows the double rounding)
+__device__ __forceinline__ uint32_t bf16_of(double x) { return f32_to_bf16_bits((float)x); }
+__device__ __forceinline__ double bf16_value(uint32_t b) { return (double)bf16_bits_to_f32(b); }
+
+template <typename IT, int D, int MJ>
+__global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
+  constexpr int CPR = D / 8, NCONT = 256 / CPR, KCH = 64 * CPR / 256;
+  constexpr int TP = 64 * MJ + 4;           // row stride of the scores (+4 words: rows on distinct banks)
+  constexpr int POOL_BYTES = NCONT * D * 8;  // pooling partials (float64)
+  constexpr int QF_BYTES = 2 * kSelRows * D * 2;
+  constexpr int SC_BYTES = kSelRows * TP * 4;
+  constexpr int SMEM = (POOL_BYTES + QF_BYTES > SC_BYTES) ? POOL_BYTES + QF_BYTES : SC_BYTES;
+  constexpr bool SCALED = sizeof(IT) == 1;
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  __shared__ float emax[4][kSelRows];
+  double* red = reinterpret_cast<double*>(smem);
+  uint16_t* qh = reinterpret_cast<uint16_t*>(smem + POOL_BYTES);  // [16][D]
+  uint16_t* ql = qh + kSelRows * D;
+  float* sc = reinterpret_cast<float*>(smem);  // [16][TP], once the pooling is done
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int T = a.T;
+  // Block order: the hardware hands block i to XCD i % 8.  XCD x takes heads
+  // x, x + 8, ... one after the other, so the head whose key means its blocks
+  // read (kept in its L2) is shared by all of its blocks in flight.
+  const int nrb = (T + kSelRows - 1) / kSelRows;
+  const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (jb / nrb), a0 = (jb % nrb) * kSelRows;
+  if (bh >= a.nbh) return;
+  const int nr = min(kSelRows, T - a0);
+  const size_t tb = (size_t)bh * T;
+
+  // ---- 1. pooling of the block's query tiles (two tiles of loads in flight)
+  {
+    const IT* Q = reinterpret_cast<const IT*>(a.q) + (size_t)bh * a.N_pad * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, a.N * D * (int)sizeof(IT));
+    const int col8 = tid % CPR, row0 = tid / CPR;
+    Chunk8<IT> cq[4][KCH];
+    auto load = [&](int r, int slot) {
+      // a tile past the block's range reads beyond the view: zeros, no traffic
+      const int t = r < nr ? a0 + r : T;
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    if (j < nj) {
-      const bool s = (sel >> j) & 1u;
-      const uint64_t bs = __ballot(s);
-      if (s && live) out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
-      base_pos += __popcll(bs);
+      for (int i = 0; i < KCH; ++i) bload8(cq[slot][i], qrs, (t * 64 + row0 + i * NCONT) * D + col8 * 8);
+    };
+    auto reduce = [&](int r, int slot) {
+      double p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = 0.0;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] += (double)elem(cq[slot][i], e);
+      load(r + 4, slot);  // the registers are free again: the tile four ahead
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[row0 * D + col8 * 8 + e] = p[e];
+      __syncthreads();
+      if (tid < D) {
+        const int at = a0 + r;
+        double sum = 0.0;
+#pragma unroll 4
+        for (int c2 = 0; c2 < NCONT; ++c2) sum += red[c2 * D + tid];
+        if constexpr (SCALED) sum *= (double)a.qs[tb + at];
+        const double mean = sum / (double)min(64, a.N - at * 64);
+        const size_t o = (tb + at) * D + tid;
+        a.qmean[o] = mean;
+        if (a.qbar_out) a.qbar_out[o] = mean;
+        const uint32_t hb = bf16_of(mean);
+        qh[r * D + tid] = (uint16_t)hb;
+        ql[r * D + tid] = (uint16_t)bf16_of(mean - bf16_value(hb));
+      }
+      __syncthreads();
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load(i, i);
+    for (int r = 0; r < nr; r += 4) {
+      reduce(r, 0);
+      if (r + 1 < nr) reduce(r + 1, 1);
+      if (r + 2 < nr) reduce(r + 2, 2);
+      if (r + 3 < nr) reduce(r + 3, 3);
+    }
+    for (int i = tid; i < (kSelRows - nr) * D; i += 256) {  // rows past T: zero operands
+      qh[nr * D + i] = 0;
+      ql[nr * D + i] = 0;
     }
   }
-  if (live && lane == 0) {
-    if (direct) {
-      row_ptr[row] = row * topk;
-      if (row == rows - 1) row_ptr[rows] = rows * topk;
+  __syncthreads();
+
+  // ---- 2. approximate scores and their error bounds
+  Frag<bf16_t> ah[D / 32], al[D / 32], aa[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    ah[c].w = *reinterpret_cast<const u32x4*>(&qh[l16 * D + 32 * c + 8 * g]);
+    al[c].w = *reinterpret_cast<const u32x4*>(&ql[l16 * D + 32 * c + 8 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aa[c].w[i] = ah[c].w[i] & 0x7FFF7FFFu;
+  }
+  __syncthreads();  // the operands are in registers: the region now holds scores
+  // the head's key means as bounds-checked buffers: tiles past T read as zeros
+  const __amdgpu_buffer_rsrc_t khr = make_rsrc(a.khi + tb * D, T * D * 2);
+  const __amdgpu_buffer_rsrc_t klr = make_rsrc(a.klo + tb * D, T * D * 2);
+  const int nkb = (T + 15) / 16;
+  float em[4] = {0.f, 0.f, 0.f, 0.f};
+  // three key blocks of operands in flight per wave (blocks w, w + 4, w + 8, ...)
+  Frag<bf16_t> bhf[3][D / 32], blf[3][D / 32];
+  auto loadb = [&](int kb, int slot) {
+    const int off = ((16 * kb + l16) * D + 8 * g) * 2;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      bhf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(khr, off + 64 * c, 0, 0);
+      blf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(klr, off + 64 * c, 0, 0);
+    }
+  };
+  auto scores = [&](int kb, int slot) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acca = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      Frag<bf16_t> babs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) babs.w[i] = bhf[slot][c].w[i] & 0x7FFF7FFFu;
+      mma(acc, ah[c], bhf[slot][c]);
+      mma(acc, ah[c], blf[slot][c]);
+      mma(acc, al[c], bhf[slot][c]);
+      mma(acca, aa[c], babs);
+    }
+    loadb(kb + 12, slot);  // in flight while the next two blocks are multiplied
+    // accumulator: lane holds column b = 16 kb + l16, rows 4 g + i
+    const int b = 16 * kb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[(4 * g + i) * TP + b] = acc[i];
+      em[i] = fmaxf(em[i], acca[i]);
+    }
+  };
+  loadb(w, 0);
+  loadb(w + 4, 1);
+  loadb(w + 8, 2);
+  for (int kb = w; kb < nkb; kb += 12) {
+    scores(kb, 0);
+    if (kb + 4 < nkb) scores(kb + 4, 1);
+    if (kb + 8 < nkb) scores(kb + 8, 2);
+  }
+  // largest bound per row: over the 16 columns of a lane group, then the waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    em[i] = row16_max_f(em[i]);
+    if (l16 == 0) emax[w][4 * g + i] = em[i];
+  }
+  __syncthreads();
+
+  // ---- 3. top-k of each row and 4. emission (wave w: rows w, w + 4, ...)
+  const int nj = (T + 63) / 64;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = w; r < nr; r += 4) {
+    const int at = a0 + r;
+    const int row = (int)(tb + at);
+    float sv[MJ];
+    uint32_t key[MJ];
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {  // (columns past T read the row's padding and are marked absent)
+      const int b = lane + 64 * j;
+      sv[j] = sc[r * TP + b];
+      key[j] = b < T ? order_key32(sv[j]) : 0u;
+    }
+    // this row's part of the score region now serves as its histogram
+    uint32_t* hw = reinterpret_cast<uint32_t*>(&sc[r * TP]);
+    wave_lds_order();
+    const int k = min(a.topk, T);
+    // the approximate top-k only fixes t' (ties among approximate scores near
+    // t' are all candidates below and are ranked exactly there)
+    uint32_t sel = radix_topk<MJ>(key, nj, k, lane, hw);
+    // t' = the smallest approximate score kept
+    float tmin = INFINITY;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j)
+      if ((sel >> j) & 1u) tmin = fminf(tmin, sv[j]);
+    tmin = wave_min_f(tmin);
+    const float E = kScoreErr * fmaxf(fmaxf(emax[0][r], emax[1][r]), fmaxf(emax[2][r], emax[3][r]));
+    const float hi = tmin + 2.f * E, lo = tmin - 2.f * E;
+    uint32_t fin = 0, fcand = 0;
+    int nin = 0, ncand = 0;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      if (j < nj) {
+        const bool ok = key[j] != 0u;
+        const bool in = ok && sv[j] > hi;
+        const bool cand = ok && !in && sv[j] >= lo;
+        if (in) fin |= 1u << j;
+        if (cand) fcand |= 1u << j;
+        nin += __popcll(__ballot(in));
+        ncand += __popcll(__ballot(cand));
+      }
+    }
+    if (ncand != k - nin) {
+      // rank the candidates by their exact float64 scores: in-tiles get the
+      // largest key, candidates order_key(sigma), the rest stay absent.  A few
+      // candidates: one wave-wide dot product each; many (degenerate rows,
+      // e.g. an all-zero query tile, where every score ties): one per lane.
+      const double* qrow = a.qmean + (tb + at) * D;  // written by this block before a barrier
+      const bool few = ncand <= 4;
+      uint64_t key64[MJ];
+      double qv[D / 64];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) qv[e] = qrow[lane + 64 * e];
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        if (j < nj) {
+          key64[j] = ((fin >> j) & 1u) ? ~0ull : 0ull;
+          uint64_t bal = __ballot((fcand >> j) & 1u);
+          if (few) {
+            while (bal) {
+              const int src = __ffsll((unsigned long long)bal) - 1;
+              bal &= bal - 1;
+              const double* krow = a.kmean + (tb + src + 64 * j) * D;
+              double part = 0.0;
+#pragma unroll
+              for (int e = 0; e < D / 64; ++e) part = fma(qv[e], krow[lane + 64 * e], part);
+              part = wave_sum_d(part);
+              if (lane == src) key64[j] = order_key(part);
+            }
+          } else if ((fcand >> j) & 1u) {
+            const double2* krow = reinterpret_cast<const double2*>(a.kmean + (tb + lane + 64 * j) * D);
+            const double2* qr2 = reinterpret_cast<const double2*>(qrow);
+            double acc = 0.0;
+#pragma unroll 4
+            for (int e = 0; e < D / 2; ++e) {
+              const double2 kk = krow[e], qq = qr2[e];
+              acc = fma(qq.x, kk.x, acc);
+              acc = fma(qq.y, kk.y, acc);
+            }
+            key64[j] = order_key(acc);
+          }
+        }
+      }
+      wave_lds_order();
+      sel = radix_topk<MJ>(key64, nj, k, lane, hw);
     } else {
-      out_cnt[row] = base_pos;
+      sel = fin | fcand;
+    }
+    if (a.force_diag && lane == (at & 63)) sel |= 1u << (at >> 6);
+
+    // emit ascending
+    int base_pos = 0;
+    const size_t obase = a.direct ? (size_t)row * a.topk : (size_t)row * (a.topk + 1);
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      if (j < nj) {
+        const bool s = (sel >> j) & 1u;
+        const uint64_t bs = __ballot(s);
+        if (s) a.out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
+        base_pos += __popcll(bs);
+      }
+    }
+    if (lane == 0) {
+      if (a.direct) {
+        a.row_ptr[row] = row * a.topk;
+        if (row == a.rows - 1) a.row_ptr[a.rows] = a.rows * a.topk;
+      } else {
+        a.out_cnt[row] = base_pos;
+      }
     }
   }
 }
@@ -289,36 +553,39 @@ __global__ void k_compact(int rows, int stride, const int32_t* __restrict__ tmp,
   for (int i = 0; i < n; ++i) col_idx[o + i] = tmp[(size_t)row * stride + i];
 }
 
-hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st) {
-  // Column parts (1..4): the split whose blocks fill the 512 block slots (two
-  // blocks per CU) best over whole rounds, so that no last round runs mostly
-  // empty (760 row blocks at 720P: 2 parts, 1520 blocks, 99% of 3 rounds).
-  const long rowblocks = (long)((s.T + 63) / 64) * s.B * s.H;
-  const int nch = (s.T + kScoreCols - 1) / kScoreCols;
-  int parts = 1;
-  double best = 0.0;
-  for (int p = 1; p <= 4 && p <= nch; ++p) {
-    const long blocks = rowblocks * p;
-    const double fill = (double)blocks / (double)(((blocks + 511) / 512) * 512);
-    if (fill > best + 1e-9) { best = fill; parts = p; }
-  }
-  dim3 g1((s.T + 63) / 64, s.B * s.H, parts);
-  if (s.d == 64) k_scores<64><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
-  else k_scores<128><<<g1, 256, 0, st>>>(s.T, w.qmean, w.kmean, w.scores);
-  return hipGetLastError();
+template <typename IT, int D>
+static void select_by_mj(int nj, dim3 grid, const SelectArgs& a, hipStream_t st) {
+  if (nj <= 8) k_select<IT, D, 8><<<grid, 256, 0, st>>>(a);
+  else if (nj <= 16) k_select<IT, D, 16><<<grid, 256, 0, st>>>(a);
+  else if (nj <= 19) k_select<IT, D, 19><<<grid, 256, 0, st>>>(a);
+  else if (nj <= 24) k_select<IT, D, 24><<<grid, 256, 0, st>>>(a);
+  else k_select<IT, D, kMaxJ><<<grid, 256, 0, st>>>(a);
 }
 
-hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st) {
+hipError_t launch_select(const Shape& s, const void* q, const float* qs, const Scratch& w, int32_t* row_ptr,
+                         int32_t* col_idx, double* qbar_out, hipStream_t st) {
   const int rows = s.B * s.H * s.T;
-  hipError_t e;
   const int direct = s.force_diag ? 0 : 1;
-  int32_t* cols = direct ? col_idx : w.sel_tmp;
-  const int nj = (s.T + 63) / 64, grid = (rows + 3) / 4;
-  if (nj <= 8) k_topk<8><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
-  else if (nj <= 16) k_topk<16><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
-  else if (nj <= 20) k_topk<20><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
-  else k_topk<kMaxJ><<<grid, 256, 0, st>>>(s.T, rows, s.topk, s.force_diag, direct, w.scores, cols, w.sel_cnt, row_ptr);
-  e = hipGetLastError();
+  SelectArgs a{};
+  a.T = s.T; a.N = s.N; a.N_pad = s.N_pad; a.topk = s.topk; a.force_diag = s.force_diag; a.direct = direct;
+  a.q = q; a.qs = qs; a.khi = w.khi; a.klo = w.klo; a.kmean = w.kmean; a.qmean = w.qmean; a.qbar_out = qbar_out;
+  a.out_cols = direct ? col_idx : w.sel_tmp;
+  a.out_cnt = w.sel_cnt;
+  a.row_ptr = row_ptr;
+  a.rows = rows;
+  a.nbh = s.B * s.H;
+  const int nj = (s.T + 63) / 64;
+  const dim3 grid(8 * ((s.B * s.H + 7) / 8) * ((s.T + kSelRows - 1) / kSelRows));
+  if (s.d == 64) {
+    if (s.dt == Dt::F32) select_by_mj<float, 64>(nj, grid, a, st);
+    else if (s.dt == Dt::BF16) select_by_mj<bf16_t, 64>(nj, grid, a, st);
+    else select_by_mj<fp8_t, 64>(nj, grid, a, st);
+  } else {
+    if (s.dt == Dt::F32) select_by_mj<float, 128>(nj, grid, a, st);
+    else if (s.dt == Dt::BF16) select_by_mj<bf16_t, 128>(nj, grid, a, st);
+    else select_by_mj<fp8_t, 128>(nj, grid, a, st);
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || direct) return e;
   k_scan<<<1, 1024, 0, st>>>(rows, w.sel_cnt, row_ptr);
   e = hipGetLastError();

@@ -14,14 +14,14 @@ hipError_t launch_rope_table(const Shape& s, float2* tab, hipStream_t st) {
 hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, const void* v,
                               const float* qs, const float* ks, const float* vs,
                               const void* uk, bool pool, bool state, const Scratch& w,
-                              double* qbar_out, double* kbar_out, hipStream_t st) {
+                              double* kbar_out, hipStream_t st) {
   StreamArgs a{};
   a.N = s.N; a.N_pad = s.N_pad; a.T = s.T;
   a.nchunk = stream_chunks(s);
   a.tpc = (s.T + a.nchunk - 1) / a.nchunk;
   a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
   a.q = q; a.k = k; a.v = v; a.qs = qs; a.ks = ks; a.vs = vs; a.uk = uk; a.H = s.H;
-  a.qmean = w.qmean; a.kmean = w.kmean; a.qbar_out = qbar_out; a.kbar_out = kbar_out;
+  a.kmean = w.kmean; a.khi = w.khi; a.klo = w.klo; a.kbar_out = kbar_out;
   a.part_s = w.part_s; a.part_z = w.part_z; a.rope = w.rope; a.vt = w.vt;
   if (state && s.compl_keys) { a.tile_s = w.tile_s; a.tile_z = w.tile_z; }
   a.nrope = rope_entries(s);

@@ -51,7 +51,8 @@ inline int stream_chunks(const Shape& s) {
 struct Scratch {
   double* qmean = nullptr;     // [BH][T][d] tile means of Q
   double* kmean = nullptr;     // [BH][T][d] tile means of K
-  double* scores = nullptr;    // [BH][T][T] float64 pooled scores
+  uint16_t* khi = nullptr;     // [BH][T][d] bf16 hi part of the key tile means
+  uint16_t* klo = nullptr;     // [BH][T][d] bf16 lo part
   int32_t* sel_tmp = nullptr;  // [BH*T][kmax] per-row selection (forced-diagonal path)
   int32_t* sel_cnt = nullptr;  // [BH*T]
   int32_t* row_ptr = nullptr;  // [BH*T + 1] internal CSR when the caller exports none
@@ -88,7 +89,7 @@ struct Scratch {
 // Workspace planning: byte offsets of each region for a given call.
 struct Plan {
   size_t total = 0;
-  size_t off_qmean = 0, off_kmean = 0, off_scores = 0, off_sel_tmp = 0, off_sel_cnt = 0;
+  size_t off_qmean = 0, off_kmean = 0, off_khi = 0, off_klo = 0, off_sel_tmp = 0, off_sel_cnt = 0;
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
   size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
   size_t off_tile_s = 0, off_tile_z = 0, off_s_full = 0, off_wo = 0;
@@ -107,11 +108,13 @@ hipError_t launch_rope_table(const Shape& s, float2* tab, hipStream_t st);
 hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, const void* v,
                               const float* qs, const float* ks, const float* vs,
                               const void* uk, bool pool, bool state, const Scratch& w,
-                              double* qbar_out, double* kbar_out, hipStream_t st);
+                              double* kbar_out, hipStream_t st);
 hipError_t launch_vtranspose(const Shape& s, const void* v, const Scratch& w, hipStream_t st);
 hipError_t launch_finalize(const Shape& s, const void* uq, const void* wo, const Scratch& w, hipStream_t st);
-hipError_t launch_scores(const Shape& s, const Scratch& w, hipStream_t st);
-hipError_t launch_topk(const Shape& s, const Scratch& w, int32_t* row_ptr, int32_t* col_idx, hipStream_t st);
+// Selection: pooling of the query tiles, pooled scores, per-row top-k and the
+// CSR (after a streaming pass that pooled the key tiles).
+hipError_t launch_select(const Shape& s, const void* q, const float* qs, const Scratch& w, int32_t* row_ptr,
+                         int32_t* col_idx, double* qbar_out, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const float* qs, const float* ks, const float* vs,
                          const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,

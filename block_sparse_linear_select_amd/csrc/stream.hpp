@@ -1,9 +1,11 @@
-// Kernels of the streaming pass over Q, K, V (one read of each) and the finalize step of the
+// Kernels of the streaming pass over K and V (one read of each) and the finalize step of the
 // linear branch.
 //
-//  * Tile pooling: float64 column sums of the valid rows of every 64-token tile
-//    of Q and K, divided by the valid count (the mean-pooled tile statistic used
-//    to find the high-energy tiles; SparkDiffusion news article, section 05).
+//  * Tile pooling of K: float64 column sums of the valid rows of every 64-token
+//    tile, divided by the valid count (the mean-pooled tile statistic used to
+//    find the high-energy tiles; SparkDiffusion news article, section 05), also
+//    split into bf16 hi + lo parts for the selection's matrix-core scores.  The
+//    query tiles are pooled by the selection kernel itself.
 //  * Linear key/value state of the rotary low-rank branch (same section: a
 //    low-rank linear branch with rotary position information):
 //      F = K U_k (matrix cores), phi = elu(F) + 1, z += sum_j phi_j,
@@ -11,7 +13,7 @@
 //      over tokens).  Each block writes one partial (S, z); the finalize kernel
 //      adds the partials in a fixed order, so results are bitwise reproducible.
 //
-// The pass is HBM-bound: every element of Q, K, V is read once with 16-byte
+// The pass is HBM-bound: every element of K and V is read once with 16-byte
 // loads, the next tile is prefetched into registers while the current one is
 // processed, and all arithmetic runs from LDS and registers.
 #pragma once
@@ -154,9 +156,9 @@ struct StreamArgs {
   const float* vs;
   const void* uk;  // [H][d][r] in the parameter type
   int H;
-  double* qmean;  // [BH][T][d] tile means of Q
   double* kmean;  // [BH][T][d] tile means of K
-  double* qbar_out;
+  uint16_t* khi;  // [BH][T][d] bf16 hi part of the means
+  uint16_t* klo;  // [BH][T][d] bf16 lo part (mean - hi, rounded)
   double* kbar_out;
   float* part_s;
   float* part_z;
@@ -199,7 +201,6 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   __shared__ __align__(16) OT Vt[(STATE && !VROW) ? D * VSTR : 1];
   __shared__ __align__(16) OT Vr[(STATE && VROW) ? 64 * VRS : 1];
   __shared__ __align__(16) uint8_t Vt8[(STATE && sizeof(T) == 1) ? D * 80 : 16];  // fp8 V^T tile for the sparse kernel
-  __shared__ double redq[POOL ? NCONT * D : 1];
   __shared__ double redk[POOL ? NCONT * D : 1];
   __shared__ int spos[64];
   __shared__ float2 rtab[RLDS ? kRopeLdsMax : 1];
@@ -213,7 +214,6 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   if (t0 >= t1) return;
 
   const size_t base = (size_t)bh * a.N_pad * D;
-  const T* Q = reinterpret_cast<const T*>(a.q) + base;
   const T* K = reinterpret_cast<const T*>(a.k) + base;
   const T* V = reinterpret_cast<const T*>(a.v) + base;
   const int col8 = tid % CPR;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
 
   // buffer views of this head's valid rows: rows >= N read as zeros
   const int nbytes = a.N * D * (int)sizeof(T);
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, nbytes), krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, nbytes), vrs = make_rsrc(V, nbytes);
   // Two tiles in flight per block: while tile t is processed from one
   // register set, tile t + 1 is already loading into the other, and tile t + 2
   // is issued into the first set once tile t sits in LDS.  Every step issues
@@ -262,13 +262,12 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   // compiler can count the loads in flight and waits for the current tile
   // only.  fp8 inputs load their per-tile scales with the tile.
   constexpr bool SCALED = sizeof(T) == 1;
-  struct TileRegs { Chunk8<T> q[KCH], k[KCH], v[VROW ? KCH : 4]; float sq, sk, sv; };
+  struct TileRegs { Chunk8<T> k[KCH], v[VROW ? KCH : 4]; float sk, sv; };
   TileRegs tra, trb;
   const size_t sbase = (size_t)bh * a.T;
   auto load_tile = [&](int t, TileRegs& c) {
     if constexpr (SCALED) {  // (scales exist for every fp8 tensor a step reads)
       const size_t i = sbase + min(t, a.T - 1);
-      if constexpr (POOL) c.sq = a.qs[i];
       c.sk = a.ks[i];
       if constexpr (STATE) c.sv = a.vs[i];
     }
@@ -276,7 +275,6 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
     for (int i = 0; i < KCH; ++i) {
       const int e = (t * 64 + row0 + i * NCONT) * D + col8 * 8;
       bload8(c.k[i], krs, e);
-      if constexpr (POOL) bload8(c.q[i], qrs, e);
     }
     if constexpr (STATE && VROW) {
 #pragma unroll
@@ -293,22 +291,19 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   auto process = [&](int t, TileRegs& c) {
     const bool live = t < t1;  // false: a step past the chunk, which only issues its loads
     // this tile's scales, taken before the registers are reloaded
-    const float tsq = SCALED && POOL ? c.sq : 1.f, tsk = SCALED ? c.sk : 1.f, tsv = SCALED && STATE ? c.sv : 1.f;
+    const float tsk = SCALED ? c.sk : 1.f, tsv = SCALED && STATE ? c.sv : 1.f;
     if (live) {
       // ---- registers -> LDS
       if constexpr (POOL) {
-        double pq[8], pk[8];
+        double pk[8];
   #pragma unroll
-        for (int e = 0; e < 8; ++e) { pq[e] = 0.0; pk[e] = 0.0; }
+        for (int e = 0; e < 8; ++e) pk[e] = 0.0;
   #pragma unroll
         for (int i = 0; i < KCH; ++i)
   #pragma unroll
-          for (int e = 0; e < 8; ++e) { pq[e] += (double)elem(c.q[i], e); pk[e] += (double)elem(c.k[i], e); }
+          for (int e = 0; e < 8; ++e) pk[e] += (double)elem(c.k[i], e);
   #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          redq[row0 * D + col8 * 8 + e] = pq[e];
-          redk[row0 * D + col8 * 8 + e] = pk[e];
-        }
+        for (int e = 0; e < 8; ++e) redk[row0 * D + col8 * 8 + e] = pk[e];
       }
       if constexpr (STATE) {
   #pragma unroll
@@ -426,21 +421,19 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
         }
       }
       if constexpr (POOL) {
-        // thread tid < D: column tid of Q; D <= tid < 2 D: column tid - D of K
-        static_assert(2 * D <= 256, "one thread per pooled column");
-        if (tid < 2 * D) {
-          const bool isk = tid >= D;
-          const int col = isk ? tid - D : tid;
-          const double* red = isk ? redk : redq;
+        // thread tid < D: column tid of K
+        if (tid < D) {
           double sum = 0.0;
   #pragma unroll
-          for (int c = 0; c < NCONT; ++c) sum += red[c * D + col];
-          if constexpr (SCALED) sum *= (double)(isk ? tsk : tsq);
+          for (int c = 0; c < NCONT; ++c) sum += redk[c * D + tid];
+          if constexpr (SCALED) sum *= (double)tsk;
           const double mean = sum / (double)min(64, a.N - t * 64);
-          const size_t o = ((size_t)bh * a.T + t) * D + col;  // one 1 KB row per tile
-          (isk ? a.kmean : a.qmean)[o] = mean;
-          double* ext = isk ? a.kbar_out : a.qbar_out;
-          if (ext) ext[o] = mean;
+          const size_t o = ((size_t)bh * a.T + t) * D + tid;  // one 1 KB row per tile
+          a.kmean[o] = mean;
+          if (a.kbar_out) a.kbar_out[o] = mean;
+          const uint32_t hb = f32_to_bf16_bits((float)mean);
+          a.khi[o] = (uint16_t)hb;
+          a.klo[o] = (uint16_t)f32_to_bf16_bits((float)(mean - (double)bf16_bits_to_f32(hb)));
         }
       }
       __syncthreads();

@@ -149,10 +149,10 @@ const char* hsa_attn_version(void);
  */
 enum {
   HSA_ATTN_KERNEL_ROPE = 0,      /* RoPE cos/sin table */
-  HSA_ATTN_KERNEL_STREAM = 1,    /* tile pooling + linear key/value state pass */
+  HSA_ATTN_KERNEL_STREAM = 1,    /* key tile pooling + linear key/value state pass */
   HSA_ATTN_KERNEL_FINALIZE = 2,  /* state reduction, S W_o, readout operands */
-  HSA_ATTN_KERNEL_SCORES = 3,    /* pooled score grid */
-  HSA_ATTN_KERNEL_TOPK = 4,      /* per-row top-k and CSR emission */
+  HSA_ATTN_KERNEL_SELECT = 3,    /* query tile pooling, pooled scores, per-row top-k, CSR emission */
+  HSA_ATTN_KERNEL_UNUSED4 = 4,   /* no kernel is timed under this kind */
   HSA_ATTN_KERNEL_ATTEND = 5,    /* block-sparse flash attention + linear readout */
   HSA_ATTN_KERNEL_QUANT = 6,     /* per-row FP8 quantisation of activations */
   HSA_ATTN_KERNEL_PROJ = 7,      /* W8A8 FP8 QKV projection with fused output quantisation */
@@ -165,12 +165,20 @@ int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
 
 /*
- * Tile selection: mean-pool Q and K per 64-token tile (float64 sums of the
- * valid rows), score every (query tile, key tile) pair by the float64 dot
- * product of the means, keep the top-k key tiles of every row (ties: lower
- * index first; plus the diagonal tile if force_diag) and emit them as CSR.
+ * Tile selection (SparkDiffusion news article, section 05: the sparse branch
+ * keeps the high-energy query/key tile interactions; section 01: 90% / 97% of
+ * the tiles are skipped, here a fixed top-k per query-tile row).  Mean-pool Q
+ * and K per 64-token tile (float64 sums of the valid rows), score every
+ * (query tile, key tile) pair by the dot product of the means, keep the top-k
+ * key tiles of every row (ties: lower index first; plus the diagonal tile if
+ * force_diag) and emit them as CSR.  The kept set is the one the float64
+ * scores give: scores are formed on the matrix cores from bf16 hi + lo parts
+ * of the means with a rigorous error bound, and the tiles whose score lies
+ * within that bound of the k-th one are ranked again by their float64 scores.
+ *   q, k: [B, H, N_pad, d] device, in_dtype; q_scale, k_scale: FP8 tile scales.
  *   row_ptr [B*H*T + 1], col_idx [B*H*T*(topk+force_diag)]: outputs.
  *   qbar_out, kbar_out: optional float64 [B, H, T, d] tile means (NULL to skip).
+ *   Workspace: HSA_ATTN_CALL_BLOCK_SELECT.  Errors as for every call.
  */
 int hsa_block_select(const hsa_attn_desc* desc, const void* q, const void* k,
                      const float* q_scale, const float* k_scale,

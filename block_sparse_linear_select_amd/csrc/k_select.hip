@@ -31,6 +31,15 @@ __device__ __forceinline__ float key32_value(uint32_t k) {
 
 constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row (keys per lane: MJ <= kMaxJ)
 
+// The histogram of a radix pass is private to one wave, and the LDS
+// operations of a wave complete in issue order: waiting for them and keeping
+// the compiler from moving memory operations is all the ordering needed (a
+// memory fence would also wait for the wave's outstanding global stores).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 // Wave-wide reductions and scans on DPP lane moves within 16-lane rows plus
 // four readlanes across the rows: no LDS traffic (a lane shuffle would go
 // through the LDS crossbar and its latency).  Results are wave-uniform.
@@ -100,13 +109,63 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return ((readlane_d(x, 0) + readlane_d(x, 16)) + readlane_d(x, 32)) + readlane_d(x, 48);
 }
 
-// The histogram of a radix pass is private to one wave, and the LDS
-// operations of a wave complete in issue order: waiting for them and keeping
-// the compiler from moving memory operations is all the ordering needed (a
-// memory fence would also wait for the wave's outstanding global stores).
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
+// The k-th largest of the values of the lanes in `live` (1 <= k <= their
+// number, counting repeats): the value v with #{x > v} < k <= #{x >= v},
+// fixed one key bit at a time from the top by ballots (order-preserving
+// keys).  Wave-uniform; no cross-lane data movement besides the ballots.
+__device__ __forceinline__ float kth_largest_lane(float x, bool live, int k) {
+  const uint32_t key = order_key32(x);
+  uint64_t cand = __ballot(live);
+  uint32_t prefix = 0;
+  int need = k;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint64_t ones = __ballot((key >> bit) & 1u) & cand;
+    const int c1 = __popcll(ones);
+    if (c1 >= need) {
+      prefix |= 1u << bit;
+      cand = ones;
+    } else {
+      need -= c1;
+      cand &= ~ones;
+    }
+  }
+  return key32_value(prefix);
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowRor4>(x);
+  x += dpp<kRowRor8>(x);
+  return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+         (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+}
+
+// The same k-th largest by ranking on the vector units: the 64 values go to
+// a wave-private LDS buffer, every lane reads them all back (broadcast reads,
+// 16 at a time) and counts those above and not below its own, so the wave's
+// scalar unit (shared by the CU's waves) stays free.
+__device__ __forceinline__ float kth_largest_vec(float x, bool live, int k, int lane, float* buf) {
+  const float xv = live ? x : -INFINITY;
+  buf[lane] = xv;
+  wave_lds_order();
+  int gt = 0, ge = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float4 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = reinterpret_cast<const float4*>(buf)[4 * b + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gt += (o[i].x > xv) + (o[i].y > xv) + (o[i].z > xv) + (o[i].w > xv);
+      ge += (o[i].x >= xv) + (o[i].y >= xv) + (o[i].z >= xv) + (o[i].w >= xv);
+    }
+  }
+  wave_lds_order();  // read before the buffer is written again
+  const uint64_t bl = __ballot(live && gt < k && ge >= k);
+  const int src = __ffsll((unsigned long long)bl) - 1;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), src));
 }
 
 // Top-k of one row held by one wave: key[j] of lane l belongs to column
@@ -409,6 +468,7 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
   // ---- 3. top-k of each row and 4. emission (wave w: rows w, w + 4, ...)
   const int nj = (T + 63) / 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int kept[kSelRows / 4] = {0, 0, 0, 0};
   for (int r = w; r < nr; r += 4) {
     const int at = a0 + r;
     const int row = (int)(tb + at);
@@ -420,35 +480,66 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
       sv[j] = sc[r * TP + b];
       key[j] = b < T ? order_key32(sv[j]) : 0u;
     }
-    // this row's part of the score region now serves as its histogram
+    // this row's part of the score region now serves as scratch of this wave
     uint32_t* hw = reinterpret_cast<uint32_t*>(&sc[r * TP]);
+    float* slot = &sc[r * TP];
     wave_lds_order();
     const int k = min(a.topk, T);
-    // the approximate top-k only fixes t' (ties among approximate scores near
-    // t' are all candidates below and are ranked exactly there)
-    uint32_t sel = radix_topk<MJ>(key, nj, k, lane, hw);
-    // t' = the smallest approximate score kept
-    float tmin = INFINITY;
+    // t' = the k-th largest approximate score (counting repeats).  The k-th
+    // largest of the 64 lane maxima is a lower bound theta of t' (k of them
+    // are at least theta), so the top-k lies among the scores >= theta; when
+    // those are at most 64 (the usual case), t' is found by ranking them one
+    // per lane.  Otherwise, a radix select over all scores.
+    float tmin = 0.f;
+    bool fast = false;
+    if (k <= 64) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < MJ; ++j)
-      if ((sel >> j) & 1u) tmin = fminf(tmin, sv[j]);
-    tmin = wave_min_f(tmin);
+      for (int j = 0; j < MJ; ++j)
+        if (key[j] != 0u) mx = fmaxf(mx, sv[j]);
+      const float theta = kth_largest_vec(mx, mx > -INFINITY, k, lane, slot + 64);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) cnt += (key[j] != 0u && sv[j] >= theta) ? 1 : 0;
+      const int pre = wave_prefix_sum(cnt, lane);
+      const int c = __builtin_amdgcn_readlane(pre, 63);
+      if (c <= 64) {
+        int pos = pre - cnt;  // this lane's candidates go to slots pos, pos + 1, ...
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+          if (key[j] != 0u && sv[j] >= theta) slot[pos++] = sv[j];
+        }
+        wave_lds_order();
+        const float cv = lane < c ? slot[lane] : -INFINITY;
+        tmin = kth_largest_vec(cv, lane < c, k, lane, slot + 64);
+        fast = true;
+        wave_lds_order();  // the slots are read before the region is used again
+      }
+    }
+    if (!fast) {
+      const uint32_t sel = radix_topk<MJ>(key, nj, k, lane, hw);
+      tmin = INFINITY;
+#pragma unroll
+      for (int j = 0; j < MJ; ++j)
+        if ((sel >> j) & 1u) tmin = fminf(tmin, sv[j]);
+      tmin = wave_min_f(tmin);
+    }
+    uint32_t sel = 0;
     const float E = kScoreErr * fmaxf(fmaxf(emax[0][r], emax[1][r]), fmaxf(emax[2][r], emax[3][r]));
     const float hi = tmin + 2.f * E, lo = tmin - 2.f * E;
     uint32_t fin = 0, fcand = 0;
-    int nin = 0, ncand = 0;
+    int cin = 0, ccand = 0;
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
-      if (j < nj) {
-        const bool ok = key[j] != 0u;
-        const bool in = ok && sv[j] > hi;
-        const bool cand = ok && !in && sv[j] >= lo;
-        if (in) fin |= 1u << j;
-        if (cand) fcand |= 1u << j;
-        nin += __popcll(__ballot(in));
-        ncand += __popcll(__ballot(cand));
-      }
+      const bool ok = key[j] != 0u;
+      const bool in = ok && sv[j] > hi;
+      const bool cand = ok && !in && sv[j] >= lo;
+      fin |= (in ? 1u : 0u) << j;
+      fcand |= (cand ? 1u : 0u) << j;
+      cin += in ? 1 : 0;
+      ccand += cand ? 1 : 0;
     }
+    const int nin = wave_sum_int(cin), ncand = wave_sum_int(ccand);
     if (ncand != k - nin) {
       // rank the candidates by their exact float64 scores: in-tiles get the
       // largest key, candidates order_key(sigma), the rest stay absent.  A few
@@ -461,22 +552,48 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) qv[e] = qrow[lane + 64 * e];
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        if (j < nj) {
-          key64[j] = ((fin >> j) & 1u) ? ~0ull : 0ull;
-          uint64_t bal = __ballot((fcand >> j) & 1u);
-          if (few) {
+      for (int j = 0; j < MJ; ++j) key64[j] = ((fin >> j) & 1u) ? ~0ull : 0ull;
+      if (few) {
+        // the (at most four) candidate columns, their key means loaded together
+        int cidx[4] = {0, 0, 0, 0};
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+          if (j < nj) {
+            uint64_t bal = __ballot((fcand >> j) & 1u);
             while (bal) {
               const int src = __ffsll((unsigned long long)bal) - 1;
               bal &= bal - 1;
-              const double* krow = a.kmean + (tb + src + 64 * j) * D;
-              double part = 0.0;
 #pragma unroll
-              for (int e = 0; e < D / 64; ++e) part = fma(qv[e], krow[lane + 64 * e], part);
-              part = wave_sum_d(part);
-              if (lane == src) key64[j] = order_key(part);
+              for (int i = 0; i < 4; ++i)
+                if (i == n) cidx[i] = src + 64 * j;
+              ++n;
             }
-          } else if ((fcand >> j) & 1u) {
+          }
+        }
+        double kv[4][D / 64];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e)
+            kv[i][e] = i < n ? a.kmean[(tb + cidx[i]) * D + lane + 64 * e] : 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < n) {
+            double part = 0.0;
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) part = fma(qv[e], kv[i][e], part);
+            part = wave_sum_d(part);
+            const int b = cidx[i];
+#pragma unroll
+            for (int j = 0; j < MJ; ++j)
+              if (lane + 64 * j == b) key64[j] = order_key(part);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+          if (j < nj && ((fcand >> j) & 1u)) {
             const double2* krow = reinterpret_cast<const double2*>(a.kmean + (tb + lane + 64 * j) * D);
             const double2* qr2 = reinterpret_cast<const double2*>(qrow);
             double acc = 0.0;
@@ -497,18 +614,22 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
     }
     if (a.force_diag && lane == (at & 63)) sel |= 1u << (at >> 6);
 
-    // emit ascending
+    // emit ascending: the kept columns are gathered in LDS, then stored contiguously
     int base_pos = 0;
-    const size_t obase = a.direct ? (size_t)row * a.topk : (size_t)row * (a.topk + 1);
+    int* oslot = reinterpret_cast<int*>(slot);
+    wave_lds_order();
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
       if (j < nj) {
         const bool s = (sel >> j) & 1u;
         const uint64_t bs = __ballot(s);
-        if (s) a.out_cols[obase + base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
+        if (s) oslot[base_pos + __popcll(bs & lt_mask)] = lane + 64 * j;
         base_pos += __popcll(bs);
       }
     }
+    // the list stays in LDS: the wave stores its rows' lists after its last
+    // row, so that no load of the loop waits behind these stores
+    kept[(r - w) >> 2] = base_pos;
     if (lane == 0) {
       if (a.direct) {
         a.row_ptr[row] = row * a.topk;
@@ -516,6 +637,17 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
       } else {
         a.out_cnt[row] = base_pos;
       }
+    }
+  }
+  wave_lds_order();
+#pragma unroll
+  for (int q = 0; q < kSelRows / 4; ++q) {
+    const int r = w + 4 * q;
+    if (r < nr) {
+      const int row = (int)(tb + a0 + r);
+      const size_t obase = a.direct ? (size_t)row * a.topk : (size_t)row * (a.topk + 1);
+      const int* oslot = reinterpret_cast<const int*>(&sc[r * TP]);
+      for (int i = lane; i < kept[q]; i += 64) a.out_cols[obase + i] = oslot[i];
     }
   }
 }

@@ -187,7 +187,9 @@ int hsa_block_select(const hsa_attn_desc* desc, const void* q, const void* k,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Block-sparse softmax branch on a given CSR: for each query tile, flash
+ * Block-sparse softmax branch on a given CSR (SparkDiffusion news article,
+ * section 05: exact softmax attention on the kept high-energy tiles; section
+ * 01: 3% of the 64x64 tiles kept at 97% sparsity): for each query tile, flash
  * attention over the kept key tiles with float32 softmax statistics.  With
  * FP8 inputs the workspace holds V transposed per tile (B*H*N_pad*d bytes);
  * the other dtypes need none.
@@ -202,7 +204,9 @@ int hsa_sparse_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Rotary low-rank linear branch alone, already multiplied by W_o:
+ * Rotary low-rank linear branch alone (SparkDiffusion news article, section
+ * 05: a low-rank linear-attention branch carrying rotary position information
+ * restores the global context), already multiplied by W_o:
  *   o_lin = O_l W_o, [B, H, N_pad, d] in out_dtype (rows >= N zero).
  * The key/value state is reduced in a fixed order (bitwise reproducible).
  */
@@ -212,7 +216,9 @@ int hsa_linear_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     void* o_lin, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The linear branch over the complement of a given mask, alone, already
+ * The linear branch over the complement of a given mask (SparkDiffusion news
+ * article, section 05: the linear branch restores what the sparsification
+ * discards; SLA in the 2026-05-02 survey post, item 1), alone, already
  * multiplied by W_o: for the queries of tile a, the sums of S and z run over
  * the valid keys outside the tiles of CSR row a (entries outside [0, T) and
  * repeats name no extra tile; a row naming every tile gives O_l = 0).  The
@@ -227,7 +233,9 @@ int hsa_linear_attn_complement(const hsa_attn_desc* desc, const void* q, const v
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The whole hybrid: O = O_s + O_l W_o.
+ * The whole hybrid (SparkDiffusion news article, section 05: the block-sparse
+ * softmax branch and the rotary low-rank linear branch, summed; section 01:
+ * the top-k tile budget per row): O = O_s + O_l W_o, selection included.
  *   With linear_keys = HSA_ATTN_LINEAR_COMPLEMENT, O_l of the queries of tile
  *   a sums over the valid keys outside the tiles of CSR row a (entries
  *   outside [0, T) and repeats name no extra tile); the workspace then also
@@ -249,7 +257,10 @@ int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass of the hybrid (all-keys linear branch) on the forward's mask:
+ * Backward pass of the hybrid (all-keys linear branch) on the forward's mask
+ * (the pages adapt the dense model to the sparse RoLA structure with a short
+ * sparse warm-up, which trains through the operator: SparkDiffusion news
+ * article, section 05; project blog, "A simple staging principle", item 1):
  * the gradients of L with respect to Q, K and V given dL/dO = d_o, with the
  * tile selection held fixed (it is piecewise constant in the inputs).  The
  * forward's linear state and the sparse branch's output and log-sum-exp are

@@ -112,21 +112,39 @@ def split_csr(row_ptr, col_idx, n_heads, T):
 
 
 class RelL2:
-    """Accumulates ||gpu - ref||^2 and ||ref||^2 over valid rows (fp64)."""
+    """Accumulates ||gpu - ref||^2 and ||ref||^2 over valid rows (fp64), and,
+    as a diagnostic beside that pooled figure, the relative L2 error of every
+    64-row tile added, so that a defect confined to one tile shows."""
 
     def __init__(self):
         self.num = 0.0
         self.den = 0.0
+        self.n_added = 0
+        self.worst = (0.0, None)  # (tile relative error, (call index, tile))
 
     def add(self, gpu, ref):
         gpu = np.asarray(gpu, np.float64)
         ref = np.asarray(ref, np.float64)
-        self.num += float(np.sum((gpu - ref) ** 2))
-        self.den += float(np.sum(ref ** 2))
+        d2 = (gpu - ref) ** 2
+        r2 = ref ** 2
+        self.num += float(np.sum(d2))
+        self.den += float(np.sum(r2))
+        n = gpu.shape[0]
+        for t0 in range(0, n, 64):
+            rn = float(np.sum(r2[t0:t0 + 64]))
+            if rn > 0:
+                e = (float(np.sum(d2[t0:t0 + 64])) / rn) ** 0.5
+                if e > self.worst[0]:
+                    self.worst = (e, (self.n_added, t0 // 64))
+        self.n_added += 1
 
     @property
     def value(self):
         return (self.num / self.den) ** 0.5 if self.den > 0 else 0.0
+
+    def __str__(self):
+        e, where = self.worst
+        return f"{self.value:.3e} (worst tile {e:.3e} at {where})"
 
 
 def to_device(inp, dev):

@@ -69,7 +69,7 @@ def test_backward_on_oracle_mask(name):
             errs["linear"][t].add((full[t] - sparse[t])[b, h, :w.N], ref_l[t][:w.N])
             assert np.all(full[t][b, h, w.N:] == 0)
     for key, e in errs.items():
-        print(f"  {key}: dQ {e[0].value:.2e}  dK {e[1].value:.2e}  dV {e[2].value:.2e}", flush=True)
+        print(f"  {key}: dQ {e[0]}  dK {e[1]}  dV {e[2]}", flush=True)
     for key, e in errs.items():
         for t in range(3):
             assert e[t].value <= TOL[w.dtype], (key, t, e[t].value)
@@ -151,7 +151,7 @@ def test_backward_full_size_sampled():
             errs[2].add(dv[0, h, lo:hi].cpu().numpy(), (ref_v + ref_l[2])[lo:hi])
         for t in (dq, dk, dv):
             assert torch.all(t[0, h, w.N:] == 0)
-    print(f"  sampled rel L2: dQ {errs[0].value:.2e}  dK {errs[1].value:.2e}  dV {errs[2].value:.2e}", flush=True)
+    print(f"  sampled rel L2: dQ {errs[0]}  dK {errs[1]}  dV {errs[2]}", flush=True)
     for e in errs:
         assert e.value <= TOL["bf16"]
 
@@ -190,6 +190,6 @@ def test_backward_edge_rows(name):
                                 to_fp64(g[b, h]))
         for t in range(3):
             errs[t].add(grads[t][b, h, :w.N], ref[t][:w.N])
-    print(f"  dQ {errs[0].value:.2e}  dK {errs[1].value:.2e}  dV {errs[2].value:.2e}", flush=True)
+    print(f"  dQ {errs[0]}  dK {errs[1]}  dV {errs[2]}", flush=True)
     for e in errs:
         assert e.value <= TOL[w.dtype]

@@ -73,7 +73,7 @@ def test_complement_on_oracle_mask(name):
         err_o.add(on[b, h, :w.N], ref[(b, h)]["o"][:w.N])
         err_l.add(oln[b, h, :w.N], ref[(b, h)]["o_lw"][:w.N])
         assert np.all(on[b, h, w.N:] == 0) and np.all(oln[b, h, w.N:] == 0)
-    print(f"  O rel L2 {err_o.value:.3e}, O_lW rel L2 {err_l.value:.3e}", flush=True)
+    print(f"  O rel L2 {err_o}, O_lW rel L2 {err_l}", flush=True)
     assert err_o.value <= Hp.TOL[w.dtype]
     assert err_l.value <= Hp.TOL[w.dtype]
 
@@ -130,7 +130,7 @@ def test_complement_edge_rows(name):
                                R.token_positions(w.grid, w.N), w.rope_base) @ Hp.params(inp, h)[2]
         e0 = np.linalg.norm(oln[b, h, :64] - full[:64]) / np.linalg.norm(full[:64])
         assert e0 <= Hp.TOL[w.dtype]
-    print(f"  O rel L2 {err_o.value:.3e}, O_lW rel L2 {err_l.value:.3e}", flush=True)
+    print(f"  O rel L2 {err_o}, O_lW rel L2 {err_l}", flush=True)
     assert err_o.value <= Hp.TOL[w.dtype]
     assert err_l.value <= Hp.TOL[w.dtype]
 

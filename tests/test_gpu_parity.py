@@ -74,7 +74,7 @@ def test_sparse_branch_on_oracle_mask(case):
             m = s.max(axis=1)
             ref_lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
             lerr = max(lerr, float(np.max(np.abs(lse[b, h, lo:hi] - ref_lse))))
-    print(f"  O_s rel L2 {err.value:.3e}, max |lse err| {lerr:.2e}", flush=True)
+    print(f"  O_s rel L2 {err}, max |lse err| {lerr:.2e}", flush=True)
     assert err.value <= Hp.TOL[w.dtype]
     assert lerr <= (1e-4 if w.dtype == "f32" else 2e-2)
 
@@ -90,7 +90,7 @@ def test_linear_branch(case):
     for b, h in heads:
         err.add(o[b, h, :w.N], ref[(b, h)]["o_lw"][:w.N])
         assert np.all(o[b, h, w.N:] == 0)
-    print(f"  O_lW rel L2 {err.value:.3e}", flush=True)
+    print(f"  O_lW rel L2 {err}", flush=True)
     assert err.value <= Hp.TOL[w.dtype]
 
 
@@ -111,7 +111,7 @@ def test_hybrid_on_oracle_mask_and_with_own_selection(case):
     for b, h in heads:
         err.add(o1n[b, h, :w.N], ref[(b, h)]["o"][:w.N])
         assert np.all(o1n[b, h, w.N:] == 0)
-    print(f"  O rel L2 {err.value:.3e}", flush=True)
+    print(f"  O rel L2 {err}", flush=True)
     assert err.value <= Hp.TOL[w.dtype]
     # the mask selected inside the hybrid call is the block-select mask
     rpb, cib = B.block_select(cfg, d["q"], d["k"], d["q_scale"], d["k_scale"])
@@ -190,7 +190,7 @@ def test_mask_reused_on_the_next_step(name):
         err.add(o[b, h, :w.N], ref["o"][:w.N])
         fresh = Hp.oracle_mask_head(inp2, b, h)[1]
         changed += sum(not np.array_equal(x, y) for x, y in zip(fresh, rows1[i]))
-    print(f"  O rel L2 {err.value:.3e}; rows whose fresh selection differs: {changed} of {len(heads) * w.T}",
+    print(f"  O rel L2 {err}; rows whose fresh selection differs: {changed} of {len(heads) * w.T}",
           flush=True)
     assert err.value <= Hp.TOL[w.dtype]
 

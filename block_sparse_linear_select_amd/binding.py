@@ -24,7 +24,7 @@ ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
-            "hsa_hybrid_attn", "hsa_hybrid_attn_backward",
+            "hsa_hybrid_attn", "hsa_hybrid_attn_noalloc", "hsa_hybrid_attn_backward",
             "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
 KERNEL_KINDS = ["rope", "stream", "finalize", "select", "unused4", "attend", "quant", "proj", "compl", "bwd_linear",
                 "bwd_sparse"]
@@ -70,6 +70,8 @@ def lib():
                                                sz, vp]
         L.hsa_hybrid_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                       vp, vp, sz, vp]
+        L.hsa_hybrid_attn_noalloc.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
+                                              vp, vp]
         L.hsa_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, f32p, vp]
         i32 = ctypes.c_int32
         L.hsa_qkv_proj_fp8.argtypes = [vp, f32p, vp, f32p, i32, i32, i32, i32, i32, vp, vp, vp, f32p, f32p, f32p, vp]
@@ -288,6 +290,26 @@ def hybrid_attn(cfg: Config, q, k, v, uq, uk, wo, q_scale=None, k_scale=None, v_
     if export_mask and row_ptr is None:
         return o, plan.row_ptr, plan.col_idx
     return o
+
+
+def hybrid_attn_noalloc(cfg: Config, q, k, v, uq, uk, wo, q_scale=None, k_scale=None, v_scale=None,
+                        row_ptr=None, col_idx=None, export_mask=False):
+    """hybrid_attn through the entry point that allocates nothing: its
+    scratch is the library's static device array (calls that overlap on one
+    GPU race on it).  With export_mask, returns (o, row_ptr, col_idx)."""
+    _check_inputs(cfg, q, k, v, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_params(cfg, uq, uk, wo)
+    rows = cfg.B * cfg.H * cfg.T
+    o = torch.empty((cfg.B, cfg.H, cfg.N_pad, cfg.d), dtype=_out_dtype(cfg), device=q.device)
+    rp_out = ci_out = None
+    if export_mask and row_ptr is None:
+        rp_out = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+        ci_out = torch.empty(rows * cfg.kmax, dtype=torch.int32, device=q.device)
+    d = cfg.desc()
+    _check(lib().hsa_hybrid_attn_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(uq), _ptr(uk), _ptr(wo), _ptr(row_ptr), _ptr(col_idx),
+                                         _ptr(rp_out), _ptr(ci_out), _ptr(o), _stream()))
+    return (o, rp_out, ci_out) if rp_out is not None else o
 
 
 def hybrid_attn_backward(cfg: Config, q, k, v, uq, uk, wo, row_ptr, col_idx, d_o):

@@ -448,12 +448,14 @@ HSA_API int hsa_linear_attn_complement(const hsa_attn_desc* desc, const void* q,
   return HSA_ATTN_OK;
 }
 
-HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
-                            const float* q_scale, const float* k_scale, const float* v_scale,
-                            const void* U_q, const void* U_k, const void* W_o,
-                            const int32_t* row_ptr_in, const int32_t* col_idx_in,
-                            int32_t* row_ptr_out, int32_t* col_idx_out,
-                            void* o, void* workspace, size_t workspace_bytes, void* stream) {
+// The hybrid call with its workspace either given by the caller or, for the
+// allocation-free entry point (noalloc), the library's static scratch.
+static int hybrid_impl(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                       const float* q_scale, const float* k_scale, const float* v_scale,
+                       const void* U_q, const void* U_k, const void* W_o,
+                       const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                       int32_t* row_ptr_out, int32_t* col_idx_out,
+                       void* o, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   Shape s;
   const bool given = row_ptr_in || col_idx_in;
   if (given && !(row_ptr_in && col_idx_in)) return fail(HSA_ATTN_ERR_CSR, "row_ptr_in and col_idx_in go together");
@@ -468,6 +470,14 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
   if (s.dt == Dt::FP8 && s.d != 128) return fail(HSA_ATTN_ERR_SHAPE, "FP8 attention needs head dim 128 (d=%d)", s.d);
   const bool internal = !given && !row_ptr_out;
   Plan p = make_plan(s, !given, internal, true, true);
+  if (noalloc) {
+    if (p.total > kStaticScratchBytes)
+      return fail(HSA_ATTN_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                  p.total, kStaticScratchBytes);
+    hipError_t e = static_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    workspace_bytes = kStaticScratchBytes;
+  }
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   Scratch w = bind_plan(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -495,6 +505,27 @@ HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void
     if (e != hipSuccess) return hip_fail(e, "complement linear branch");
   }
   return HSA_ATTN_OK;
+}
+
+HSA_API int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const void* U_q, const void* U_k, const void* W_o,
+                            const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                            int32_t* row_ptr_out, int32_t* col_idx_out,
+                            void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  return hybrid_impl(desc, q, k, v, q_scale, k_scale, v_scale, U_q, U_k, W_o, row_ptr_in, col_idx_in, row_ptr_out,
+                     col_idx_out, o, workspace, workspace_bytes, stream, false);
+}
+
+static_assert(kStaticScratchBytes == HSA_ATTN_STATIC_SCRATCH_BYTES, "static scratch size");
+
+HSA_API int hsa_hybrid_attn_noalloc(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* q_scale, const float* k_scale, const float* v_scale,
+                                    const void* U_q, const void* U_k, const void* W_o,
+                                    const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                                    int32_t* row_ptr_out, int32_t* col_idx_out, void* o, void* stream) {
+  return hybrid_impl(desc, q, k, v, q_scale, k_scale, v_scale, U_q, U_k, W_o, row_ptr_in, col_idx_in, row_ptr_out,
+                     col_idx_out, o, nullptr, 0, stream, true);
 }
 
 // ---------------------------------------------------------------- W8A8 projections

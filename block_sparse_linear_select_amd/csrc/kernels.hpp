@@ -100,6 +100,11 @@ struct Plan {
 };
 
 Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool vt, bool backward = false);
+
+// Size of the static scratch behind hsa_hybrid_attn_noalloc, and its device
+// address on the current device (taken on the first call there).
+constexpr size_t kStaticScratchBytes = (size_t)256 << 20;  // HSA_ATTN_STATIC_SCRATCH_BYTES
+hipError_t static_scratch(void** out);
 Scratch bind_plan(const Plan& p, void* ws);
 
 // Launchers: each enqueues its kernels on `st` and returns hipSuccess or the

@@ -257,6 +257,28 @@ int hsa_hybrid_attn(const hsa_attn_desc* desc, const void* q, const void* k, con
                     void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hsa_hybrid_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same call and result, with the scratch taken from a static device array
+ * of HSA_ATTN_STATIC_SCRATCH_BYTES (256 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  A call whose workspace would exceed
+ * it returns HSA_ATTN_ERR_WORKSPACE before anything is enqueued (the
+ * workspace size of HSA_ATTN_CALL_HYBRID says how much a call needs; the
+ * 720P bf16 call needs ~140 MiB, FP8 at 720P ~510 MiB and is rejected).
+ * Every call on one GPU shares that array, so calls that overlap in time on
+ * one GPU (different streams, or threads) race and must be serialised by the
+ * caller; nothing in the array needs to start at zero.  The first call on a
+ * device takes the array's address there (hipGetSymbolAddress); no call
+ * allocates.
+ */
+#define HSA_ATTN_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int hsa_hybrid_attn_noalloc(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            const void* U_q, const void* U_k, const void* W_o,
+                            const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                            int32_t* row_ptr_out, int32_t* col_idx_out, void* o, void* stream);
+
+/*
  * Backward pass of the hybrid (all-keys linear branch) on the forward's mask
  * (the pages adapt the dense model to the sparse RoLA structure with a short
  * sparse warm-up, which trains through the operator: SparkDiffusion news

@@ -151,3 +151,19 @@ def test_slices_beyond_32_bit_offsets_are_rejected():
         assert rc == -2 and b"2^31" in B.lib().hsa_attn_last_error(), call
     rc, _ = _ws(_cfg(grid=(1023, 64, 64), N=1023 * 64 * 64, N_pad=1023 * 64 * 64, topk=3), B.CALL_LINEAR)
     assert rc == 0
+
+
+def test_noalloc_rejects_a_call_beyond_its_static_scratch_before_any_launch():
+    """The allocation-free hybrid call checks its workspace need against the
+    static scratch before it touches the GPU: 720P FP8 (~0.5 GB with the
+    transposed V tiles) is rejected, with nothing enqueued."""
+    from workloads import make_workload
+    cfg = B.Config.from_workload(make_workload("wan14b_720p_fp8"))
+    d = cfg.desc()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced
+    rc = B.lib().hsa_hybrid_attn_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                         None, None, None, None, fake, None)
+    assert rc == -4 and b"static scratch" in B.lib().hsa_attn_last_error()
+    n = ctypes.c_size_t(0)
+    assert B.lib().hsa_attn_workspace_size(ctypes.byref(d), B.CALL_HYBRID, ctypes.byref(n)) == 0
+    assert n.value > (256 << 20)

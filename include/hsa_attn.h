@@ -293,8 +293,10 @@ int hsa_hybrid_attn_noalloc(const hsa_attn_desc* desc, const void* q, const void
  * O_l = num / den (see hsa_linear_attn), S and z.
  *   q, k, v: [B, H, N_pad, d] float32 or bf16 (HSA_ATTN_ERR_DTYPE for FP8);
  *   U_q, U_k, W_o as for the forward; row_ptr / col_idx: the forward's CSR
- *   (entries outside [0, T) are skipped; rows with repeated entries are
- *   outside this call's domain); d_o: [B, H, N_pad, d] in the input type
+ *   (entries outside [0, T) are skipped; rows with repeated entries, or with
+ *   more than topk + force_diag entries in [0, T), are outside this call's
+ *   domain: the transposed mask it builds holds B*H*T*(topk + force_diag)
+ *   entries, so set topk to the longest row of a mask not made by selection); d_o: [B, H, N_pad, d] in the input type
  *   (rows >= N are ignored).
  *   d_q, d_k, d_v: float32 [B, H, N_pad, d], written in full (rows >= N zero).
  *   desc->linear_keys must be HSA_ATTN_LINEAR_ALL_KEYS (HSA_ATTN_ERR_SHAPE

@@ -161,12 +161,14 @@ def test_backward_edge_rows(name):
     """A row keeping no tile (its sparse gradients vanish), a row keeping every
     tile, rows with entries outside [0, T) (skipped, as the forward skips
     them), on the GPU against the oracle given the same mask without them.
-    The full row holds more entries than the descriptor's topk."""
+    The descriptor's topk is the longest row (T), which sizes the transposed
+    mask."""
+    import dataclasses
     w = Hp.CASES[name]
     inp = Hp.gen(w)
     d = Hp.to_device(inp, DEV)
-    cfg = B.Config.from_workload(w)
     T = w.T
+    cfg = dataclasses.replace(B.Config.from_workload(w), topk=T)
     rng = np.random.default_rng(9)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     clean, dirty = {}, {}

@@ -525,11 +525,16 @@ static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& 
 // LDS-direct loads into XOR-swizzled unpadded tiles, the next K pair loading
 // during the PV step and the next V pair during the score step.
 // ---------------------------------------------------------------------------
-// Swizzles of the fp8 tiles: K rows of 128 bytes (two rows per 256-byte bank
-// set), V^T rows of 64 bytes (four rows per bank set); the 16 rows of one
-// 16-byte fragment read land on distinct banks.
-__device__ __forceinline__ int swz_k8(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_v8(int row) { return (row >> 2) & 3; }
+// Swizzles of the fp8 tiles.  A 16-byte LDS read is served eight lanes at a
+// time from 128 bytes of banks (the bf16 layout, free of conflicts under that
+// rule, reads none; the counters read ~1 conflict cycle per access cycle for
+// a layout that was only free of them per 16 lanes over 256 bytes).  Lanes
+// 8i .. 8i + 7 of a fragment read take 8 consecutive rows: K rows are 128
+// bytes, so the 8 rows get 8 distinct granule positions; V^T rows are 64
+// bytes (two rows per 128 bytes), so the 4 row pairs get 4 distinct granule
+// positions within their half.
+__device__ __forceinline__ int swz_k8(int row) { return row & 7; }
+__device__ __forceinline__ int swz_v8(int row) { return (row >> 1) & 3; }
 
 template <int R, bool SPARSE, bool LINEAR>
 __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {

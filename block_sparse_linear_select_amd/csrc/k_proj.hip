@@ -80,10 +80,11 @@ constexpr int kPXL = kPM * kPK / 1024 / kPWaves;  // LDS-direct loads per wave p
 constexpr int kPWL = kPN * kPK / 1024 / kPWaves;  // ... and weights
 constexpr int kPLoads = kPXL + kPWL;
 
-// Tile rows are 128 bytes (8 granules); two rows share a 256-byte bank set.
-// Granule p of row r sits at position p ^ ((r >> 1) & 7), so the 16 rows of
-// one fragment read (two granules per lane group) hit distinct banks.
-__device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
+// Tile rows are 128 bytes (8 granules).  A 16-byte LDS read is served eight
+// lanes at a time from 128 bytes of banks, and lanes 8i .. 8i + 7 of a
+// fragment read take 8 consecutive rows: granule p of row r sits at position
+// p ^ (r & 7), so those 8 rows hit 8 distinct granule positions.
+__device__ __forceinline__ int swz_p(int row) { return row & 7; }
 
 // Block: 8 waves; wave (wr, wc) computes tokens 128 wr .. +127 x columns
 // 64 wc .. +63 as 4 x 8 steps of 16 columns x 16 tokens: A = W rows (columns
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
   const i32x4_t xrs = make_rsrc_regs(a.x + (size_t)m0 * a.C, (int)mrows * a.C);
   // LDS-direct load i of a tile fills bytes [1024 i, +1024): rows 8 i + lane / 8,
   // slot lane % 8; the slot holds granule slot ^ swz(row).  The lane part of
-  // the source offset depends on i only through i & 1.
+  // the source offset depends on i only through i & 1 (with rows 8 i + lane / 8
+  // and this swizzle, not at all).
   int lp[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {

@@ -525,15 +525,14 @@ static inline hipError_t attend_bf16_by_shape(const Shape& s, const AttendArgs& 
 // LDS-direct loads into XOR-swizzled unpadded tiles, the next K pair loading
 // during the PV step and the next V pair during the score step.
 // ---------------------------------------------------------------------------
-// Swizzles of the fp8 tiles.  A 16-byte LDS read is served eight lanes at a
-// time from 128 bytes of banks (the bf16 layout, free of conflicts under that
-// rule, reads none; the counters read ~1 conflict cycle per access cycle for
-// a layout that was only free of them per 16 lanes over 256 bytes).  Lanes
-// 8i .. 8i + 7 of a fragment read take 8 consecutive rows: K rows are 128
-// bytes, so the 8 rows get 8 distinct granule positions; V^T rows are 64
-// bytes (two rows per 128 bytes), so the 4 row pairs get 4 distinct granule
-// positions within their half.
-__device__ __forceinline__ int swz_k8(int row) { return row & 7; }
+// Swizzles of the fp8 tiles (K rows of 128 bytes, V^T rows of 64 bytes):
+// granule p of row r sits at position p ^ f(r).  The rule by which gfx950
+// serves the lanes of a 16-byte LDS read was measured, not assumed: with the
+// LDS bank-conflict counter, a probe over every XOR swizzle of the K rows
+// linear in the row bits reads 0 conflict cycles for the one below and 4 per
+// read instruction for f(r) = r & 7 or (r >> 1) & 7; for the V^T rows,
+// (r >> 1) & 3 reads 0 and (r >> 2) & 3 reads 4.
+__device__ __forceinline__ int swz_k8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 __device__ __forceinline__ int swz_v8(int row) { return (row >> 1) & 3; }
 
 template <int R, bool SPARSE, bool LINEAR>

@@ -80,11 +80,12 @@ constexpr int kPXL = kPM * kPK / 1024 / kPWaves;  // LDS-direct loads per wave p
 constexpr int kPWL = kPN * kPK / 1024 / kPWaves;  // ... and weights
 constexpr int kPLoads = kPXL + kPWL;
 
-// Tile rows are 128 bytes (8 granules).  A 16-byte LDS read is served eight
-// lanes at a time from 128 bytes of banks, and lanes 8i .. 8i + 7 of a
-// fragment read take 8 consecutive rows: granule p of row r sits at position
-// p ^ (r & 7), so those 8 rows hit 8 distinct granule positions.
-__device__ __forceinline__ int swz_p(int row) { return row & 7; }
+// Tile rows are 128 bytes (8 granules); granule p of row r sits at position
+// p ^ f(r), f(r) = 2 (r mod 4) + bit 2 of r.  On gfx950 this swizzle reads
+// with no LDS bank conflicts (measured by the bank-conflict counter over
+// every XOR swizzle linear in the row bits; r & 7 and (r >> 1) & 7 cost 4
+// conflict cycles per 16-byte read instruction).
+__device__ __forceinline__ int swz_p(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 // Block: 8 waves; wave (wr, wc) computes tokens 128 wr .. +127 x columns
 // 64 wc .. +63 as 4 x 8 steps of 16 columns x 16 tokens: A = W rows (columns
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_proj_fp8(ProjArgs a) {
   // LDS-direct load i of a tile fills bytes [1024 i, +1024): rows 8 i + lane / 8,
   // slot lane % 8; the slot holds granule slot ^ swz(row).  The lane part of
   // the source offset depends on i only through i & 1 (with rows 8 i + lane / 8
-  // and this swizzle, not at all).
+  // and a swizzle of r mod 8, not at all).
   int lp[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {

@@ -204,10 +204,10 @@ __device__ __forceinline__ float group4_sum(float x) {
   return x + wave_xor(x, 32);
 }
 
-// elu(x) + 1, without a branch: the exponential of min(x, 0) is always
-// formed (one transcendental op) and selected for x <= 0.
+// elu(x) + 1, without a branch: the exponential of x is always formed (one
+// transcendental op) and selected for x <= 0.
 __device__ __forceinline__ float elu1(float x) {
-  const float e = __expf(fminf(x, 0.f));
+  const float e = __expf(x);  // taken only for x <= 0 (for large x it overflows and is not selected)
   return x > 0.f ? x + 1.f : e;
 }
 

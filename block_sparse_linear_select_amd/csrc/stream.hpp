@@ -54,12 +54,6 @@ __device__ __forceinline__ RopeSlot rope_slot(int jp, int rank, int gt, int gh) 
   return s;
 }
 
-__device__ __forceinline__ int pack_pos(int tok, int gh, int gw) {
-  int hw = gh * gw;
-  int t = tok / hw, rem = tok - t * hw;
-  int h = rem / gw, w = rem - h * gw;
-  return (t << 20) | (h << 10) | w;
-}
 typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
 
 // Value of the neighbouring lane in the pair (2m, 2m + 1): a DPP quad
@@ -202,7 +196,9 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   __shared__ __align__(16) OT Vr[(STATE && VROW) ? 64 * VRS : 1];
   __shared__ __align__(16) uint8_t Vt8[(STATE && sizeof(T) == 1) ? D * 80 : 16];  // fp8 V^T tile for the sparse kernel
   __shared__ double redk[POOL ? NCONT * D : 1];
-  __shared__ int spos[64];
+  // per token of the current tile: the RoPE table row of its position on each
+  // axis (the axis's offset in the table + position x pairs of the axis)
+  __shared__ __align__(16) int sofs[3][64];
   __shared__ float2 rtab[RLDS ? kRopeLdsMax : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -224,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   const int r = 16 * rb + l16;
   Frag<OT> uf[D / 32];
   RopeSlot rs;
-  int psh = 0, pmask = 0;
+  const int* sax = nullptr;  // this lane's axis row of sofs, from token 4 g
   float zacc = 0.f;
   f32x4 accS[DBW];
   if constexpr (STATE) {
@@ -245,8 +241,7 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
     if constexpr (RLDS) {
       for (int i = tid; i < a.nrope; i += 256) rtab[i] = a.rope[i];  // published by the loop's first barrier
     }
-    psh = rs.axis == 0 ? 20 : (rs.axis == 1 ? 10 : 0);  // field of the packed position on this axis
-    pmask = rs.axis == 0 ? 0xFFF : 1023;
+    sax = &sofs[rs.axis][4 * g];
 #pragma unroll
     for (int j = 0; j < DBW; ++j) accS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -318,7 +313,15 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           for (int e = 0; e < 8; ++e)
             st4(&Vt[(c8 * 8 + e) * VSTR + p0], elem(c.v[0], e), elem(c.v[1], e), elem(c.v[2], e), elem(c.v[3], e));
         }
-        if (tid < 64) spos[tid] = pack_pos(min(t * 64 + tid, a.N - 1), a.gh, a.gw);
+        if (tid < 64) {
+          const int tok = min(t * 64 + tid, a.N - 1), hw = a.gh * a.gw;
+          const int pt = tok / hw, rem = tok - pt * hw;
+          const int ph = rem / a.gw, pw = rem - ph * a.gw;
+          constexpr int PT = 3 * R / 16, PH = 3 * R / 16, PW = R / 8;  // RoPE pairs per axis
+          sofs[0][tid] = pt * PT;
+          sofs[1][tid] = a.gt * PT + ph * PH;
+          sofs[2][tid] = a.gt * PT + a.gh * PH + pw * PW;
+        }
         if constexpr (sizeof(T) == 1) {
           if (a.vt && tid < NVU) stage_vt8(Vt8, tid, c.v);
         }
@@ -347,19 +350,31 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
         }
         float kp[4][4];
         float ztile = 0.f;  // this lane's share of the tile's feature sum
+        float phi[4][4];
+  #pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) phi[tb][i] = elu1(accF[tb][i] * sk);
+        if (__builtin_expect(t * 64 + 64 > a.N, 0)) {  // ragged last tile: tokens past N add nothing
+  #pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t * 64 + 16 * tb + 4 * g + i >= a.N) phi[tb][i] = 0.f;
+        }
   #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
+          // table rows of this lane's four tokens 16 tb + 4 g + i on its axis
+          const int4 ro = *reinterpret_cast<const int4*>(sax + 16 * tb);
+          const int rows[4] = {ro.x, ro.y, ro.z, ro.w};
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * tb + 4 * g + i;
-            const float e1 = elu1(accF[tb][i] * sk);
-            const float phi = (t * 64 + tok < a.N) ? e1 : 0.f;
-            if constexpr (TILES) ztile += phi;
-            else zacc += phi;
-            const float other = quad_swap1(phi);  // the feature paired with this lane's by RoPE
-            const int pa = (spos[tok] >> psh) & pmask;
-            const float2 cs = RLDS ? rtab[rs.off + pa * rs.half + rs.m] : a.rope[rs.off + pa * rs.half + rs.m];
-            float rot = (r & 1) ? (other * cs.y + phi * cs.x) : (phi * cs.x - other * cs.y);
+            const float f = phi[tb][i];
+            if constexpr (TILES) ztile += f;
+            else zacc += f;
+            const float other = quad_swap1(f);  // the feature paired with this lane's by RoPE
+            const float2 cs = RLDS ? rtab[rows[i] + rs.m] : a.rope[rows[i] + rs.m];
+            float rot = (r & 1) ? (other * cs.y + f * cs.x) : (f * cs.x - other * cs.y);
             kp[tb][i] = rot * sv;
           }
         }

@@ -25,9 +25,6 @@ __device__ __forceinline__ uint32_t order_key32(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u >> 31) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key32_value(uint32_t k) {
-  return __uint_as_float((k >> 31) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 constexpr int kMaxJ = 32;  // up to 64 * 32 = 2048 tiles per row (keys per lane: MJ <= kMaxJ)
 
@@ -109,30 +106,6 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return ((readlane_d(x, 0) + readlane_d(x, 16)) + readlane_d(x, 32)) + readlane_d(x, 48);
 }
 
-// The k-th largest of the values of the lanes in `live` (1 <= k <= their
-// number, counting repeats): the value v with #{x > v} < k <= #{x >= v},
-// fixed one key bit at a time from the top by ballots (order-preserving
-// keys).  Wave-uniform; no cross-lane data movement besides the ballots.
-__device__ __forceinline__ float kth_largest_lane(float x, bool live, int k) {
-  const uint32_t key = order_key32(x);
-  uint64_t cand = __ballot(live);
-  uint32_t prefix = 0;
-  int need = k;
-#pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint64_t ones = __ballot((key >> bit) & 1u) & cand;
-    const int c1 = __popcll(ones);
-    if (c1 >= need) {
-      prefix |= 1u << bit;
-      cand = ones;
-    } else {
-      need -= c1;
-      cand &= ~ones;
-    }
-  }
-  return key32_value(prefix);
-}
-
 __device__ __forceinline__ int wave_sum_int(int x) {
   x += dpp<kQuadXor1>(x);
   x += dpp<kQuadXor2>(x);
@@ -142,30 +115,29 @@ __device__ __forceinline__ int wave_sum_int(int x) {
          (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
 }
 
-// The same k-th largest by ranking on the vector units: the 64 values go to
+// The k-th largest of the values of the lanes in `live` (1 <= k <= their
+// number, counting repeats), by ranking on the vector units: the 64 values go to
 // a wave-private LDS buffer, every lane reads them all back (broadcast reads,
-// 16 at a time) and counts those above and not below its own, so the wave's
-// scalar unit (shared by the CU's waves) stays free.
+// 16 at a time) and counts those strictly above its own.  A value with fewer
+// than k values above it is at least the k-th largest, and the k-th largest
+// itself has fewer than k above it (ties included), so the k-th largest is the
+// smallest such value: a wave minimum on lane moves, with the scalar unit
+// (shared by the CU's waves) left free.
 __device__ __forceinline__ float kth_largest_vec(float x, bool live, int k, int lane, float* buf) {
   const float xv = live ? x : -INFINITY;
   buf[lane] = xv;
   wave_lds_order();
-  int gt = 0, ge = 0;
+  int gt = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     float4 o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = reinterpret_cast<const float4*>(buf)[4 * b + i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gt += (o[i].x > xv) + (o[i].y > xv) + (o[i].z > xv) + (o[i].w > xv);
-      ge += (o[i].x >= xv) + (o[i].y >= xv) + (o[i].z >= xv) + (o[i].w >= xv);
-    }
+    for (int i = 0; i < 4; ++i) gt += (o[i].x > xv) + (o[i].y > xv) + (o[i].z > xv) + (o[i].w > xv);
   }
   wave_lds_order();  // read before the buffer is written again
-  const uint64_t bl = __ballot(live && gt < k && ge >= k);
-  const int src = __ffsll((unsigned long long)bl) - 1;
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), src));
+  return wave_min_f(live && gt < k ? xv : INFINITY);
 }
 
 // Top-k of one row held by one wave: key[j] of lane l belongs to column

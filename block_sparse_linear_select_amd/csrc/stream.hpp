@@ -164,8 +164,8 @@ struct StreamArgs {
 };
 
 // RoPE tables up to this many entries (11.5 KB at 720P, rank 64) are staged
-// in LDS once per block, so the per-token lookups are LDS reads (bf16 inputs;
-// two blocks per CU still fit).
+// in LDS once per block, so the per-token lookups are LDS reads (two blocks
+// per CU still fit: at most ~75 KB each, for fp8 inputs with d = 128).
 constexpr int kRopeLdsMax = 1536;
 
 // TILES: also write every tile's own state and feature sum (the partial
@@ -630,7 +630,7 @@ template <typename T, typename OT, int D, int R>
 static hipError_t stream_dispatch(const Shape& s, const StreamArgs& a, bool pool, bool state, hipStream_t st) {
   dim3 grid(a.nchunk, s.B * s.H);
   // (the fp8 variant's LDS is already full with its two V^T tiles)
-  const bool rlds = a.nrope <= kRopeLdsMax && std::is_same<T, bf16_t>::value;
+  const bool rlds = a.nrope <= kRopeLdsMax;
   if (state && a.tile_s) {  // per-tile states for the complement variant
     if (pool && rlds) k_stream<T, OT, D, R, true, true, true, true><<<grid, 256, 0, st>>>(a);
     else if (pool) k_stream<T, OT, D, R, true, true, false, true><<<grid, 256, 0, st>>>(a);

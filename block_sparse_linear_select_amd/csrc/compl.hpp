@@ -115,6 +115,11 @@ __global__ __launch_bounds__(256, 2) void k_compl(ComplArgs a) {
   static_assert(NCH >= 1 && NFE % (256 * CE) == 0, "state split");
   static_assert(G >= 1 && G <= 8, "rows per block");
   __shared__ __align__(16) uint8_t lds[SFB > LISTB ? SFB : LISTB];
+  // bf16 operands: the head's W_o^T fragments staged once per block (32 KB at
+  // d = 128), read by every row's output step from LDS instead of L2 (float
+  // operands would need twice that and read them from memory)
+  constexpr int NWE = NDB * (D / 32) * 512;
+  __shared__ __align__(16) OT WOs[SPLIT ? NWE : 8];
   __shared__ float ZC[R];
   __shared__ int wcnt[4];
   __shared__ int nkept_sh[G];
@@ -127,6 +132,11 @@ __global__ __launch_bounds__(256, 2) void k_compl(ComplArgs a) {
   const int h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
+  if constexpr (SPLIT) {  // published by the first barrier below
+    const OT* wsrc = reinterpret_cast<const OT*>(a.wo_frag) + (size_t)h * NWE;
+    for (int e = 8 * tid; e < NWE; e += 8 * 256)
+      *reinterpret_cast<u32x4*>(&WOs[e]) = *reinterpret_cast<const u32x4*>(wsrc + e);
+  }
   uint8_t* kept = lds;                                                       // [G][kComplMaxT]
   uint32_t* list = reinterpret_cast<uint32_t*>(lds + G * kComplMaxT);        // tile | row mask << 16
 
@@ -337,7 +347,8 @@ __global__ __launch_bounds__(256, 2) void k_compl(ComplArgs a) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
         Frag<OT> wf;
-        load8(wf, WO + ((size_t)(jo * (D / 32) + c) * 64 + lane) * 8);
+        if constexpr (SPLIT) wf.w = *reinterpret_cast<const u32x4*>(&WOs[((jo * (D / 32) + c) * 64 + lane) * 8]);
+        else load8(wf, WO + ((size_t)(jo * (D / 32) + c) * 64 + lane) * 8);
         mma(acc_w, wf, nh[c]);
         if constexpr (SPLIT) mma(acc_w, wf, nl[c]);
       }

@@ -239,12 +239,21 @@ def bench_backward(w, cfg, d, args, dev):
     ms, per = time_calls(run, steps, max(1, args.warmup // 2), torch.cuda.current_stream())
     kern = kernel_split(run, steps)
     log(f"  {steps} backward calls: {ms:.3f} ms/call (sparse part {kern['bwd_sparse']:.3f} ms)")
-    pairs = w.B * w.H * w.T * w.topk
+    # the same gradients from the training forward's saved O_s and log-sum-exp (no sparse recompute)
+    _, o_s, lse = B.hybrid_attn_train(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], row_ptr=sel.row_ptr,
+                                      col_idx=sel.col_idx)
+    run_saved = lambda: B.hybrid_attn_backward_saved(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"],
+                                                     sel.row_ptr, sel.col_idx, o_s, lse, g)
+    ms_saved, per_saved = time_calls(run_saved, steps, max(1, args.warmup // 2), torch.cuda.current_stream())
+    log(f"  {steps} backward calls on saved statistics: {ms_saved:.3f} ms/call")
+    cols = sel.col_idx[:int(sel.row_ptr[-1].item())]
+    pairs = int(((cols >= 0) & (cols < w.T)).sum().item())
     flops = 5 * 2.0 * 64 * 64 * w.d * pairs
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else 157.3
     ach = flops / (kern["bwd_sparse"] * 1e-3) / 1e12
     return {"ms_per_call": ms, **{"ms_" + k: v for k, v in percentiles(per).items()}, "kernels_ms": kern,
             "steps": steps,
+            "saved_statistics": {"ms_per_call": ms_saved, **{"ms_" + k: v for k, v in percentiles(per_saved).items()}},
             "sparse_roofline": {"bound": "mfma", "kernel": "k_bwd_dq + k_bwd_dv + k_bwd_dk (+ transposed mask)",
                                 "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                                 "flop": flops, "executed_flop": flops * 8 / 5}}

@@ -24,7 +24,8 @@ ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
             "hsa_attn_timing_enable", "hsa_attn_timing_read",
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
-            "hsa_hybrid_attn", "hsa_hybrid_attn_noalloc", "hsa_hybrid_attn_backward",
+            "hsa_hybrid_attn", "hsa_hybrid_attn_noalloc", "hsa_hybrid_attn_train", "hsa_hybrid_attn_backward",
+            "hsa_hybrid_attn_backward_saved",
             "hsa_quantize_rows_fp8", "hsa_qkv_proj_fp8"]
 KERNEL_KINDS = ["rope", "stream", "finalize", "select", "unused4", "attend", "quant", "proj", "compl", "bwd_linear",
                 "bwd_sparse"]
@@ -70,6 +71,10 @@ def lib():
                                                sz, vp]
         L.hsa_hybrid_attn.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                       vp, vp, sz, vp]
+        L.hsa_hybrid_attn_train.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32p, i32p, i32p, i32p, vp, vp, f32p,
+                                            vp, sz, vp]
+        L.hsa_hybrid_attn_backward_saved.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, f32p, vp, f32p,
+                                                     f32p, f32p, vp, sz, vp]
         L.hsa_hybrid_attn_noalloc.argtypes = [dp, vp, vp, vp, f32p, f32p, f32p, vp, vp, vp, i32p, i32p, i32p, i32p,
                                               vp, vp]
         L.hsa_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, f32p, vp]
@@ -329,6 +334,51 @@ def hybrid_attn_backward(cfg: Config, q, k, v, uq, uk, wo, row_ptr, col_idx, d_o
                                           _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv
 
+
+
+def hybrid_attn_train(cfg: Config, q, k, v, uq, uk, wo, row_ptr=None, col_idx=None, export_mask=False):
+    """hybrid_attn that also returns what the backward needs from it: (o, o_s,
+    lse) with o_s the sparse branch's output alone and lse its log-sum-exp
+    [B, H, N_pad] float32; with export_mask, (o, o_s, lse, row_ptr, col_idx)."""
+    _check_inputs(cfg, q, k, v)
+    _check_params(cfg, uq, uk, wo)
+    rows = cfg.B * cfg.H * cfg.T
+    shape = (cfg.B, cfg.H, cfg.N_pad, cfg.d)
+    o = torch.empty(shape, dtype=_out_dtype(cfg), device=q.device)
+    o_s = torch.empty(shape, dtype=_out_dtype(cfg), device=q.device)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N_pad), dtype=torch.float32, device=q.device)
+    rp_out = ci_out = None
+    if export_mask and row_ptr is None:
+        rp_out = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+        ci_out = torch.empty(rows * cfg.kmax, dtype=torch.int32, device=q.device)
+    ws = _workspace(cfg, CALL_HYBRID, q.device)
+    d = cfg.desc()
+    _check(lib().hsa_hybrid_attn_train(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(uq), _ptr(uk), _ptr(wo),
+                                       _ptr(row_ptr), _ptr(col_idx), _ptr(rp_out), _ptr(ci_out), _ptr(o), _ptr(o_s),
+                                       _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return (o, o_s, lse, rp_out, ci_out) if rp_out is not None else (o, o_s, lse)
+
+
+def hybrid_attn_backward_saved(cfg: Config, q, k, v, uq, uk, wo, row_ptr, col_idx, o_s, lse, d_o):
+    """hybrid_attn_backward with the sparse branch's output and log-sum-exp
+    from hybrid_attn_train instead of recomputed."""
+    _check_inputs(cfg, q, k, v)
+    _check_params(cfg, uq, uk, wo)
+    _need(d_o, "d_o", (cfg.B, cfg.H, cfg.N_pad, cfg.d), _TORCH_IN[cfg.dtype])
+    _need(o_s, "o_s", (cfg.B, cfg.H, cfg.N_pad, cfg.d), _out_dtype(cfg))
+    _need(lse, "lse", (cfg.B, cfg.H, cfg.N_pad), torch.float32)
+    _need(row_ptr, "row_ptr", (cfg.B * cfg.H * cfg.T + 1,), torch.int32)
+    if col_idx.dtype != torch.int32 or not col_idx.is_cuda or col_idx.dim() != 1:
+        raise ValueError("col_idx must be a 1-D int32 device tensor")
+    shape = (cfg.B, cfg.H, cfg.N_pad, cfg.d)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    ws = _workspace(cfg, CALL_BACKWARD, q.device)
+    d = cfg.desc()
+    _check(lib().hsa_hybrid_attn_backward_saved(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(uq), _ptr(uk),
+                                                _ptr(wo), _ptr(row_ptr), _ptr(col_idx), _ptr(o_s), _ptr(lse),
+                                                _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                                _stream()))
+    return dq, dk, dv
 
 def timing_enable(max_launches: int):
     """Bracket every kernel launch with HIP events on its stream (0 disables)."""

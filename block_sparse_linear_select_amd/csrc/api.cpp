@@ -456,7 +456,8 @@ static int hybrid_impl(const hsa_attn_desc* desc, const void* q, const void* k, 
                        const void* U_q, const void* U_k, const void* W_o,
                        const int32_t* row_ptr_in, const int32_t* col_idx_in,
                        int32_t* row_ptr_out, int32_t* col_idx_out,
-                       void* o, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+                       void* o, void* workspace, size_t workspace_bytes, void* stream, bool noalloc,
+                       void* o_s = nullptr, float* lse = nullptr) {
   Shape s;
   const bool given = row_ptr_in || col_idx_in;
   if (given && !(row_ptr_in && col_idx_in)) return fail(HSA_ATTN_ERR_CSR, "row_ptr_in and col_idx_in go together");
@@ -498,7 +499,7 @@ static int hybrid_impl(const hsa_attn_desc* desc, const void* q, const void* k, 
   // all keys: the query-tile kernel also reads the linear branch out; the
   // complement variant adds its own readout to the sparse output afterwards
   hipError_t e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
-    return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, rp, ci, true, !s.compl_keys, w, o, nullptr, st);
+    return launch_attend(s, q, k, v, q_scale, k_scale, v_scale, rp, ci, true, !s.compl_keys, w, o, lse, st, o_s);
   });
   if (e != hipSuccess) return hip_fail(e, "hybrid attention");
   if (s.compl_keys) {
@@ -527,6 +528,20 @@ HSA_API int hsa_hybrid_attn_noalloc(const hsa_attn_desc* desc, const void* q, co
                                     int32_t* row_ptr_out, int32_t* col_idx_out, void* o, void* stream) {
   return hybrid_impl(desc, q, k, v, q_scale, k_scale, v_scale, U_q, U_k, W_o, row_ptr_in, col_idx_in, row_ptr_out,
                      col_idx_out, o, nullptr, 0, stream, true);
+}
+
+HSA_API int hsa_hybrid_attn_train(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                  const void* U_q, const void* U_k, const void* W_o,
+                                  const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                                  int32_t* row_ptr_out, int32_t* col_idx_out, void* o, void* o_s, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, s, true, false);
+  if (rc) return rc;
+  if ((rc = check_backward(s))) return rc;  // the calls whose gradients the backward gives
+  if (!o_s || !lse) return fail(HSA_ATTN_ERR_NULL, "o_s and lse are required");
+  return hybrid_impl(desc, q, k, v, nullptr, nullptr, nullptr, U_q, U_k, W_o, row_ptr_in, col_idx_in, row_ptr_out,
+                     col_idx_out, o, workspace, workspace_bytes, stream, false, o_s, lse);
 }
 
 // ---------------------------------------------------------------- W8A8 projections
@@ -574,11 +589,11 @@ HSA_API int hsa_qkv_proj_fp8(const void* x_codes, const float* x_scales, const v
 }
 
 // ---------------------------------------------------------------- backward
-HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
-                                     const void* U_q, const void* U_k, const void* W_o,
-                                     const int32_t* row_ptr, const int32_t* col_idx, const void* d_o,
-                                     float* d_q, float* d_k, float* d_v,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+static int backward_impl(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                         const void* U_q, const void* U_k, const void* W_o,
+                         const int32_t* row_ptr, const int32_t* col_idx, const void* o_s, const float* lse,
+                         const void* d_o, float* d_q, float* d_k, float* d_v,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   int rc = check_desc(desc, s, true, false);
   if (rc) return rc;
@@ -591,12 +606,19 @@ HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, c
   Scratch w = bind_plan(p, workspace);
   w.csc_cap = (long)s.B * s.H * s.T * s.kmax;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the forward state (S, z) and the sparse branch's output and log-sum-exp, recomputed
+  // the forward state (S, z), recomputed; the sparse branch's output and
+  // log-sum-exp as the training forward saved them, or recomputed
   if ((rc = run_linear_state(s, q, k, v, nullptr, nullptr, nullptr, U_q, U_k, W_o, false, w, st))) return rc;
-  hipError_t e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
-    return launch_attend(s, q, k, v, nullptr, nullptr, nullptr, row_ptr, col_idx, true, false, w, w.os, w.lse, st);
-  });
-  if (e != hipSuccess) return hip_fail(e, "sparse recompute");
+  hipError_t e;
+  if (o_s) {
+    w.os = const_cast<void*>(o_s);
+    w.lse = const_cast<float*>(lse);
+  } else {
+    e = timed(HSA_ATTN_KERNEL_ATTEND, st, [&] {
+      return launch_attend(s, q, k, v, nullptr, nullptr, nullptr, row_ptr, col_idx, true, false, w, w.os, w.lse, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "sparse recompute");
+  }
   e = timed(HSA_ATTN_KERNEL_BWD_LINEAR, st, [&] {
     return launch_backward(s, q, k, v, d_o, U_q, U_k, W_o, row_ptr, col_idx, w, d_q, d_k, d_v, 1, st);
   });
@@ -606,4 +628,23 @@ HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, c
   });
   if (e != hipSuccess) return hip_fail(e, "sparse backward");
   return HSA_ATTN_OK;
+}
+
+HSA_API int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                     const void* U_q, const void* U_k, const void* W_o,
+                                     const int32_t* row_ptr, const int32_t* col_idx, const void* d_o,
+                                     float* d_q, float* d_k, float* d_v,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(desc, q, k, v, U_q, U_k, W_o, row_ptr, col_idx, nullptr, nullptr, d_o, d_q, d_k, d_v,
+                       workspace, workspace_bytes, stream);
+}
+
+HSA_API int hsa_hybrid_attn_backward_saved(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                           const void* U_q, const void* U_k, const void* W_o,
+                                           const int32_t* row_ptr, const int32_t* col_idx, const void* o_s,
+                                           const float* lse, const void* d_o, float* d_q, float* d_k, float* d_v,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!o_s || !lse) return fail(HSA_ATTN_ERR_NULL, "o_s and lse are required");
+  return backward_impl(desc, q, k, v, U_q, U_k, W_o, row_ptr, col_idx, o_s, lse, d_o, d_q, d_k, d_v,
+                       workspace, workspace_bytes, stream);
 }

@@ -45,6 +45,7 @@ struct AttendArgs {
   const float* vs;
   void* o;
   float* lse;
+  void* o_s;  // optional, sparse + linear kernels of bf16/float inputs: O_s alone (output type, rows >= N zero)
   long nrows;
 };
 
@@ -222,6 +223,22 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         r4[i] = qvalid ? x : 0.f;
       }
       st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+    }
+    if constexpr (SPARSE && LINEAR) {
+      if (a.o_s) {  // the sparse branch's output alone, as the sparse-only kernel writes it
+        T* OS = reinterpret_cast<T*>(a.o_s) + base + (size_t)qrow * D;
+#pragma unroll
+        for (int jd = 0; jd < NDB; ++jd) {
+          float r4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = 0.f;
+            x += acc_o[jd][i] * inv_l;
+            r4[i] = qvalid ? x : 0.f;
+          }
+          st4o(OS + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+        }
+      }
     }
   }
 }
@@ -480,6 +497,25 @@ __global__ __launch_bounds__(128, 2) void k_attend_bf16(AttendArgs a) {
         r4[i] = qvalid[qb] ? x : 0.f;
       }
       st4o(O + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+    }
+  }
+  if constexpr (SPARSE && LINEAR) {
+    if (a.o_s) {  // the sparse branch's output alone, as the sparse-only kernel writes it
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        bf16_t* OS = reinterpret_cast<bf16_t*>(a.o_s) + base + (size_t)qrow[qb] * D;
+#pragma unroll
+        for (int jd = 0; jd < NDB; ++jd) {
+          float r4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = 0.f;
+            x += acc_o[qb][jd][i] * inv_l[qb];
+            r4[i] = qvalid[qb] ? x : 0.f;
+          }
+          st4o(OS + 16 * jd + 4 * g, r4[0], r4[1], r4[2], r4[3]);
+        }
+      }
     }
   }
 }

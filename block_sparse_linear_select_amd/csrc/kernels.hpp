@@ -123,7 +123,7 @@ hipError_t launch_select(const Shape& s, const void* q, const float* qs, const S
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const float* qs, const float* ks, const float* vs,
                          const int32_t* row_ptr, const int32_t* col_idx, bool sparse, bool linear,
-                         const Scratch& w, void* o, float* lse, hipStream_t st);
+                         const Scratch& w, void* o, float* lse, hipStream_t st, void* o_s = nullptr);
 // Backward pass pieces (float32 gradients): part 1 = the linear branch (its dq,
 // dk, dv written, D written), part 2 = the transposed mask and the sparse
 // branch (dq, dk, dv added to).

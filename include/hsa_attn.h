@@ -296,8 +296,8 @@ int hsa_hybrid_attn_noalloc(const hsa_attn_desc* desc, const void* q, const void
  *   (entries outside [0, T) are skipped; rows with repeated entries, or with
  *   more than topk + force_diag entries in [0, T), are outside this call's
  *   domain: the transposed mask it builds holds B*H*T*(topk + force_diag)
- *   entries, so set topk to the longest row of a mask not made by selection); d_o: [B, H, N_pad, d] in the input type
- *   (rows >= N are ignored).
+ *   entries, so set topk to the longest row of a mask not made by selection);
+ *   d_o: [B, H, N_pad, d] in the input type (rows >= N are ignored).
  *   d_q, d_k, d_v: float32 [B, H, N_pad, d], written in full (rows >= N zero).
  *   desc->linear_keys must be HSA_ATTN_LINEAR_ALL_KEYS (HSA_ATTN_ERR_SHAPE
  *   otherwise).  Workspace: HSA_ATTN_CALL_BACKWARD.
@@ -307,6 +307,42 @@ int hsa_hybrid_attn_backward(const hsa_attn_desc* desc, const void* q, const voi
                              const int32_t* row_ptr, const int32_t* col_idx, const void* d_o,
                              float* d_q, float* d_k, float* d_v,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training forward: hsa_hybrid_attn (all-keys linear branch, float32 or bf16
+ * inputs) that also saves what the backward needs from it, as FlashAttention
+ * saves its log-sum-exp, so that hsa_hybrid_attn_backward_saved can skip the
+ * sparse recompute (one attention pass).  Same passages as the backward: the
+ * sparse warm-up trains through the operator (SparkDiffusion news article,
+ * section 05; project blog, "A simple staging principle", item 1).
+ *   Arguments as for hsa_hybrid_attn (no scales: FP8 inputs and the
+ *   complement variant give HSA_ATTN_ERR_DTYPE / HSA_ATTN_ERR_SHAPE, and topk
+ *   must lie in [1, T] also with a given mask, as for the backward), plus
+ *   o_s: [B, H, N_pad, d] in out_dtype, the sparse branch's output O_s alone
+ *   (rows >= N zero), bitwise what hsa_sparse_attn writes on the same mask;
+ *   lse: float [B, H, N_pad], its natural-log log-sum-exp (rows >= N
+ *   undefined), as hsa_sparse_attn's lse.  Both required (HSA_ATTN_ERR_NULL).
+ *   o is bitwise what hsa_hybrid_attn writes.  Workspace: HSA_ATTN_CALL_HYBRID.
+ */
+int hsa_hybrid_attn_train(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const void* U_q, const void* U_k, const void* W_o,
+                          const int32_t* row_ptr_in, const int32_t* col_idx_in,
+                          int32_t* row_ptr_out, int32_t* col_idx_out, void* o, void* o_s, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hsa_hybrid_attn_backward with the sparse branch's output and log-sum-exp
+ * taken from hsa_hybrid_attn_train (o_s, lse: as that call wrote them, for
+ * the same inputs and mask) instead of recomputed: the same gradients, bit
+ * for bit, without one attention pass.  o_s and lse are required
+ * (HSA_ATTN_ERR_NULL); everything else as for hsa_hybrid_attn_backward.
+ * Workspace: HSA_ATTN_CALL_BACKWARD.
+ */
+int hsa_hybrid_attn_backward_saved(const hsa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                   const void* U_q, const void* U_k, const void* W_o,
+                                   const int32_t* row_ptr, const int32_t* col_idx, const void* o_s,
+                                   const float* lse, const void* d_o, float* d_q, float* d_k, float* d_v,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * W8A8 FP8 projections in front of the attention (SparkDiffusion news

@@ -167,3 +167,31 @@ def test_noalloc_rejects_a_call_beyond_its_static_scratch_before_any_launch():
     n = ctypes.c_size_t(0)
     assert B.lib().hsa_attn_workspace_size(ctypes.byref(d), B.CALL_HYBRID, ctypes.byref(n)) == 0
     assert n.value > (256 << 20)
+
+
+def test_training_forward_and_saved_backward_arguments():
+    """The training forward and the backward on saved statistics take the
+    backward's domain (float32/bf16, all-keys branch) and need o_s and lse."""
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    need = _ws(_cfg(), B.CALL_HYBRID)[1]
+    d = _cfg().desc()
+    # o_s and lse required
+    rc = L.hsa_hybrid_attn_train(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, None, None, None,
+                                 fake, None, fake, fake, need, None)
+    assert rc == -1 and b"o_s" in L.hsa_attn_last_error()
+    rc = L.hsa_hybrid_attn_backward_saved(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                          None, fake, fake, fake, fake, fake, need, None)
+    assert rc == -1
+    # FP8 inputs and the complement variant are outside the backward's domain
+    d8 = _cfg(dtype="fp8").desc()
+    rc = L.hsa_hybrid_attn_train(ctypes.byref(d8), fake, fake, fake, fake, fake, fake, None, None, None, None,
+                                 fake, fake, fake, fake, need, None)
+    assert rc == -3
+    dc = _cfg(linear_keys="complement").desc()
+    rc = L.hsa_hybrid_attn_train(ctypes.byref(dc), fake, fake, fake, fake, fake, fake, None, None, None, None,
+                                 fake, fake, fake, fake, need, None)
+    assert rc == -2
+    rc = L.hsa_hybrid_attn_backward_saved(ctypes.byref(dc), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                          fake, fake, fake, fake, fake, fake, need, None)
+    assert rc == -2

@@ -195,3 +195,55 @@ def test_backward_edge_rows(name):
     print(f"  dQ {errs[0]}  dK {errs[1]}  dV {errs[2]}", flush=True)
     for e in errs:
         assert e.value <= TOL[w.dtype]
+
+
+def _same_bits(a, b):
+    a, b = a.contiguous(), b.contiguous()
+    if a.dtype.is_floating_point:
+        it = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[a.element_size()]
+        a, b = a.view(it), b.view(it)
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_d64_r16", "bf16_aligned_diag"])
+def test_training_forward_saves_the_sparse_output_and_lse(name):
+    """O of the training forward is bitwise hsa_hybrid_attn's; O_s and the
+    log-sum-exp it saves are bitwise hsa_sparse_attn's on the same mask."""
+    print(f"\n[case {name}]", flush=True)
+    inp = Hp.gen(name)
+    w = inp.w
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    args = (cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"])
+    o, o_s, lse, rp, ci = B.hybrid_attn_train(*args, export_mask=True)
+    o_ref, rp_ref, ci_ref = B.hybrid_attn(*args, export_mask=True)
+    torch.cuda.synchronize()
+    assert _same_bits(o, o_ref)
+    assert torch.equal(rp, rp_ref)
+    n = int(rp[-1])
+    assert torch.equal(ci[:n], ci_ref[:n])
+    os_ref, lse_ref = B.sparse_attn(cfg, d["q"], d["k"], d["v"], rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    assert _same_bits(o_s, os_ref)
+    assert _same_bits(lse[:, :, :w.N], lse_ref[:, :, :w.N])
+    assert torch.all(o_s[:, :, w.N:] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_ragged", "bf16_d64_r16", "bf16_aligned_diag", "bf16_long_rows"])
+def test_backward_on_saved_statistics_equals_the_recomputing_backward(name):
+    """The backward fed the training forward's O_s and log-sum-exp gives the
+    recomputing backward's gradients bit for bit."""
+    print(f"\n[case {name}]", flush=True)
+    inp = Hp.gen(name)
+    w = inp.w
+    d = Hp.to_device(inp, DEV)
+    cfg = B.Config.from_workload(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rp, ci = Hp.csr_tensors([Hp.oracle_mask_head(inp, *bh)[1] for bh in heads], DEV)
+    g = upstream_grad(w, seed=w.seed + 21, pad_value=3.0).to(DEV)
+    _, o_s, lse = B.hybrid_attn_train(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], row_ptr=rp, col_idx=ci)
+    ref = _run(cfg, d, rp, ci, g)
+    got = B.hybrid_attn_backward_saved(cfg, d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"], rp, ci, o_s, lse, g)
+    torch.cuda.synchronize()
+    for x, y, what in zip(ref, got, ("dq", "dk", "dv")):
+        assert _same_bits(x, y), what

@@ -40,8 +40,8 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
   if (select) {
     p.off_qmean = take(bh * s.d * s.T * sizeof(double));
     p.off_kmean = take(bh * s.d * s.T * sizeof(double));
-    p.off_khi = take(bh * s.d * s.T * sizeof(uint16_t));
-    p.off_klo = take(bh * s.d * s.T * sizeof(uint16_t));
+    p.off_khi = take(bh * s.d * kfrag_tiles(s.T) * sizeof(uint16_t));
+    p.off_klo = take(bh * s.d * kfrag_tiles(s.T) * sizeof(uint16_t));
     if (s.force_diag) {
       p.off_sel_tmp = take(rows * (s.topk + 1) * sizeof(int32_t));
       p.off_sel_cnt = take(rows * sizeof(int32_t));

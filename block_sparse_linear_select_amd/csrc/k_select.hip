@@ -272,8 +272,8 @@ struct SelectArgs {
   int T, N, N_pad, topk, force_diag, direct;
   const void* q;        // [BH][N_pad][D] in the input type
   const float* qs;      // fp8: [BH][T] tile scales of Q
-  const uint16_t* khi;  // [BH][T][D] bf16 hi part of the key tile means
-  const uint16_t* klo;  // [BH][T][D] bf16 lo part
+  const uint16_t* khi;  // bf16 hi part of the key tile means, fragment order (kfrag_index)
+  const uint16_t* klo;  // bf16 lo part, the same order
   const double* kmean;  // [BH][T][D]
   double* qmean;        // [BH][T][D], written
   double* qbar_out;     // optional export [BH][T][D]
@@ -385,19 +385,21 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
     for (int i = 0; i < 4; ++i) aa[c].w[i] = ah[c].w[i] & 0x7FFF7FFFu;
   }
   __syncthreads();  // the operands are in registers: the region now holds scores
-  // the head's key means as bounds-checked buffers: tiles past T read as zeros
-  const __amdgpu_buffer_rsrc_t khr = make_rsrc(a.khi + tb * D, T * D * 2);
-  const __amdgpu_buffer_rsrc_t klr = make_rsrc(a.klo + tb * D, T * D * 2);
+  // the head's key means in fragment order as bounds-checked buffers: the
+  // padding of the last key block holds zeros, blocks past it read as zeros
+  const size_t kfb = (size_t)bh * kfrag_tiles(T) * D;
+  const __amdgpu_buffer_rsrc_t khr = make_rsrc(a.khi + kfb, kfrag_tiles(T) * D * 2);
+  const __amdgpu_buffer_rsrc_t klr = make_rsrc(a.klo + kfb, kfrag_tiles(T) * D * 2);
   const int nkb = (T + 15) / 16;
   float em[4] = {0.f, 0.f, 0.f, 0.f};
   // three key blocks of operands in flight per wave (blocks w, w + 4, w + 8, ...)
   Frag<bf16_t> bhf[3][D / 32], blf[3][D / 32];
   auto loadb = [&](int kb, int slot) {
-    const int off = ((16 * kb + l16) * D + 8 * g) * 2;
+    const int off = (kb * (D / 32) * 64 + lane) * 16;  // one 1 KB run per (kb, c)
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      bhf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(khr, off + 64 * c, 0, 0);
-      blf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(klr, off + 64 * c, 0, 0);
+      bhf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(khr, off + 1024 * c, 0, 0);
+      blf[slot][c].w = __builtin_amdgcn_raw_buffer_load_b128(klr, off + 1024 * c, 0, 0);
     }
   };
   auto scores = [&](int kb, int slot) {

@@ -9,6 +9,16 @@ namespace hsa {
 
 enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };
 
+// Layout of the bf16 hi and lo parts of the key tile means: the order of the
+// selection's matrix-core B fragments.  Per (b, h): key block kb of 16 tiles,
+// 32-wide d chunk c, then lane (tile mod 16) + 16 ((d mod 32) / 8), then 8
+// consecutive d; one fragment load of a (kb, c) reads 1 KB contiguous.  The
+// tiles are padded to whole key blocks (the padding holds zeros).
+__host__ __device__ inline int kfrag_tiles(int T) { return 16 * ((T + 15) / 16); }
+__host__ __device__ inline size_t kfrag_index(int t, int d, int D) {
+  return ((size_t)((t >> 4) * (D / 32) + (d >> 5)) * 64 + ((d & 31) >> 3) * 16 + (t & 15)) * 8 + (d & 7);
+}
+
 // Validated sizes as the kernels see them.
 struct Shape {
   int B, H, N, N_pad, d, T;
@@ -51,8 +61,8 @@ inline int stream_chunks(const Shape& s) {
 struct Scratch {
   double* qmean = nullptr;     // [BH][T][d] tile means of Q
   double* kmean = nullptr;     // [BH][T][d] tile means of K
-  uint16_t* khi = nullptr;     // [BH][T][d] bf16 hi part of the key tile means
-  uint16_t* klo = nullptr;     // [BH][T][d] bf16 lo part
+  uint16_t* khi = nullptr;     // bf16 hi part of the key tile means, fragment order (kfrag_index)
+  uint16_t* klo = nullptr;     // bf16 lo part, the same order
   int32_t* sel_tmp = nullptr;  // [BH*T][kmax] per-row selection (forced-diagonal path)
   int32_t* sel_cnt = nullptr;  // [BH*T]
   int32_t* row_ptr = nullptr;  // [BH*T + 1] internal CSR when the caller exports none

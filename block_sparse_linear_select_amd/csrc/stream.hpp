@@ -151,8 +151,8 @@ struct StreamArgs {
   const void* uk;  // [H][d][r] in the parameter type
   int H;
   double* kmean;  // [BH][T][d] tile means of K
-  uint16_t* khi;  // [BH][T][d] bf16 hi part of the means
-  uint16_t* klo;  // [BH][T][d] bf16 lo part (mean - hi, rounded)
+  uint16_t* khi;  // bf16 hi part of the means, in fragment order (kfrag_index)
+  uint16_t* klo;  // bf16 lo part (mean - hi, rounded), the same order
   double* kbar_out;
   float* part_s;
   float* part_z;
@@ -447,8 +447,9 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
           a.kmean[o] = mean;
           if (a.kbar_out) a.kbar_out[o] = mean;
           const uint32_t hb = f32_to_bf16_bits((float)mean);
-          a.khi[o] = (uint16_t)hb;
-          a.klo[o] = (uint16_t)f32_to_bf16_bits((float)(mean - (double)bf16_bits_to_f32(hb)));
+          const size_t of = (size_t)bh * kfrag_tiles(a.T) * D + kfrag_index(t, tid, D);  // fragment order
+          a.khi[of] = (uint16_t)hb;
+          a.klo[of] = (uint16_t)f32_to_bf16_bits((float)(mean - (double)bf16_bits_to_f32(hb)));
         }
       }
       __syncthreads();
@@ -464,6 +465,15 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   for (int t = t0; t < t1; t += 2) {
     process(t, tra);
     process(t + 1, trb);
+  }
+  if constexpr (POOL) {  // the padding of the last key block of the hi / lo parts reads as zero
+    if (t1 == a.T && tid < D) {
+      for (int t = a.T; t < kfrag_tiles(a.T); ++t) {
+        const size_t of = (size_t)bh * kfrag_tiles(a.T) * D + kfrag_index(t, tid, D);
+        a.khi[of] = 0;
+        a.klo[of] = 0;
+      }
+    }
   }
 
   if constexpr (STATE) {

@@ -75,7 +75,10 @@ Plan make_plan(const Shape& s, bool select, bool csr_internal, bool linear, bool
     const int nrc = (s.rank + 31) / 32, ndb = s.d / 16, nrb = s.rank / 16;
     const size_t nfe = (size_t)ndb * nrc * 512, nch = stream_chunks(s), rd = (size_t)s.rank * s.d;
     if (!p.compl_keys) p.off_s_full = take(bh * nfe * sizeof(float));
-    p.off_s_plain = take(bh * rd * sizeof(float));
+    p.off_s_pfrag = take(bh * rd * sizeof(float));
+    p.off_wob = take((size_t)s.H * s.d * s.d * elt);
+    p.off_uqp = take((size_t)s.H * ndb * nrc * 512 * elt);
+    p.off_ukp = take((size_t)s.H * ndb * nrc * 512 * elt);
     p.off_os = take(bh * (size_t)s.N_pad * s.d * elt);
     p.off_lse = take(bh * (size_t)s.N_pad * sizeof(float));
     p.off_dsum = take(bh * (size_t)s.N_pad * sizeof(float));
@@ -127,7 +130,10 @@ Scratch bind_plan(const Plan& p, void* ws) {
   if (p.vt) w.vt = b + p.off_vt;
   if (p.backward) {
     w.s_full = reinterpret_cast<float*>(b + p.off_s_full);
-    w.s_plain = reinterpret_cast<float*>(b + p.off_s_plain);
+    w.s_pfrag = reinterpret_cast<float*>(b + p.off_s_pfrag);
+    w.wob_frag = b + p.off_wob;
+    w.uqp_frag = b + p.off_uqp;
+    w.ukp_frag = b + p.off_ukp;
     w.os = b + p.off_os;
     w.lse = reinterpret_cast<float*>(b + p.off_lse);
     w.dsum = reinterpret_cast<float*>(b + p.off_dsum);

@@ -61,7 +61,10 @@ struct BwdArgs {
   float* dsum;             // [BH][N_pad] D_i
   const float* z;          // [BH][R]
   const float* s_frag;     // [BH][NFE] S^T as float readout A fragments
-  const float* s_plain;    // [BH][R][D]
+  const float* s_pfrag;    // [BH][R*D] S in perm_frag_index order
+  const void* wob_frag;    // [H][D*D] W_o as A fragments
+  const void* uqp_frag;    // [H] U_q in perm_frag_index order
+  void* ukp_frag;          // [H] U_k in perm_frag_index order (written by k_bwd_fin)
   const void* uq_frag;     // [H] U_q^T A fragments
   void* uk_frag;           // [H] U_k^T A fragments (written by k_bwd_fin)
   const float2* rope;
@@ -119,34 +122,11 @@ __device__ __forceinline__ void load8_any(float* x, const bf16_t* p) {
   for (int s = 0; s < 8; ++s) x[s] = bf16_bits_to_f32((w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
 }
 __device__ __forceinline__ void load8_any(float* x, const float* p) { load8f(x, p); }
-// 4 consecutive elements as floats
-__device__ __forceinline__ void load4_any(float* x, const bf16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  x[0] = bf16_bits_to_f32(w.x & 0xFFFFu); x[1] = bf16_bits_to_f32(w.x >> 16);
-  x[2] = bf16_bits_to_f32(w.y & 0xFFFFu); x[3] = bf16_bits_to_f32(w.y >> 16);
-}
-__device__ __forceinline__ void load4_any(float* x, const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
-// A fragment of a parameter matrix P [d][r] (row-major) with rows d = row and
-// the contraction over r in the permuted chunk order: slot s of lane group g
-// of chunk rc is r = 32 rc + 16 (s / 4) + 4 g + s % 4 (zero past R).
-template <typename OT, int R>
-__device__ __forceinline__ void param_perm_frag(Frag<OT>& f, const OT* P, int row, int rc, int g) {
-  float x[8];
-  load4_any(x, P + (size_t)row * R + 32 * rc + 4 * g);
-  if (32 * rc + 16 < R) load4_any(x + 4, P + (size_t)row * R + 32 * rc + 16 + 4 * g);
-  else x[4] = x[5] = x[6] = x[7] = 0.f;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) f.set_pair(p, x[2 * p], x[2 * p + 1]);
-}
-// (cos, sin) of the rotation of feature pair jp (0 .. r/2 - 1) of token tok
+// (cos, sin) of the rotation of feature pair jp (0 .. r/2 - 1) at latent
+// position (t, y, x)
 template <int R>
-__device__ __forceinline__ float2 rope_cs(const float2* rope, int gt, int gh, int gw, int tok, int jp) {
+__device__ __forceinline__ float2 rope_at(const float2* rope, int gt, int gh, int t, int y, int x, int jp) {
   constexpr int ht = 3 * R / 16, hh = 3 * R / 16, hwp = R / 8;
-  const int hw = gh * gw;
-  const int t = tok / hw, rem = tok - t * hw, y = rem / gw, x = rem - y * gw;
   if (jp < ht) return rope[t * ht + jp];
   if (jp < ht + hh) return rope[gt * ht + y * hh + (jp - ht)];
   return rope[gt * ht + gh * hh + x * hwp + (jp - ht - hh)];
@@ -797,10 +777,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   const T* G = reinterpret_cast<const T*>(a.dout) + base;
   const T* OS = reinterpret_cast<const T*>(a.os) + base;
   const T* UQF = reinterpret_cast<const T*>(a.uq_frag) + (size_t)h * NRB * (D / 32) * 512;
-  const T* UQ = reinterpret_cast<const T*>(a.uq) + (size_t)h * D * R;
-  const T* WO = reinterpret_cast<const T*>(a.wo) + (size_t)h * D * D;
+  // parameter operands in fragment order: every fragment load reads one contiguous run
+  const T* UQP = reinterpret_cast<const T*>(a.uqp_frag) + (size_t)h * NDB * NRC * 512;
+  const T* WOB = reinterpret_cast<const T*>(a.wob_frag) + (size_t)h * D * D;
   const float* SF = a.s_frag + (size_t)bh * NFE;
-  const float* SP = a.s_plain + (size_t)bh * R * D;
+  const float* SPF = a.s_pfrag + (size_t)bh * R * D;
   const float* Z = a.z + (size_t)bh * R;
 
   f32x4 dsacc[NBW];
@@ -837,6 +818,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
     // phi > 1 and phi elsewhere)
     const int ql = 16 * w + l16;
     const int tok = qvalid ? qrow : 0;
+    int pt, py, px;  // the query's latent position
+    {
+      const int hw = a.gh * a.gw, rem = tok - (tok / hw) * hw;
+      pt = tok / hw;
+      py = rem / a.gw;
+      px = rem - py * a.gw;
+    }
     float fq[NRB][4];
     float den = 0.f;
     Frag<T> qpf[NRC];
@@ -858,7 +846,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
         }
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-          const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, (16 * rb + 4 * g) / 2 + pr);
+          const float2 cs = rope_at<R>(a.rope, a.gt, a.gh, pt, py, px, (16 * rb + 4 * g) / 2 + pr);
           const float x0 = fq[rb][2 * pr], x1 = fq[rb][2 * pr + 1];
           qp[rb][2 * pr] = x0 * cs.x - x1 * cs.y;
           qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
@@ -891,7 +879,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
         for (int cc = 0; cc < D / 32; ++cc) {
           Frag<T> wf;
-          load8(wf, WO + (size_t)(16 * jd + l16) * D + 32 * cc + 8 * g);
+          load8(wf, WOB + ((size_t)(jd * (D / 32) + cc) * 64 + lane) * 8);
           mma(gw[hh], wf, gf[cc]);
         }
         *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
@@ -929,10 +917,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
       dqp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const float* sp = SP + (size_t)(16 * rb + l16) * D + 32 * c + 4 * g;
         float x[8];
-        load4_any(x, sp);
-        load4_any(x + 4, sp + 16);
+        load8f(x, SPF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
         Frag<T> hi, lo;
         split8(x, hi, lo);
         mma_hl(dqp[rb], hi, lo, gnf[c]);
@@ -945,7 +931,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int m = 16 * rb + 4 * g + 2 * pr;
-        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
+        const float2 cs = rope_at<R>(a.rope, a.gt, a.gh, pt, py, px, m / 2);
         const float x0 = dqp[rb][2 * pr], x1 = dqp[rb][2 * pr + 1];
         const float d0 = fmaf(gden, Z[m], x0 * cs.x + x1 * cs.y);
         const float d1 = fmaf(gden, Z[m + 1], -x0 * cs.y + x1 * cs.x);
@@ -969,7 +955,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
         Frag<T> uf;
-        param_perm_frag<T, R>(uf, UQ, 16 * jd + l16, rc, g);
+        load8(uf, UQP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
         mma(acc, uf, dxf[rc]);
       }
       *reinterpret_cast<float4*>(dqo + 16 * jd + 4 * g) =
@@ -1061,6 +1047,12 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdArgs a) {
         const int c = f % (D / 32), rbk = f / (D / 32);
         out[idx] = U[(size_t)(32 * c + 8 * (l >> 4) + s2) * R + 16 * rbk + (l & 15)];
       }
+      T* pout = reinterpret_cast<T*>(a.ukp_frag) + (size_t)h * (D / 16) * NRC * 512;
+      for (int idx = tid; idx < (D / 16) * NRC * 512; idx += 256) {
+        int rr, cc;
+        perm_frag_source(idx, R, &rr, &cc);
+        pout[idx] = cc < R ? U[(size_t)rr * R + cc] : T{};
+      }
     }
   }
 }
@@ -1085,7 +1077,7 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
   const T* K = reinterpret_cast<const T*>(a.k) + base;
   const T* V = reinterpret_cast<const T*>(a.v) + base;
   const T* UKF = reinterpret_cast<const T*>(a.uk_frag) + (size_t)h * NRB * (D / 32) * 512;
-  const T* UK = reinterpret_cast<const T*>(a.uk) + (size_t)h * D * R;
+  const T* UKP = reinterpret_cast<const T*>(a.ukp_frag) + (size_t)h * NDB * NRC * 512;
   const float* DSF = a.ds_frag + (size_t)bh * NFE;
   const float* DSP = a.ds_plain + (size_t)bh * R * D;
   const float* DZ = a.dz + (size_t)bh * R;
@@ -1134,13 +1126,14 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int tok = kvalid[kb] ? krow[kb] : 0;
+    const int hw = a.gh * a.gw, pt = tok / hw, rem = tok - pt * hw, py = rem / a.gw, px = rem - py * a.gw;
     float kp[NRB][4], dx[NRB][4];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int m = 16 * rb + 4 * g + 2 * pr;
-        const float2 cs = rope_cs<R>(a.rope, a.gt, a.gh, a.gw, tok, m / 2);
+        const float2 cs = rope_at<R>(a.rope, a.gt, a.gh, pt, py, px, m / 2);
         const float e0 = xk[kb][rb][2 * pr], e1 = xk[kb][rb][2 * pr + 1];
         const float f0 = elu1(e0), f1 = elu1(e1);
         kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
@@ -1177,7 +1170,7 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
       Frag<T> hi, lo;
       split8(x, hi, lo);
       Frag<T> uf;
-      param_perm_frag<T, R>(uf, UK, 16 * jd + l16, rc, g);
+      load8(uf, UKP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         mma_hl(av[kb], hi, lo, kpf[kb][rc]);

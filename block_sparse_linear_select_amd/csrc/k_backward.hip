@@ -16,7 +16,8 @@ hipError_t launch_backward(const Shape& s, const void* q, const void* k, const v
   a.scale = s.scale;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.uq = uq; a.uk = uk; a.wo = wo;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
-  a.os = w.os; a.lse = w.lse; a.dsum = w.dsum; a.z = w.z; a.s_frag = w.s_full; a.s_plain = w.s_plain;
+  a.os = w.os; a.lse = w.lse; a.dsum = w.dsum; a.z = w.z; a.s_frag = w.s_full; a.s_pfrag = w.s_pfrag;
+  a.wob_frag = w.wob_frag; a.uqp_frag = w.uqp_frag; a.ukp_frag = w.ukp_frag;
   a.uq_frag = w.uq_frag; a.uk_frag = w.uk_frag; a.rope = w.rope;
   a.part_ds = w.part_ds; a.part_dz = w.part_dz; a.ds_plain = w.ds_plain; a.ds_frag = w.ds_frag; a.dz = w.dz;
   a.dq = dq; a.dk = dk; a.dv = dv;

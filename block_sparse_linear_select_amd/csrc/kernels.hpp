@@ -19,6 +19,25 @@ __host__ __device__ inline size_t kfrag_index(int t, int d, int D) {
   return ((size_t)((t >> 4) * (D / 32) + (d >> 5)) * 64 + ((d & 31) >> 3) * 16 + (t & 15)) * 8 + (d & 7);
 }
 
+// Position of element (row, col) of a row-major matrix with ncol columns in
+// the fragment order the backward's linear kernels read their parameter
+// operands in (one 1 KB or 2 KB run per fragment load): 16-row block, 32-wide
+// column chunk (ceil(ncol / 32) per row block), lane (row mod 16) + 16 g,
+// slot s, where slots 0-3 hold columns 32 c + 4 g + s and slots 4-7 columns
+// 32 c + 16 + 4 g + (s - 4) (slots past ncol hold zeros).
+__host__ __device__ inline size_t perm_frag_index(int row, int col, int ncol) {
+  const int nch = (ncol + 31) / 32, c = col >> 5, wc = col & 31;
+  const int g = (wc & 15) >> 2, s = (wc & 3) + (wc >= 16 ? 4 : 0);
+  return ((size_t)((row >> 4) * nch + c) * 64 + g * 16 + (row & 15)) * 8 + s;
+}
+// The inverse: the (row, col) a fragment slot holds; col >= ncol marks a zero slot.
+__host__ __device__ inline void perm_frag_source(size_t idx, int ncol, int* row, int* col) {
+  const int nch = (ncol + 31) / 32, s = (int)(idx & 7), l = (int)((idx >> 3) & 63);
+  const int fr = (int)(idx >> 9), c = fr % nch, g = l >> 4;
+  *row = 16 * (fr / nch) + (l & 15);
+  *col = 32 * c + (s < 4 ? 4 * g + s : 16 + 4 * g + (s - 4));
+}
+
 // Validated sizes as the kernels see them.
 struct Shape {
   int B, H, N, N_pad, d, T;
@@ -79,7 +98,10 @@ struct Scratch {
   float* s_full = nullptr;     // [BH] full state S (before W_o) as float readout fragments
   void* wo_frag = nullptr;     // [H] W_o^T as matrix-core A fragments
   // backward pass
-  float* s_plain = nullptr;    // [BH][r][d] S (before W_o)
+  float* s_pfrag = nullptr;    // [BH][r*d] S (before W_o) in perm_frag_index order
+  void* wob_frag = nullptr;    // [H][d*d] W_o as A fragments (rows 16-blocks, 32-wide column chunks)
+  void* uqp_frag = nullptr;    // [H] U_q in perm_frag_index order
+  void* ukp_frag = nullptr;    // [H] U_k in perm_frag_index order
   void* os = nullptr;          // [BH][N_pad][d] sparse-branch output, output type
   float* lse = nullptr;        // [BH][N_pad]
   float* dsum = nullptr;       // [BH][N_pad] dO . O_s
@@ -103,7 +125,7 @@ struct Plan {
   size_t off_row_ptr = 0, off_col_idx = 0, off_part_s = 0, off_part_z = 0, off_sp = 0;
   size_t off_z = 0, off_uq = 0, off_rope = 0, off_vt = 0;
   size_t off_tile_s = 0, off_tile_z = 0, off_s_full = 0, off_wo = 0;
-  size_t off_s_plain = 0, off_os = 0, off_lse = 0, off_dsum = 0, off_part_ds = 0, off_part_dz = 0;
+  size_t off_s_pfrag = 0, off_wob = 0, off_uqp = 0, off_ukp = 0, off_os = 0, off_lse = 0, off_dsum = 0, off_part_ds = 0, off_part_dz = 0;
   size_t off_ds_plain = 0, off_ds_frag = 0, off_dz = 0, off_uk = 0, off_csc_cnt = 0, off_col_ptr = 0, off_row_idx = 0;
   size_t off_csc_bits = 0;
   bool select = false, csr_internal = false, linear = false, vt = false, compl_keys = false, backward = false;

@@ -532,7 +532,9 @@ struct FinalArgs {
   float* z;
   void* uq_frag;
   float* s_full;   // optional: [BH] S itself (before W_o) as float readout A fragments
-  float* s_plain;  // optional: [BH][r][d] S itself (before W_o)
+  float* s_pfrag;  // optional (backward): [BH][r*d] S itself (before W_o), perm_frag_index order
+  void* wob_frag;  // optional (backward): [H] W_o as A fragments
+  void* uqp_frag;  // optional (backward): [H] U_q in perm_frag_index order
   void* wo_frag;   // optional: [H] W_o^T as A fragments
 };
 
@@ -579,8 +581,26 @@ __global__ __launch_bounds__(256) void k_finalize(FinalArgs a) {
     a.z[(size_t)bh * R + tid] = s;
   }
   __syncthreads();
-  if (a.s_plain) {
-    for (int e = tid; e < kFinRows * D; e += 256) a.s_plain[((size_t)bh * R + r0) * D + e] = S[e];
+  if (a.s_pfrag) {
+    for (int e = tid; e < kFinRows * D; e += 256)
+      a.s_pfrag[(size_t)bh * R * D + perm_frag_index(r0 + e / D, e % D, D)] = S[e];
+    if (blockIdx.y == 0 && bh < a.H) {
+      // W_o A fragments: frag (jd, cc), lane l, slot s -> W_o[16 jd + l%16][32 cc + 8 (l/16) + s]
+      const OT* W = reinterpret_cast<const OT*>(a.wo) + (size_t)h * D * D;
+      OT* wout = reinterpret_cast<OT*>(a.wob_frag) + (size_t)h * D * D;
+      for (int idx = tid; idx < D * D; idx += 256) {
+        const int s2 = idx & 7, l = (idx >> 3) & 63, fr = idx >> 9;
+        const int cc = fr % (D / 32), jd = fr / (D / 32);
+        wout[idx] = W[(size_t)(16 * jd + (l & 15)) * D + 32 * cc + 8 * (l >> 4) + s2];
+      }
+      const OT* U = reinterpret_cast<const OT*>(a.uq) + (size_t)h * D * R;
+      OT* uout = reinterpret_cast<OT*>(a.uqp_frag) + (size_t)h * (D / 16) * NRC * 512;
+      for (int idx = tid; idx < (D / 16) * NRC * 512; idx += 256) {
+        int rr, cc;
+        perm_frag_source(idx, R, &rr, &cc);
+        uout[idx] = cc < R ? U[(size_t)rr * R + cc] : OT{};
+      }
+    }
   }
   if (a.s_full) {
     constexpr int NFE = (D / 16) * NRC * 512;

@@ -443,17 +443,17 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
   const int nj = (T + 63) / 64;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int kept[kSelRows / 4] = {0, 0, 0, 0};
+  // bit j: column lane + 64 j exists (columns past T read the row's padding)
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) vmask |= (lane + 64 * j < T ? 1u : 0u) << j;
   for (int r = w; r < nr; r += 4) {
     const int at = a0 + r;
     const int row = (int)(tb + at);
     float sv[MJ];
-    uint32_t key[MJ];
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {  // (columns past T read the row's padding and are marked absent)
-      const int b = lane + 64 * j;
-      sv[j] = sc[r * TP + b];
-      key[j] = b < T ? order_key32(sv[j]) : 0u;
-    }
+    for (int j = 0; j < MJ; ++j) sv[j] = sc[r * TP + lane + 64 * j];
+    auto ok = [&](int j) { return ((vmask >> j) & 1u) != 0u; };
     // this row's part of the score region now serves as scratch of this wave
     uint32_t* hw = reinterpret_cast<uint32_t*>(&sc[r * TP]);
     float* slot = &sc[r * TP];
@@ -470,18 +470,18 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < MJ; ++j)
-        if (key[j] != 0u) mx = fmaxf(mx, sv[j]);
+        if (ok(j)) mx = fmaxf(mx, sv[j]);
       const float theta = kth_largest_vec(mx, mx > -INFINITY, k, lane, slot + 64);
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) cnt += (key[j] != 0u && sv[j] >= theta) ? 1 : 0;
+      for (int j = 0; j < MJ; ++j) cnt += (ok(j) && sv[j] >= theta) ? 1 : 0;
       const int pre = wave_prefix_sum(cnt, lane);
       const int c = __builtin_amdgcn_readlane(pre, 63);
       if (c <= 64) {
         int pos = pre - cnt;  // this lane's candidates go to slots pos, pos + 1, ...
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
-          if (key[j] != 0u && sv[j] >= theta) slot[pos++] = sv[j];
+          if (ok(j) && sv[j] >= theta) slot[pos++] = sv[j];
         }
         wave_lds_order();
         const float cv = lane < c ? slot[lane] : -INFINITY;
@@ -491,6 +491,9 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
       }
     }
     if (!fast) {
+      uint32_t key[MJ];  // order-preserving keys, 0 for absent columns
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) key[j] = ok(j) ? order_key32(sv[j]) : 0u;
       const uint32_t sel = radix_topk<MJ>(key, nj, k, lane, hw);
       tmin = INFINITY;
 #pragma unroll
@@ -505,9 +508,8 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
     int cin = 0, ccand = 0;
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
-      const bool ok = key[j] != 0u;
-      const bool in = ok && sv[j] > hi;
-      const bool cand = ok && !in && sv[j] >= lo;
+      const bool in = ok(j) && sv[j] > hi;
+      const bool cand = ok(j) && !in && sv[j] >= lo;
       fin |= (in ? 1u : 0u) << j;
       fcand |= (cand ? 1u : 0u) << j;
       cin += in ? 1 : 0;

@@ -229,6 +229,72 @@ def test_given_csr_with_empty_row_and_out_of_range_columns(name):
         assert err <= Hp.TOL[w.dtype]
 
 
+def _neighbour_rows(T, rng):
+    """Rows for consecutive query tiles with every overlap pattern between
+    neighbours: equal, disjoint, nested, partly shared, one side empty, and
+    rows longer than 64 entries, with out-of-range entries at both ends of
+    some rows (each row sorted ascending)."""
+    rows = []
+    for a in range(T):
+        kind = (a // 2) % 6
+        if a % 2 == 0 or kind == 0:
+            n = min(T, 70 if kind == 5 else 3 + (a % 5))
+            r = np.sort(rng.choice(T, size=n, replace=False))
+        else:
+            prev = rows[a - 1]
+            if kind == 1:    # disjoint from the previous row
+                rest = np.setdiff1d(np.arange(T), prev)
+                r = np.sort(rng.choice(rest, size=min(len(rest), 4), replace=False))
+            elif kind == 2:  # a subset of it
+                r = np.sort(rng.choice(prev, size=max(1, len(prev) // 2), replace=False))
+            elif kind == 3:  # empty
+                r = np.array([], dtype=np.int64)
+            elif kind == 4:  # a superset of it
+                extra = rng.choice(np.setdiff1d(np.arange(T), prev), size=3, replace=False)
+                r = np.sort(np.concatenate([prev, extra]))
+            else:            # long, sharing about half of the previous long row
+                keep = rng.choice(prev, size=len(prev) // 2, replace=False)
+                extra = rng.choice(np.setdiff1d(np.arange(T), prev), size=min(T - len(prev), 40), replace=False)
+                r = np.sort(np.concatenate([keep, extra]))
+        rows.append(r.astype(np.int64))
+    for a in range(0, T, 3):  # out-of-range entries at the ends (still ascending)
+        rows[a] = np.concatenate([[-7, -1], rows[a], [T, T + 9]]).astype(np.int64)
+    return rows
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "bf16_long_rows", "bf16_d64_r16"])
+def test_neighbouring_rows_sharing_key_tiles(name):
+    """Each query tile sees exactly its own row, whatever its neighbours keep
+    (sparse branch vs the oracle, every tile checked alone)."""
+    w = Hp.CASES[name]
+    print(f"\n[case {name}] T={w.T}", flush=True)
+    inp = Hp.gen(w)
+    d = Hp.to_device(inp, DEV)
+    rng = np.random.default_rng(5)
+    rows_h = [_neighbour_rows(w.T, rng) for _ in range(w.B * w.H)]
+    rp, ci = Hp.csr_tensors(rows_h, DEV)
+    o, lse = B.sparse_attn(_cfg(w), d["q"], d["k"], d["v"], rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    i = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            qh, kh, vh = Hp.head_arrays(inp, b, h)
+            err = Hp.RelL2()
+            for a, row in enumerate(rows_h[i]):
+                kept = [int(c) for c in row if 0 <= c < w.T]
+                ref = R.sparse_tile(qh, kh, vh, w.N, a, kept, w.softmax_scale)
+                got = o[b, h, 64 * a:64 * a + len(ref)]
+                if not kept:
+                    assert np.all(got == 0)
+                    continue
+                e = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+                assert e <= Hp.TOL[w.dtype], (b, h, a, e)
+                err.add(got, ref)
+            assert err.value <= Hp.TOL[w.dtype]
+            i += 1
+
+
 def test_topk_one_keeps_the_argmax():
     w = Hp.CASES["bf16_ragged"].with_(topk=1)
     inp = Hp.gen(w)

@@ -420,6 +420,15 @@ def main():
                       "density": nnz / (w.B * w.H * w.T * w.T), "rank": w.rank, "linear_keys": args.linear_keys,
                       "parallelism": "single GPU"}}
     out.update(call_figures(w, ms, per, kern, nnz, args.linear_keys))
+    if "linear_state" in out:
+        # a library read of the same K and V bytes on this GPU, for scale: torch's
+        # sum over each tensor (rows past N included; FP8 codes summed as bytes)
+        kv = [x.view(torch.uint8) if x.element_size() == 1 else x for x in (d["k"], d["v"])]
+        rd = lambda: [x.sum(dtype=torch.int64 if x.dtype == torch.uint8 else torch.float32) for x in kv]
+        ms_sum, _ = time_calls(rd, 10, 3, stream)
+        nb = sum(x.numel() * x.element_size() for x in kv)
+        out["linear_state"]["torch_sum_kv"] = {"bytes": nb, "ms": ms_sum, "GBps": nb / (ms_sum * 1e-3) / 1e9,
+                                               "frac_hbm": nb / (ms_sum * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if not args.no_reuse:
         # Mask reuse: select once, then run the hybrid call on that CSR (the
         # streaming pass then computes the linear state only).  Same inputs,

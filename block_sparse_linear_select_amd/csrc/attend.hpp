@@ -790,7 +790,10 @@ __global__ __launch_bounds__(128, 2) void k_attend_fp8(AttendArgs a) {
           }
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][kb][0], s[qb][kb][1], 0, false);
+            // the low half first, the high half second: the word passed as the
+            // first step's untouched high half is overwritten, so it may be any
+            // register (the first input's own bits: no zero to materialise)
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][kb][0], s[qb][kb][1], __float_as_int(s[qb][kb][0]), false);
             wd = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][kb][2], s[qb][kb][3], wd, true);
             pf[qb][kb] = wd;
           }

@@ -420,6 +420,16 @@ def main():
                       "density": nnz / (w.B * w.H * w.T * w.T), "rank": w.rank, "linear_keys": args.linear_keys,
                       "parallelism": "single GPU"}}
     out.update(call_figures(w, ms, per, kern, nnz, args.linear_keys))
+    # the same call captured once in a HIP graph and replayed (a serving loop's
+    # way to call it: no launch gaps between the call's kernels)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    ms_g, per_g = time_calls(graph.replay, args.steps, args.warmup, stream)
+    out["graph_replay"] = {"ms_per_call": ms_g, **{"ms_" + k: v for k, v in percentiles(per_g).items()},
+                           "value": dense_equivalent_flops(w.N, w.d, w.H, w.B) / (ms_g * 1e-3) / 1e12}
+    log(f"  {args.steps} graph replays: {ms_g:.3f} ms/call")
+    del graph
     if "linear_state" in out:
         # a library read of the same K and V bytes on this GPU, for scale: torch's
         # sum over each tensor (rows past N included; FP8 codes summed as bytes)

@@ -59,7 +59,9 @@
  *     entries yields O_s = 0 for its queries.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises the host or copies device data to
- *     the host.  The library allocates no device memory: scratch space comes
+ *     the host, and a call enqueues kernel launches only (no memsets or
+ *     copies), so a stream capture of it (a HIP graph) replays the call; with
+ *     per-kernel timing on, it also records HIP events.  The library allocates no device memory: scratch space comes
  *     from the caller's workspace of at least hsa_attn_workspace_size()
  *     bytes, 256-byte aligned, which must stay untouched until the stream
  *     work completes.  Calls on different streams with separate workspaces

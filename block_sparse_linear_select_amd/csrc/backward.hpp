@@ -145,10 +145,10 @@ template <int RG> __device__ __forceinline__ int swz_kt(int row) {
   const int rr = row / (16 / RG);
   return 2 * (rr & (RG / 2 - 1)) + ((rr / (RG / 2)) & 1);
 }
-// dma_offsets with that swizzle.
-template <int RB>
+// dma_offsets with that swizzle (NW waves share the tile's loads).
+template <int RB, int NW = 2>
 __device__ __forceinline__ void dma_offsets_kt(int w, int lane, int* off) {
-  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / 2;
+  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / NW;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int lin = 1024 * (NI * w + i) + 16 * lane;
@@ -1188,164 +1188,30 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
   }
 }
 
-// bf16 sparse dV and dK (two launches, so that each holds half the
-// accumulators): one block per key tile = 2 waves x 32 keys, over the query
-// tiles that keep it (CSC).  Query-side tiles go global -> LDS by LDS-direct
-// loads, and so do the lse (and D) of the staged query tile, so that the loop
-// issues no other global loads: a global load issued behind an LDS-direct
-// load would, when its value is first used, wait for that load as well.
-//
-// dV: Q (row reads, S = Q K^T) and dO (transposing reads, dv += P^T dO); the
-// next Q loads during the dv step, the next dO during the S step.
+// bf16 sparse dV and dK in one launch: one block per key tile = 4 waves,
+// two per gradient (the dV waves hold K, the dK waves K and V, each the
+// accumulators of its 32 keys), over the query tiles that keep the key tile
+// (CSC).  The query-side tiles Q and dO are staged once per step for all four
+// waves instead of once per kernel: both in the layout that serves row reads
+// and transposing reads (dV reads Q by rows and dO transposed, dK reads Q and
+// dO by rows and Q transposed), both double-buffered, so the next query
+// tile's Q, dO, lse and D load during the whole step and one barrier per step
+// suffices.  Each wave's arithmetic is that of its gradient alone, in the same
+// order, so dV and dK are bitwise those of separate dV and dK passes.
 template <int D>
-__global__ __launch_bounds__(128, 2) void k_bwd_dv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
   constexpr int NKB = 2, NDB = D / 16;
-  constexpr int NI = 64 * RB / 1024 / 2;
-  __shared__ __align__(16) uint8_t Qs[64 * RB];
-  __shared__ __align__(16) uint8_t Tv[64 * RB];
-  __shared__ __align__(16) float Ls[64];
-
-  const int L = uniform(a.col_order[blockIdx.x]);
-  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
-  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)bh * a.N_pad * D;
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
-  const int nbytes = a.N * RB;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)K, 0, nbytes, kBufferFlags);
-  const i32x4_t qrs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.q) + base, nbytes);
-  const i32x4_t grs = make_rsrc_regs(reinterpret_cast<const bf16_t*>(a.dout) + base, nbytes);
-  const i32x4_t lrs = make_rsrc_regs(a.lse + (size_t)bh * a.N_pad, a.N * 4);  // rows >= N read as 0
-
-  int krow[NKB];
-  bool kvalid[NKB];
-  Frag<bf16_t> kf[NKB][D / 32];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
-    kvalid[kb] = krow[kb] < a.N;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)  // rows >= N read as zeros
-      kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-  }
-  f32x4 acc[NKB][NDB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (a.N < 0) { Qs[tid] = 0; Tv[tid] = 0; Ls[tid & 63] = 0.f; }
-  const int beg = a.col_ptr[(size_t)bh * a.T + kt];
-  const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
-  const float c2 = a.scale * kLog2e;
-  int roff[NI], toff[NI];
-  dma_offsets<RB, false>(w, lane, roff);
-  dma_offsets<RB, true>(w, lane, toff);
-  const int raddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
-  const int rowl = 4 * g + (l16 >> 2);
-  const int taddr = rowl * RB + 16 * swz_v<RG>(rowl) + 16 * ((l16 >> 1) & 1) + 8 * (l16 & 1);
-  int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
-  int row = __builtin_amdgcn_readlane(rowv, 0);
-  int nrow = __builtin_amdgcn_readlane(rowv, 1);
-  auto issue_q = [&](int r) {
-    dma_tile<RB>(qrs, r, roff, Qs, w);
-    if (w == 0) lds_dma4(lrs, Ls, r * 256 + 4 * lane);
-  };
-  if (beg < end) {
-    issue_q(row);
-    dma_tile<RB>(grs, row, toff, Tv, w);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-  }
-  for (int j = beg; j < end; ++j) {
-    const bool more = j + 1 < end;
-    Frag<bf16_t> bfr[NKB][2];  // P as B fragments over queries
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
-      f32x4 s[2][NKB];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qb = 2 * c + h2;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < D / 32; ++cc) {
-          Frag<bf16_t> qfr;
-          qfr.w = *reinterpret_cast<const u32x4*>(&Qs[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) mma(s[h2][kb], qfr, kf[kb][cc]);
-        }
-        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[16 * qb + 4 * g]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        // query rows >= N: Q, dO and lse read as zeros, so P = 1 meets a zero dO row
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[h2][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's share of the dO tile has landed
-    lds_barrier();                              // dO visible; both waves are done with Q and lse
-    if (more) issue_q(nrow);
-#pragma unroll
-    for (int jd = 0; jd < NDB; ++jd) {
-      const int ta = taddr ^ (32 * jd);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        Frag<bf16_t> tf;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Tv[ta + (32 * c + 16 * hh) * RB]));
-          const uint2 u = __builtin_bit_cast(uint2, t);
-          tf.w[2 * hh] = u.x;
-          tf.w[2 * hh + 1] = u.y;
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q and lse have landed
-    lds_barrier();                              // next Q visible; both waves are done with dO
-    if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
-      rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    if (more) dma_tile<RB>(grs, nrow, toff, Tv, w);
-    row = nrow;
-    nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
-  }
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    if (!kvalid[kb]) continue;
-    float* out = a.dv + base + (size_t)krow[kb] * D;
-#pragma unroll
-    for (int jd = 0; jd < NDB; ++jd) {
-      float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
-      x.x += acc[kb][jd][0]; x.y += acc[kb][jd][1]; x.z += acc[kb][jd][2]; x.w += acc[kb][jd][3];
-      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = x;
-    }
-  }
-}
-
-// dK: Q, double-buffered and read both by rows (S = Q K^T) and transposed
-// (dk += scale dS^T Q), so each query tile is staged once, and dO (row
-// reads, dP = dO V^T); lse and D come with Q.  The next Q loads during the
-// S/dP step, the next dO during the dk step.
-template <int D>
-__global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
-  constexpr int RB = 2 * D, RG = RB / 16;
-  constexpr int NKB = 2, NDB = D / 16;
-  constexpr int NI = 64 * RB / 1024 / 2;
+  constexpr int NW = 4;
+  constexpr int NI = 64 * RB / 1024 / NW;
   __shared__ __align__(16) uint8_t Qb[2][64 * RB];
-  __shared__ __align__(16) uint8_t Gs[64 * RB];
+  __shared__ __align__(16) uint8_t Gb[2][64 * RB];
   __shared__ __align__(16) float Ls[2][2][64];  // [buffer][lse, D][query]
 
   const int L = uniform(a.col_order[blockIdx.x]);
   const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int role = uniform(w >> 1), wk = w & 1;  // role 0: dV, 1: dK; wk: which 32 keys of the tile
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
@@ -1364,12 +1230,13 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
   Frag<bf16_t> kf[NKB][D / 32], vf[NKB][D / 32];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
+    krow[kb] = kt * 64 + 32 * wk + 16 * kb + l16;
     kvalid[kb] = krow[kb] < a.N;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
       kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-      vf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
+      vf[kb][c].w = role ? __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0)
+                         : u32x4{0u, 0u, 0u, 0u};
     }
   }
   f32x4 acc[NKB][NDB];
@@ -1378,90 +1245,26 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (a.N < 0) { Qb[0][tid] = 0; Qb[1][tid] = 0; Gs[tid] = 0; Ls[0][0][tid & 63] = 0.f; }
+  if (a.N < 0) { Qb[0][tid] = 0; Qb[1][tid] = 0; Gb[0][tid] = 0; Gb[1][tid] = 0; Ls[0][0][tid & 63] = 0.f; }
   const int beg = a.col_ptr[(size_t)bh * a.T + kt];
   const int end = (int)min((long)a.col_ptr[(size_t)bh * a.T + kt + 1], a.csc_cap);
   const float c2 = a.scale * kLog2e;
-  int qoff[NI], goff[NI];
-  dma_offsets_kt<RB>(w, lane, qoff);
-  dma_offsets<RB, false>(w, lane, goff);
-  const int qaddr = l16 * RB + 16 * (g ^ swz_kt<RG>(l16));
-  const int gaddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
+  int off[NI];  // Q and dO share the layout, hence the offsets
+  dma_offsets_kt<RB, NW>(w, lane, off);
+  const int raddr = l16 * RB + 16 * (g ^ swz_kt<RG>(l16));  // row reads
   const int rowl = 4 * g + (l16 >> 2);
-  const int taddr = rowl * RB + 16 * (((l16 >> 1) & 1) ^ swz_kt<RG>(rowl)) + 8 * (l16 & 1);
+  const int taddr = rowl * RB + 16 * (((l16 >> 1) & 1) ^ swz_kt<RG>(rowl)) + 8 * (l16 & 1);  // transposing reads
   int rowv = beg + lane < end ? a.row_idx[beg + lane] : 0;
   int row = __builtin_amdgcn_readlane(rowv, 0);
   int nrow = __builtin_amdgcn_readlane(rowv, 1);
-  auto issue_q = [&](int r, int buf) {
-    dma_tile<RB>(qrs, r, qoff, Qb[buf], w);
-    lds_dma4(srs, Ls[buf][w], r * 256 + 4 * lane);
+  auto issue = [&](int r, int buf) {
+    dma_tile<RB, NW>(qrs, r, off, Qb[buf], w);
+    dma_tile<RB, NW>(grs, r, off, Gb[buf], w);
+    if (w < 2) lds_dma4(srs, Ls[buf][w], r * 256 + 4 * lane);
   };
-  if (beg < end) {
-    issue_q(row, 0);
-    dma_tile<RB>(grs, row, goff, Gs, w);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-  }
-  for (int j = beg; j < end; ++j) {
-    const int cur = (j - beg) & 1;
-    const bool more = j + 1 < end;
-    if (more) issue_q(nrow, cur ^ 1);  // that buffer was last read by the previous dk step
-    const uint8_t* Qc = Qb[cur];
-    Frag<bf16_t> bfr[NKB][2];  // scale dS as B fragments over queries
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {  // query blocks 2c, 2c + 1 -> chunk c of the contraction over queries
-      f32x4 s[2][NKB], dp[2][NKB];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int qb = 2 * c + h2;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int cc = 0; cc < D / 32; ++cc) {
-          Frag<bf16_t> qfr, gfr;
-          qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(qaddr ^ (64 * cc)) + 16 * RB * qb]);
-          gfr.w = *reinterpret_cast<const u32x4*>(&Gs[(gaddr ^ (64 * cc)) + 16 * RB * qb]);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            mma(s[h2][kb], qfr, kf[kb][cc]);
-            mma(dp[h2][kb], gfr, vf[kb][cc]);
-          }
-        }
-        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        // query rows >= N read as zeros (Q, dO, lse, D), so P = 1 meets dP - D = 0: only
-        // the ragged last tile is guarded (a per-element guard compiles to a branch per
-        // element); the barrier keeps the exps of the two halves from piling up live
-        if (row * 64 + 64 <= a.N) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-              s[h2][kb][i] = p * (dp[h2][kb][i] - dv4[i]) * a.scale;
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-              s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
-    }
-    lds_barrier();  // both waves are done with dO
-    if (more) dma_tile<RB>(grs, nrow, goff, Gs, w);
+  // B fragments over queries of chunk c (query blocks 2c, 2c + 1) for the
+  // transposing product of transposed tile `tt`: acc[kb][jd] += tt^T-part x frag
+  auto tprod = [&](const uint8_t* tt, const Frag<bf16_t> (&bfr)[NKB][2]) {
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       const int ta = taddr ^ (32 * jd);
@@ -1470,7 +1273,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
         Frag<bf16_t> tf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&Qc[ta + (32 * c + 16 * hh) * RB]));
+          const s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(&tt[ta + (32 * c + 16 * hh) * RB]));
           const uint2 u = __builtin_bit_cast(uint2, t);
           tf.w[2 * hh] = u.x;
           tf.w[2 * hh + 1] = u.y;
@@ -1479,8 +1282,106 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
         for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q, lse, D and dO have landed
-    lds_barrier();                              // they are visible; both waves are done with this Q
+  };
+  if (beg < end) {
+    issue(row, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+  }
+  for (int j = beg; j < end; ++j) {
+    const int cur = (j - beg) & 1;
+    const bool more = j + 1 < end;
+    if (more) issue(nrow, cur ^ 1);  // that buffer was last read in the previous step
+    const uint8_t* Qc = Qb[cur];
+    const uint8_t* Gc = Gb[cur];
+    Frag<bf16_t> bfr[NKB][2];
+    if (role == 0) {
+      // dV += P^T dO, P = exp(scale q k^T - lse)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x4 s[2][NKB];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int qb = 2 * c + h2;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int cc = 0; cc < D / 32; ++cc) {
+            Frag<bf16_t> qfr;
+            qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma(s[h2][kb], qfr, kf[kb][cc]);
+          }
+          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          // query rows >= N: Q, dO and lse read as zeros, so P = 1 meets a zero dO row
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[h2][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
+      }
+      tprod(Gc, bfr);
+    } else {
+      // dK += scale dS^T q, dS = P (dP - D), dP = dO v^T
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x4 s[2][NKB], dp[2][NKB];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int qb = 2 * c + h2;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int cc = 0; cc < D / 32; ++cc) {
+            Frag<bf16_t> qfr, gfr;
+            qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+            gfr.w = *reinterpret_cast<const u32x4*>(&Gc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              mma(s[h2][kb], qfr, kf[kb][cc]);
+              mma(dp[h2][kb], gfr, vf[kb][cc]);
+            }
+          }
+          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          // query rows >= N read as zeros (Q, dO, lse, D), so P = 1 meets dP - D = 0: only
+          // the ragged last tile is guarded (a per-element guard compiles to a branch per
+          // element); the barrier keeps the exps of the two halves from piling up live
+          if (row * 64 + 64 <= a.N) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+                s[h2][kb][i] = p * (dp[h2][kb][i] - dv4[i]) * a.scale;
+              }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+                s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
+              }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
+      }
+      tprod(Qc, bfr);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q, dO, lse and D have landed
+    lds_barrier();                              // they are visible; every wave is done with this step's tiles
     if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
       rowv = j + 2 + lane < end ? a.row_idx[j + 2 + lane] : 0;
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1488,10 +1389,11 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dk_bf16(BwdArgs a) {
     row = nrow;
     nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
   }
+  float* outp = role ? a.dk : a.dv;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     if (!kvalid[kb]) continue;
-    float* out = a.dk + base + (size_t)krow[kb] * D;
+    float* out = outp + base + (size_t)krow[kb] * D;
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
@@ -1559,11 +1461,9 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   }
   if constexpr (sizeof(T) == 2) {
     if (s.d == 64) {
-      k_bwd_dv_bf16<64><<<rows, 128, 0, st>>>(a);
-      k_bwd_dk_bf16<64><<<rows, 128, 0, st>>>(a);
+      k_bwd_dkv_bf16<64><<<rows, 256, 0, st>>>(a);
     } else {
-      k_bwd_dv_bf16<128><<<rows, 128, 0, st>>>(a);
-      k_bwd_dk_bf16<128><<<rows, 128, 0, st>>>(a);
+      k_bwd_dkv_bf16<128><<<rows, 256, 0, st>>>(a);
     }
   } else {
     if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);

@@ -71,11 +71,12 @@ template <int RG> __device__ __forceinline__ int swz_k(int row) { return (row / 
 template <int RG> __device__ __forceinline__ int swz_v(int row) { return 2 * ((row / (16 / RG)) & (RG / 2 - 1)); }
 
 // One wave's share of the LDS-direct loads of a 64-row tile (RB bytes per
-// row): load i of wave w fills LDS bytes [1024 (NI w + i), +1024).
+// row) moved by NW waves: load i of wave w fills LDS bytes
+// [1024 (NI w + i), +1024) with NI = RB / (16 NW).
 // off[i] = the lane's byte offset within the tile of the granule it moves.
-template <int RB, bool V>
+template <int RB, bool V, int NW = 2>
 __device__ __forceinline__ void dma_offsets(int w, int lane, int* off) {
-  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / 2;
+  constexpr int RG = RB / 16, NI = 64 * RB / 1024 / NW;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int lin = 1024 * (NI * w + i) + 16 * lane;
@@ -84,9 +85,9 @@ __device__ __forceinline__ void dma_offsets(int w, int lane, int* off) {
     off[i] = row * RB + 16 * gr;
   }
 }
-template <int RB>
+template <int RB, int NW = 2>
 __device__ __forceinline__ void dma_tile(const i32x4_t& rs, int col, const int* off, uint8_t* dst, int w) {
-  constexpr int NI = 64 * RB / 1024 / 2;
+  constexpr int NI = 64 * RB / 1024 / NW;
   const int base = col * 64 * RB;  // out-of-range columns fall outside the buffer and load zeros
   static_for<0, NI>([&](auto ic) {
     constexpr int i = decltype(ic)::value;

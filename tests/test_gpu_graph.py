@@ -73,3 +73,42 @@ def test_reused_mask_call_replays_from_a_graph():
         g.replay()
         torch.cuda.synchronize()
         _same(plan.o, o_ref, f"replay {rep}")
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "f32_d128_r64"])
+def test_training_step_replays_from_a_graph(name):
+    """A training step captured whole: the forward that selects its mask and
+    saves the sparse statistics, then the backward on them."""
+    from workloads.gen import upstream_grad
+    print(f"\n[case {name}]", flush=True)
+    w = Hp.CASES[name]
+    d = Hp.to_device(Hp.gen(w), DEV)
+    cfg = B.Config.from_workload(w)
+    go = upstream_grad(w, seed=w.seed + 3).to(DEV)
+    par = (d["q"], d["k"], d["v"], d["uq"], d["uk"], d["wo"])
+
+    def step():
+        o, o_s, lse, rp, ci = B.hybrid_attn_train(cfg, *par, export_mask=True)
+        grads = B.hybrid_attn_backward_saved(cfg, *par, rp, ci, o_s, lse, go)
+        return (o, o_s, lse, rp, ci) + tuple(grads)
+
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    n = int(ref[3][-1])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step()
+    names = ("o", "o_s", "lse", "row_ptr", "col_idx", "dq", "dk", "dv")
+    for rep in range(3):
+        for t in out:
+            t.view(torch.uint8).fill_(0xFF)
+        step()  # the program's own eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for nm, x, y in zip(names, out, ref):
+            if nm == "lse":  # rows >= N are undefined
+                x, y = x[:, :, : w.N], y[:, :, : w.N]
+            if nm == "col_idx":
+                x, y = x[:n], y[:n]
+            _same(x, y, f"replay {rep}: {nm}")
+    print("  3 replays bitwise equal to the eager step", flush=True)

@@ -757,8 +757,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   constexpr int GST = D + 4, QST = R + 4;       // LDS row strides (floats)
   constexpr int NB = NDB * NRB, NBW = NB / 4;    // 16x16 blocks of dS^T, per wave
   static_assert(NB % 4 == 0, "dS blocks per wave");
+  // bf16 operands: q' of the tile's queries is kept in LDS as the bf16 values
+  // the dS product packs it to (float operands keep floats), and the head's
+  // W_o^T fragments (32 KB at d = 128) are staged once per block, so that the
+  // gW step reads them from LDS instead of from L2 for every tile and wave
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int QSTB = R + 8;                    // bf16 q' row stride (elements)
   __shared__ __align__(16) float GN[64 * GST];
-  __shared__ __align__(16) float QP[64 * QST];
+  __shared__ __align__(16) float QP[BF ? 4 : 64 * QST];
+  __shared__ __align__(16) uint16_t QPB[BF ? 64 * QSTB : 8];
+  __shared__ __align__(16) T WOS[BF ? D * D : 8];
   __shared__ float zred[4][R];
 
   // XCD-aware order: the hardware hands block i to XCD i % 8; all chunks of
@@ -783,6 +791,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   const float* SF = a.s_frag + (size_t)bh * NFE;
   const float* SPF = a.s_pfrag + (size_t)bh * R * D;
   const float* Z = a.z + (size_t)bh * R;
+  if constexpr (BF) {
+    for (int i = tid; i < D * D / 8; i += 256)
+      reinterpret_cast<u32x4*>(WOS)[i] = reinterpret_cast<const u32x4*>(WOB)[i];
+    __syncthreads();
+  }
 
   f32x4 dsacc[NBW];
 #pragma unroll
@@ -852,8 +865,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
           qp[rb][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
         }
         // q' of the tile's queries for the dS product (the previous tile's product is done)
-        *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =
-            make_float4(qp[rb][0], qp[rb][1], qp[rb][2], qp[rb][3]);
+        if constexpr (BF)
+          *reinterpret_cast<uint2*>(&QPB[ql * QSTB + 16 * rb + 4 * g]) =
+              make_uint2(pack_bf16x2(qp[rb][0], qp[rb][1]), pack_bf16x2(qp[rb][2], qp[rb][3]));
+        else
+          *reinterpret_cast<float4*>(&QP[ql * QST + 16 * rb + 4 * g]) =
+              make_float4(qp[rb][0], qp[rb][1], qp[rb][2], qp[rb][3]);
       }
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
@@ -879,7 +896,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
         for (int cc = 0; cc < D / 32; ++cc) {
           Frag<T> wf;
-          load8(wf, WOB + ((size_t)(jd * (D / 32) + cc) * 64 + lane) * 8);
+          if constexpr (BF) load8(wf, WOS + ((jd * (D / 32) + cc) * 64 + lane) * 8);
+          else load8(wf, WOB + ((size_t)(jd * (D / 32) + cc) * 64 + lane) * 8);
           mma(gw[hh], wf, gf[cc]);
         }
         *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
@@ -973,17 +991,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
       const int bi = w + 4 * ii, je = bi % NDB, rb = bi / NDB;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float x[8], y[8];
+        float x[8];
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-          const int qq = 32 * c + 8 * g + s2;
-          x[s2] = GN[qq * GST + 16 * je + l16];
-          y[s2] = QP[qq * QST + 16 * rb + l16];
-        }
+        for (int s2 = 0; s2 < 8; ++s2) x[s2] = GN[(32 * c + 8 * g + s2) * GST + 16 * je + l16];
         Frag<T> hi, lo, qb;
         split8(x, hi, lo);
+        if constexpr (BF) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) qb.set_pair(p, y[2 * p], y[2 * p + 1]);
+          for (int p = 0; p < 4; ++p) {
+            const int qq = 32 * c + 8 * g + 2 * p;
+            qb.w[p] = (uint32_t)QPB[qq * QSTB + 16 * rb + l16] | ((uint32_t)QPB[(qq + 1) * QSTB + 16 * rb + l16] << 16);
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int qq = 32 * c + 8 * g + 2 * p;
+            qb.set_pair(p, QP[qq * QST + 16 * rb + l16], QP[(qq + 1) * QST + 16 * rb + l16]);
+          }
+        }
         mma_hl(dsacc[ii], hi, lo, qb);
       }
     }

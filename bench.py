@@ -309,6 +309,41 @@ def call_figures(w, ms, per, kern, nnz, linear_keys="all"):
     }
 
 
+def bench_locality(w, cfg, d, sc, sel, args, dev):
+    """The sparse attend kernel alone (hsa_sparse_attn) on the selected mask and
+    on three masks of the same size and the same k tiles per row that differ
+    only in which key tiles the rows share: every row the same k tiles (they
+    stay in L2), a band of k consecutive tiles around the row, and k tiles
+    drawn uniformly per row.  Shows how much of the kernel's time depends on
+    key tiles being re-fetched from memory."""
+    import torch
+    from block_sparse_linear_select_amd import binding as B
+    T, k, bh = w.T, w.topk, w.B * w.H
+    a = torch.arange(T)
+    g = torch.Generator().manual_seed(1234)
+    masks = {
+        "selected": None,
+        "same_tiles": torch.arange(k).repeat(T, 1),
+        "band": (a - k // 2).clamp(0, T - k)[:, None] + torch.arange(k)[None, :],
+        "uniform_random": torch.stack([torch.randperm(T, generator=g)[:k].sort().values for _ in range(T)]),
+    }
+    rp = (torch.arange(bh * T + 1, dtype=torch.int32) * k).to(dev)
+    res = {}
+    for name, m in masks.items():
+        if m is None:
+            row_ptr, col_idx = sel.row_ptr, sel.col_idx
+        else:
+            row_ptr, col_idx = rp, m.to(torch.int32).repeat(bh, 1).reshape(-1).contiguous().to(dev)
+        run = lambda: B.sparse_attn(cfg, d["q"], d["k"], d["v"], row_ptr, col_idx, sc["q_scale"], sc["k_scale"],
+                                    sc["v_scale"])
+        for _ in range(args.warmup):
+            run()
+        kern = kernel_split(run, min(args.steps, 20))
+        res[name] = {"attend_ms": kern["attend"]}
+        log(f"  sparse attend on the {name} mask: {kern['attend']:.3f} ms")
+    return res
+
+
 def bench_second_workload(name, args, dev):
     """Another workload of the same shape (the FP8 one), timed the same way:
     whole calls with p50/p95, the kernel split, and its roofline."""
@@ -362,6 +397,9 @@ def main():
                          "of each row's kept tiles")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the fifth measurement: the backward pass (dQ, dK, dV) on the selected mask")
+    ap.add_argument("--no-locality", action="store_true",
+                    help="skip the sparse attend kernel on masks of the same size with shared, banded and uniformly "
+                         "drawn key tiles")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warmup, run 3 launches of a plain elementwise kernel that reads and writes MIB "
                          "MiB each (reference for HBM byte counters)")
@@ -439,6 +477,17 @@ def main():
         nb = sum(x.numel() * x.element_size() for x in kv)
         out["linear_state"]["torch_sum_kv"] = {"bytes": nb, "ms": ms_sum, "GBps": nb / (ms_sum * 1e-3) / 1e9,
                                                "frac_hbm": nb / (ms_sum * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        # the read rate of a plain streaming kernel over the same two tensors
+        # (the library's calibration read), the practical ceiling of the pass
+        sink = torch.empty(B.READ_SINK_WORDS, dtype=torch.int32, device=dev)
+        ms_rd = 0.0
+        for x in (d["k"], d["v"]):  # one launch per timed call, events around it
+            ms_rd += percentiles(time_calls(lambda: B.read_calibrate(x, sink), 20, 5, stream)[1])["p50"]
+        ceil = nb / (ms_rd * 1e-3) / 1e9
+        out["linear_state"]["read_ceiling"] = {"kernel": "hsa_attn_read_calibrate over K and V", "bytes": nb,
+                                               "ms": ms_rd, "GBps": ceil, "frac_hbm": ceil / PEAK_HBM_GBS}
+        out["linear_state"]["kv_frac_read_ceiling"] = out["linear_state"]["kv_GBps"] / ceil
+        log(f"  read ceiling {ceil:.0f} GB/s; streaming pass {out['linear_state']['kv_GBps']:.0f} GB/s")
     if not args.no_reuse:
         # Mask reuse: select once, then run the hybrid call on that CSR (the
         # streaming pass then computes the linear state only).  Same inputs,
@@ -451,6 +500,16 @@ def main():
         out["mask_reuse"] = {"ms_per_call": ms_r, **{"ms_" + k: v for k, v in percentiles(per_r).items()},
                              "value": dense_equivalent_flops(w.N, w.d, w.H, w.B) / (ms_r * 1e-3) / 1e12,
                              "kernels_ms": kern_r}
+        if "linear_state" in out:
+            # on a given mask the streaming pass is the state reduction alone (no key pooling)
+            ls = out["linear_state"]
+            gbs = ls["kv_bytes"] / (kern_r["stream"] * 1e-3) / 1e9
+            ls["state_only"] = {"kernel": "k_stream without pooling (calls on a given mask)", "ms": kern_r["stream"],
+                                "kv_GBps": gbs, "kv_frac_hbm": gbs / PEAK_HBM_GBS}
+            if "read_ceiling" in ls:
+                ls["state_only"]["kv_frac_read_ceiling"] = gbs / ls["read_ceiling"]["GBps"]
+    if not args.no_locality and args.linear_keys == "all":
+        out["attend_locality"] = bench_locality(w, cfg, d, sc, sel, args, dev)
     if not args.no_proj and w.d == 128:
         out["qkv_proj"] = bench_proj(w, args, dev)
     if not args.no_bwd and w.dtype != "fp8" and args.linear_keys == "all":

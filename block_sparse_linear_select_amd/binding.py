@@ -22,7 +22,7 @@ CALL_BLOCK_SELECT, CALL_SPARSE, CALL_LINEAR, CALL_HYBRID, CALL_LINEAR_COMPLEMENT
 ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "WORKSPACE", -5: "CSR", -6: "HIP"}
 
 EXPORTED = ["hsa_attn_workspace_size", "hsa_attn_last_error", "hsa_attn_version",
-            "hsa_attn_timing_enable", "hsa_attn_timing_read",
+            "hsa_attn_timing_enable", "hsa_attn_timing_read", "hsa_attn_read_calibrate",
             "hsa_block_select", "hsa_sparse_attn", "hsa_linear_attn", "hsa_linear_attn_complement",
             "hsa_hybrid_attn", "hsa_hybrid_attn_noalloc", "hsa_hybrid_attn_train", "hsa_hybrid_attn_backward",
             "hsa_hybrid_attn_backward_saved",
@@ -82,6 +82,7 @@ def lib():
         L.hsa_qkv_proj_fp8.argtypes = [vp, f32p, vp, f32p, i32, i32, i32, i32, i32, vp, vp, vp, f32p, f32p, f32p, vp]
         L.hsa_attn_timing_enable.argtypes = [ctypes.c_int]
         L.hsa_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+        L.hsa_attn_read_calibrate.argtypes = [vp, sz, vp, sz, vp]
         for name in EXPORTED:
             if name not in ("hsa_attn_last_error", "hsa_attn_version"):
                 getattr(L, name).restype = ctypes.c_int
@@ -392,6 +393,19 @@ def timing_read() -> dict:
     cnt = (ctypes.c_int32 * n)()
     _check(lib().hsa_attn_timing_read(ms, cnt))
     return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+READ_SINK_WORDS = 2048 * 256
+
+
+def read_calibrate(buf: torch.Tensor, sink: torch.Tensor):
+    """One plain streaming read of the bytes of `buf` (a multiple of 16) into
+    one word per thread of `sink` (int32, at least READ_SINK_WORDS): the read
+    rate of a simple kernel on this GPU, not part of the attention."""
+    if not buf.is_cuda or not sink.is_cuda or sink.dtype != torch.int32:
+        raise ValueError("buf must be a device tensor and sink a device int32 tensor")
+    _check(lib().hsa_attn_read_calibrate(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
+                                         _stream()))
 
 
 def version() -> str:

@@ -280,6 +280,19 @@ HSA_API int hsa_attn_timing_enable(int max_launches) {
   return HSA_ATTN_OK;
 }
 
+HSA_API int hsa_attn_read_calibrate(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                                    void* stream) {
+  if (!buf || !sink) return fail(HSA_ATTN_ERR_NULL, "read_calibrate: buf and sink are required");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(HSA_ATTN_ERR_SHAPE, "read_calibrate: bytes=%zu must be a positive multiple of 16", bytes);
+  if (sink_words < (size_t)HSA_ATTN_READ_SINK_WORDS)
+    return fail(HSA_ATTN_ERR_SHAPE, "read_calibrate: sink holds %zu words, %d are needed", sink_words,
+                HSA_ATTN_READ_SINK_WORDS);
+  hipError_t e = hsa::launch_read_calibrate(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read calibration");
+  return HSA_ATTN_OK;
+}
+
 HSA_API int hsa_attn_timing_read(double* ms_out, int32_t* launches_out) {
   if (!ms_out || !launches_out) return fail(HSA_ATTN_ERR_NULL, "ms_out and launches_out are required");
   std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -350,7 +350,8 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
 #pragma unroll 4
         for (int c2 = 0; c2 < NCONT; ++c2) sum += red[c2 * D + tid];
         if constexpr (SCALED) sum *= (double)a.qs[tb + at];
-        const double mean = sum / (double)min(64, a.N - at * 64);
+        const int cnt = min(64, a.N - at * 64);  // a full tile: exactly a multiply by 2^-6
+        const double mean = cnt == 64 ? sum * 0.015625 : sum / (double)cnt;
         const size_t o = (tb + at) * D + tid;
         a.qmean[o] = mean;
         if (a.qbar_out) a.qbar_out[o] = mean;

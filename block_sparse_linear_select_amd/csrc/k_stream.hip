@@ -52,4 +52,37 @@ hipError_t launch_vtranspose(const Shape& s, const void* v, const Scratch& w, hi
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- read calibration
+// A plain streaming read of a device buffer: 16-byte loads, eight per thread
+// in flight, grid-stride, folded into one word per thread.  It reaches the
+// read rate a simple kernel gets from this GPU's memory, the practical
+// ceiling against which the streaming pass (one read of K and V) is measured.
+static __global__ __launch_bounds__(256) void k_read_calibrate(const u32x4* __restrict__ p, size_t n,
+                                                                uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * 256 < n; i += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  // the group that does not fit whole (every later group starts past n)
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i + u * 256 < n) {
+      const u32x4 t = p[i + u * 256];
+      acc ^= t[0] ^ t[1] ^ t[2] ^ t[3];
+    }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+hipError_t launch_read_calibrate(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  k_read_calibrate<<<kReadCalibrateBlocks, 256, 0, st>>>(reinterpret_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace hsa

@@ -141,6 +141,8 @@ Scratch bind_plan(const Plan& p, void* ws);
 
 // Launchers: each enqueues its kernels on `st` and returns hipSuccess or the
 // launch error.
+constexpr int kReadCalibrateBlocks = 2048;  // blocks of 256 threads: one sink word per thread
+hipError_t launch_read_calibrate(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_rope_table(const Shape& s, float2* tab, hipStream_t st);
 hipError_t launch_stream_pass(const Shape& s, const void* q, const void* k, const void* v,
                               const float* qs, const float* ks, const float* vs,

@@ -442,7 +442,9 @@ __global__ __launch_bounds__(256, 2) void k_stream(StreamArgs a) {
   #pragma unroll
           for (int c = 0; c < NCONT; ++c) sum += redk[c * D + tid];
           if constexpr (SCALED) sum *= (double)tsk;
-          const double mean = sum / (double)min(64, a.N - t * 64);
+          // a full tile divides by 64, exactly a multiply by 2^-6
+          const int cnt = min(64, a.N - t * 64);
+          const double mean = cnt == 64 ? sum * 0.015625 : sum / (double)cnt;
           const size_t o = ((size_t)bh * a.T + t) * D + tid;  // one 1 KB row per tile
           a.kmean[o] = mean;
           if (a.kbar_out) a.kbar_out[o] = mean;

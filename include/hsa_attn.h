@@ -167,6 +167,18 @@ int hsa_attn_timing_enable(int max_launches);
 int hsa_attn_timing_read(double* ms_out, int32_t* launches_out);
 
 /*
+ * Read-rate calibration (a measurement aid, not part of the attention): reads
+ * `bytes` (a positive multiple of 16) from the device buffer `buf` once with
+ * 16-byte loads and writes one XOR-folded word per thread into the device
+ * array `sink` (at least HSA_ATTN_READ_SINK_WORDS words, caller-owned).  Its
+ * duration gives the read rate a plain streaming kernel reaches from this
+ * GPU's memory, the practical ceiling for the streaming pass over K and V.
+ * Asynchronous on `stream`; errors: NULL, SHAPE (nothing launched), HIP.
+ */
+#define HSA_ATTN_READ_SINK_WORDS (2048 * 256)
+int hsa_attn_read_calibrate(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+
+/*
  * Tile selection (SparkDiffusion news article, section 05: the sparse branch
  * keeps the high-energy query/key tile interactions; section 01: 90% / 97% of
  * the tiles are skipped, here a fixed top-k per query-tile row).  Mean-pool Q

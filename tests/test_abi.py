@@ -195,3 +195,16 @@ def test_training_forward_and_saved_backward_arguments():
     rc = L.hsa_hybrid_attn_backward_saved(ctypes.byref(dc), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                           fake, fake, fake, fake, fake, fake, need, None)
     assert rc == -2
+
+
+def test_read_calibration_arguments():
+    """The read-rate calibration validates its arguments before any launch."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: every case below is rejected first
+    assert L.hsa_attn_read_calibrate(None, 1 << 20, fake, B.READ_SINK_WORDS, None) == -1
+    assert L.hsa_attn_read_calibrate(fake, 1 << 20, None, B.READ_SINK_WORDS, None) == -1
+    assert L.hsa_attn_read_calibrate(fake, 0, fake, B.READ_SINK_WORDS, None) == -2
+    assert L.hsa_attn_read_calibrate(fake, (1 << 20) + 8, fake, B.READ_SINK_WORDS, None) == -2
+    assert L.hsa_attn_read_calibrate(fake, 1 << 20, fake, B.READ_SINK_WORDS - 1, None) == -2
+    assert b"sink" in L.hsa_attn_last_error()

@@ -298,12 +298,12 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
   constexpr int POOL_BYTES = NCONT * D * 8;  // pooling partials (float64)
   constexpr int QF_BYTES = 2 * kSelRows * D * 2;
   constexpr int SC_BYTES = kSelRows * TP * 4;
-  constexpr int SMEM = (POOL_BYTES + QF_BYTES > SC_BYTES) ? POOL_BYTES + QF_BYTES : SC_BYTES;
+  constexpr int SMEM = (2 * POOL_BYTES + QF_BYTES > SC_BYTES) ? 2 * POOL_BYTES + QF_BYTES : SC_BYTES;
   constexpr bool SCALED = sizeof(IT) == 1;
   __shared__ __align__(16) uint8_t smem[SMEM];
   __shared__ float emax[4][kSelRows];
   double* red = reinterpret_cast<double*>(smem);
-  uint16_t* qh = reinterpret_cast<uint16_t*>(smem + POOL_BYTES);  // [16][D]
+  uint16_t* qh = reinterpret_cast<uint16_t*>(smem + 2 * POOL_BYTES);  // [16][D]
   uint16_t* ql = qh + kSelRows * D;
   float* sc = reinterpret_cast<float*>(smem);  // [16][TP], once the pooling is done
 
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
   const int nr = min(kSelRows, T - a0);
   const size_t tb = (size_t)bh * T;
 
-  // ---- 1. pooling of the block's query tiles (two tiles of loads in flight)
+  // ---- 1. pooling of the block's query tiles (four tiles of loads in flight, two reduced per round)
   {
     const IT* Q = reinterpret_cast<const IT*>(a.q) + (size_t)bh * a.N_pad * D;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, a.N * D * (int)sizeof(IT));
@@ -332,7 +332,9 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
 #pragma unroll
       for (int i = 0; i < KCH; ++i) bload8(cq[slot][i], qrs, (t * 64 + row0 + i * NCONT) * D + col8 * 8);
     };
-    auto reduce = [&](int r, int slot) {
+    // partial column sums of the tile in register slot `slot` into partial
+    // region h; the slot then loads the tile four ahead
+    auto partials = [&](int r, int slot, int h) {
       double p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = 0.0;
@@ -342,32 +344,39 @@ __global__ __launch_bounds__(256, 2) void k_select(SelectArgs a) {
         for (int e = 0; e < 8; ++e) p[e] += (double)elem(cq[slot][i], e);
       load(r + 4, slot);  // the registers are free again: the tile four ahead
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[row0 * D + col8 * 8 + e] = p[e];
+      for (int e = 0; e < 8; ++e) red[h * NCONT * D + row0 * D + col8 * 8 + e] = p[e];
+    };
+    // two tiles per round (r and r + 1, slots s0 and s0 + 1): one barrier
+    // publishes both tiles' partials, and threads tid < 2 D finish the means
+    // of both, column tid % D of tile r + tid / D
+    auto reduce2 = [&](int r, int s0) {
+      partials(r, s0, 0);
+      if (r + 1 < nr) partials(r + 1, s0 + 1, 1);
       __syncthreads();
-      if (tid < D) {
-        const int at = a0 + r;
+      const int h = tid / D, col = tid % D;
+      if (h < 2 && r + h < nr) {
+        const int at = a0 + r + h;
+        const double* rh = red + h * NCONT * D;
         double sum = 0.0;
 #pragma unroll 4
-        for (int c2 = 0; c2 < NCONT; ++c2) sum += red[c2 * D + tid];
+        for (int c2 = 0; c2 < NCONT; ++c2) sum += rh[c2 * D + col];
         if constexpr (SCALED) sum *= (double)a.qs[tb + at];
         const int cnt = min(64, a.N - at * 64);  // a full tile: exactly a multiply by 2^-6
         const double mean = cnt == 64 ? sum * 0.015625 : sum / (double)cnt;
-        const size_t o = (tb + at) * D + tid;
+        const size_t o = (tb + at) * D + col;
         a.qmean[o] = mean;
         if (a.qbar_out) a.qbar_out[o] = mean;
         const uint32_t hb = bf16_of(mean);
-        qh[r * D + tid] = (uint16_t)hb;
-        ql[r * D + tid] = (uint16_t)bf16_of(mean - bf16_value(hb));
+        qh[(r + h) * D + col] = (uint16_t)hb;
+        ql[(r + h) * D + col] = (uint16_t)bf16_of(mean - bf16_value(hb));
       }
       __syncthreads();
     };
 #pragma unroll
     for (int i = 0; i < 4; ++i) load(i, i);
     for (int r = 0; r < nr; r += 4) {
-      reduce(r, 0);
-      if (r + 1 < nr) reduce(r + 1, 1);
-      if (r + 2 < nr) reduce(r + 2, 2);
-      if (r + 3 < nr) reduce(r + 3, 3);
+      reduce2(r, 0);
+      if (r + 2 < nr) reduce2(r + 2, 2);
     }
     for (int i = tid; i < (kSelRows - nr) * D; i += 256) {  // rows past T: zero operands
       qh[nr * D + i] = 0;

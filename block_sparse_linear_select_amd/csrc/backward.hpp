@@ -1213,20 +1213,21 @@ __global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
   }
 }
 
-// bf16 sparse dV and dK in one launch: one block per key tile = 4 waves,
-// two per gradient (the dV waves hold K, the dK waves K and V, each the
-// accumulators of its 32 keys), over the query tiles that keep the key tile
-// (CSC).  The query-side tiles Q and dO are staged once per step for all four
-// waves instead of once per kernel: both in the layout that serves row reads
-// and transposing reads (dV reads Q by rows and dO transposed, dK reads Q and
-// dO by rows and Q transposed), both double-buffered, so the next query
-// tile's Q, dO, lse and D load during the whole step and one barrier per step
-// suffices.  Each wave's arithmetic is that of its gradient alone, in the same
-// order, so dV and dK are bitwise those of separate dV and dK passes.
+// bf16 sparse dV and dK in one launch: one block per key tile = 4 waves, each
+// holding K and V of its 16 keys and the accumulators of both gradients, over
+// the query tiles that keep the key tile (CSC).  Per query tile a wave forms
+// S = q k^T and dP = dO v^T, P = exp(scale S - lse) and dS = P (dP - D) scale,
+// and adds P^T dO to dV and dS^T q to dK, so the scores and their
+// exponentials are computed once per kept pair.  The query-side tiles Q and
+// dO are staged once per step for all four waves: both in the layout that
+// serves row reads and transposing reads (Q and dO by rows for S and dP,
+// both transposed for the two gradient products), both double-buffered, so
+// the next query tile's Q, dO, lse and D load during the whole step and one
+// barrier per step suffices.
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
-  constexpr int NKB = 2, NDB = D / 16;
+  constexpr int NDB = D / 16;
   constexpr int NW = 4;
   constexpr int NI = 64 * RB / 1024 / NW;
   __shared__ __align__(16) uint8_t Qb[2][64 * RB];
@@ -1236,7 +1237,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   const int L = uniform(a.col_order[blockIdx.x]);
   const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int role = uniform(w >> 1), wk = w & 1;  // role 0: dV, 1: dK; wk: which 32 keys of the tile
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + base;
@@ -1250,25 +1250,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
   const i32x4_t srs = make_rsrc_regs(w == 0 ? (const float*)a.lse + (size_t)bh * a.N_pad
                                             : (const float*)a.dsum + (size_t)bh * a.N_pad, a.N * 4);
 
-  int krow[NKB];
-  bool kvalid[NKB];
-  Frag<bf16_t> kf[NKB][D / 32], vf[NKB][D / 32];
+  const int krow = kt * 64 + 16 * w + l16;
+  const bool kvalid = krow < a.N;
+  Frag<bf16_t> kf[D / 32], vf[D / 32];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    krow[kb] = kt * 64 + 32 * wk + 16 * kb + l16;
-    kvalid[kb] = krow[kb] < a.N;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
-      kf[kb][c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0);
-      vf[kb][c].w = role ? __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow[kb] * D + 32 * c + 8 * g) * 2, 0, 0)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
+    kf[c].w = __builtin_amdgcn_raw_buffer_load_b128(krs, (krow * D + 32 * c + 8 * g) * 2, 0, 0);
+    vf[c].w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (krow * D + 32 * c + 8 * g) * 2, 0, 0);
   }
-  f32x4 acc[NKB][NDB];
+  f32x4 accv[NDB], acck[NDB];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int j = 0; j < NDB; ++j) acc[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NDB; ++j) {
+    accv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acck[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (a.N < 0) { Qb[0][tid] = 0; Qb[1][tid] = 0; Gb[0][tid] = 0; Gb[1][tid] = 0; Ls[0][0][tid & 63] = 0.f; }
   const int beg = a.col_ptr[(size_t)bh * a.T + kt];
@@ -1287,9 +1282,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
     dma_tile<RB, NW>(grs, r, off, Gb[buf], w);
     if (w < 2) lds_dma4(srs, Ls[buf][w], r * 256 + 4 * lane);
   };
-  // B fragments over queries of chunk c (query blocks 2c, 2c + 1) for the
-  // transposing product of transposed tile `tt`: acc[kb][jd] += tt^T-part x frag
-  auto tprod = [&](const uint8_t* tt, const Frag<bf16_t> (&bfr)[NKB][2]) {
+  // acc[jd] += (transposed tile tt)^T-part x B fragments over the 32 queries of chunk c
+  auto tprod = [&](const uint8_t* tt, const Frag<bf16_t> (&bfr)[2], f32x4 (&acc)[NDB]) {
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
       const int ta = taddr ^ (32 * jd);
@@ -1303,8 +1297,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
           tf.w[2 * hh] = u.x;
           tf.w[2 * hh + 1] = u.y;
         }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) mma(acc[kb][jd], tf, bfr[kb][c]);
+        mma(acc[jd], tf, bfr[c]);
       }
     }
   };
@@ -1319,92 +1312,47 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
     if (more) issue(nrow, cur ^ 1);  // that buffer was last read in the previous step
     const uint8_t* Qc = Qb[cur];
     const uint8_t* Gc = Gb[cur];
-    Frag<bf16_t> bfr[NKB][2];
-    if (role == 0) {
-      // dV += P^T dO, P = exp(scale q k^T - lse)
+    Frag<bf16_t> pfr[2], dsfr[2];
+    const bool full = row * 64 + 64 <= a.N;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x4 s[2][NKB];
+    for (int c = 0; c < 2; ++c) {
+      f32x4 p[2], ds[2];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int qb = 2 * c + h2;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int qb = 2 * c + h2;
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int cc = 0; cc < D / 32; ++cc) {
-            Frag<bf16_t> qfr;
-            qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) mma(s[h2][kb], qfr, kf[kb][cc]);
-          }
-          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          // query rows >= N: Q, dO and lse read as zeros, so P = 1 meets a zero dO row
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[h2][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
+        for (int cc = 0; cc < D / 32; ++cc) {
+          Frag<bf16_t> qfr, gfr;
+          qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+          gfr.w = *reinterpret_cast<const u32x4*>(&Gc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
+          mma(s, qfr, kf[cc]);
+          mma(dp, gfr, vf[cc]);
         }
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        // query rows >= N read as zeros (Q, dO, lse, D): P = 1 meets a zero dO row in dV,
+        // and dS is zeroed there explicitly (only the ragged last tile takes the guard)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
-      }
-      tprod(Gc, bfr);
-    } else {
-      // dK += scale dS^T q, dS = P (dP - D), dP = dO v^T
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x4 s[2][NKB], dp[2][NKB];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int qb = 2 * c + h2;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            s[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dp[h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-          for (int cc = 0; cc < D / 32; ++cc) {
-            Frag<bf16_t> qfr, gfr;
-            qfr.w = *reinterpret_cast<const u32x4*>(&Qc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-            gfr.w = *reinterpret_cast<const u32x4*>(&Gc[(raddr ^ (64 * cc)) + 16 * RB * qb]);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-              mma(s[h2][kb], qfr, kf[kb][cc]);
-              mma(dp[h2][kb], gfr, vf[kb][cc]);
-            }
-          }
-          const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][0][16 * qb + 4 * g]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&Ls[cur][1][16 * qb + 4 * g]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-          // query rows >= N read as zeros (Q, dO, lse, D), so P = 1 meets dP - D = 0: only
-          // the ragged last tile is guarded (a per-element guard compiles to a branch per
-          // element); the barrier keeps the exps of the two halves from piling up live
-          if (row * 64 + 64 <= a.N) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-                s[h2][kb][i] = p * (dp[h2][kb][i] - dv4[i]) * a.scale;
-              }
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const bool ok = row * 64 + 16 * qb + 4 * g + i < a.N;
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[h2][kb][i], c2, -lv[i] * kLog2e));
-                s[h2][kb][i] = ok ? p * (dp[h2][kb][i] - dv4[i]) * a.scale : 0.f;
-              }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[i] * kLog2e));
+          p[h2][i] = e;
+          ds[h2][i] = e * (dp[i] - dv4[i]) * a.scale;
         }
+        if (!full) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) pack_rows(bfr[kb][c], s[0][kb], s[1][kb], 1.f);
+          for (int i = 0; i < 4; ++i)
+            if (row * 64 + 16 * qb + 4 * g + i >= a.N) ds[h2][i] = 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      tprod(Qc, bfr);
+      pack_rows(pfr[c], p[0], p[1], 1.f);
+      pack_rows(dsfr[c], ds[0], ds[1], 1.f);
     }
+    tprod(Gc, pfr, accv);   // dV += P^T dO
+    tprod(Qc, dsfr, acck);  // dK += dS^T q
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's shares of the next Q, dO, lse and D have landed
     lds_barrier();                              // they are visible; every wave is done with this step's tiles
     if (((j + 2 - beg) & 63) == 0 && j + 2 < end) {
@@ -1414,16 +1362,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
     row = nrow;
     nrow = __builtin_amdgcn_readlane(rowv, (j + 2 - beg) & 63);
   }
-  float* outp = role ? a.dk : a.dv;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    if (!kvalid[kb]) continue;
-    float* out = outp + base + (size_t)krow[kb] * D;
+  if (kvalid) {
+    float* ov = a.dv + base + (size_t)krow * D;
+    float* ok = a.dk + base + (size_t)krow * D;
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd) {
-      float4 x = *reinterpret_cast<float4*>(out + 16 * jd + 4 * g);
-      x.x += acc[kb][jd][0]; x.y += acc[kb][jd][1]; x.z += acc[kb][jd][2]; x.w += acc[kb][jd][3];
-      *reinterpret_cast<float4*>(out + 16 * jd + 4 * g) = x;
+      float4 x = *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g);
+      x.x += accv[jd][0]; x.y += accv[jd][1]; x.z += accv[jd][2]; x.w += accv[jd][3];
+      *reinterpret_cast<float4*>(ov + 16 * jd + 4 * g) = x;
+      float4 y = *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g);
+      y.x += acck[jd][0]; y.y += acck[jd][1]; y.z += acck[jd][2]; y.w += acck[jd][3];
+      *reinterpret_cast<float4*>(ok + 16 * jd + 4 * g) = y;
     }
   }
 }
@@ -1485,11 +1434,8 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
     else k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);
   }
   if constexpr (sizeof(T) == 2) {
-    if (s.d == 64) {
-      k_bwd_dkv_bf16<64><<<rows, 256, 0, st>>>(a);
-    } else {
-      k_bwd_dkv_bf16<128><<<rows, 256, 0, st>>>(a);
-    }
+    if (s.d == 64) k_bwd_dkv_bf16<64><<<rows, 256, 0, st>>>(a);
+    else k_bwd_dkv_bf16<128><<<rows, 256, 0, st>>>(a);
   } else {
     if (s.d == 64) k_bwd_dkv<T, 64><<<grid, 256, 0, st>>>(a);
     else k_bwd_dkv<T, 128><<<grid, 256, 0, st>>>(a);

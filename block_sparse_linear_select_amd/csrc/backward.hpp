@@ -428,17 +428,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
   }
 }
 
-// bf16 sparse dQ: one block per query tile = 2 waves x 32 queries (each K,
-// V or K^T fragment read from LDS feeds two matrix-core steps).  K and V
+// bf16 sparse dQ: one block per query tile = NW waves of 64 / NW queries
+// (4 x 16: 162 registers, three waves per SIMD within the 48 KB of LDS a
+// block stages; 2 x 32 would let each fragment read from LDS feed two
+// matrix-core steps, but at 256 registers and 48 KB only three blocks fit a
+// CU, one and a half waves per SIMD).  K and V
 // tiles go global -> LDS by LDS-direct loads into XOR-swizzled tiles; the K
 // tile, double-buffered, is read both by rows (S = Q K^T) and transposed
 // (dq += scale dS K), so each key tile is staged once.  The next K tile loads
 // during the scores step, the next V tile during the dq step.
-template <int D>
-__global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void k_bwd_dq_bf16(BwdArgs a) {
   constexpr int RB = 2 * D, RG = RB / 16;
-  constexpr int NQB = 2, NDB = D / 16;
-  constexpr int NI = 64 * RB / 1024 / 2;   // LDS-direct loads per wave per tile
+  constexpr int NQB = 2 * 2 / NW, NDB = D / 16;  // 16-query blocks per wave
+  constexpr int NI = 64 * RB / 1024 / NW;   // LDS-direct loads per wave per tile
   __shared__ __align__(16) uint8_t Kb[2][64 * RB];
   __shared__ __align__(16) uint8_t Vs[64 * RB];
 
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
   Frag<bf16_t> qf[NQB][D / 32], gf[NQB][D / 32];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    qrow[qb] = qa * 64 + 32 * w + 16 * qb + l16;
+    qrow[qb] = qa * 64 + 16 * NQB * w + 16 * qb + l16;
     qvalid[qb] = qrow[qb] < a.N;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {  // rows >= N read as zeros
@@ -482,8 +485,8 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
   const int beg = a.row_ptr[(size_t)bh * a.T + qa], end = a.row_ptr[(size_t)bh * a.T + qa + 1];
   const float c2 = a.scale * kLog2e;
   int koff[NI], voff[NI];
-  dma_offsets_kt<RB>(w, lane, koff);
-  dma_offsets<RB, false>(w, lane, voff);
+  dma_offsets_kt<RB, NW>(w, lane, koff);
+  dma_offsets<RB, false, NW>(w, lane, voff);
   const int kaddr = l16 * RB + 16 * (g ^ swz_kt<RG>(l16));
   const int vaddr = l16 * RB + 16 * (g ^ swz_k<RG>(l16));
   const int rowl = 4 * g + (l16 >> 2);
@@ -492,15 +495,15 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
   int col = __builtin_amdgcn_readlane(colv, 0);
   int ncol = __builtin_amdgcn_readlane(colv, 1);
   if (beg < end) {
-    dma_tile<RB>(krs, col, koff, Kb[0], w);
-    dma_tile<RB>(vrs, col, voff, Vs, w);
+    dma_tile<RB, NW>(krs, col, koff, Kb[0], w);
+    dma_tile<RB, NW>(vrs, col, voff, Vs, w);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   for (int j = beg; j < end; ++j) {
     const int cur = (j - beg) & 1;
     const bool more = j + 1 < end;
-    if (more) dma_tile<RB>(krs, ncol, koff, Kb[cur ^ 1], w);  // that buffer was last read by the previous dq step
+    if (more) dma_tile<RB, NW>(krs, ncol, koff, Kb[cur ^ 1], w);  // that buffer was last read by the previous dq step
     const uint8_t* Kc = Kb[cur];
     const int kvalid = (col >= 0 && col < a.T) ? min(64, a.N - col * 64) : 0;
     Frag<bf16_t> dsf[NQB][2];
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_dq_bf16(BwdArgs a) {
       }
     }
     lds_barrier();  // both waves are done with V
-    if (more) dma_tile<RB>(vrs, ncol, voff, Vs, w);
+    if (more) dma_tile<RB, NW>(vrs, ncol, voff, Vs, w);
     if (kvalid > 0) {
 #pragma unroll
       for (int jd = 0; jd < NDB; ++jd) {
@@ -1427,8 +1430,8 @@ static hipError_t bwd_sparse(const Shape& s, BwdArgs a, int32_t* csc_cnt, int32_
   a.col_order = csc_cnt;
   const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
   if constexpr (sizeof(T) == 2) {
-    if (s.d == 64) k_bwd_dq_bf16<64><<<grid, 128, 0, st>>>(a);
-    else k_bwd_dq_bf16<128><<<grid, 128, 0, st>>>(a);
+    if (s.d == 64) k_bwd_dq_bf16<64, 4><<<grid, 256, 0, st>>>(a);
+    else k_bwd_dq_bf16<128, 4><<<grid, 256, 0, st>>>(a);
   } else {
     if (s.d == 64) k_bwd_dq<T, 64><<<grid, 256, 0, st>>>(a);
     else k_bwd_dq<T, 128><<<grid, 256, 0, st>>>(a);

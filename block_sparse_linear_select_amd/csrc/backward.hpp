@@ -122,6 +122,26 @@ __device__ __forceinline__ void load8_any(float* x, const bf16_t* p) {
   for (int s = 0; s < 8; ++s) x[s] = bf16_bits_to_f32((w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
 }
 __device__ __forceinline__ void load8_any(float* x, const float* p) { load8f(x, p); }
+// Fragment loads from a per-head parameter array through one buffer
+// descriptor: the lane's byte offset in a register and the fragment's offset
+// as a scalar, so that a loop over many fragments holds no address register
+// per fragment (64-bit per-fragment addresses, hoisted out of the tile loop,
+// would not fit beside the loop's values).
+__device__ __forceinline__ void fload(Frag<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  f.w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ void fload(Frag<float>& f, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f.v[i] = __uint_as_float(a[i]); f.v[4 + i] = __uint_as_float(b[i]); }
+}
+__device__ __forceinline__ void fload8f(float* x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { x[i] = __uint_as_float(a[i]); x[4 + i] = __uint_as_float(b[i]); }
+}
 // (cos, sin) of the rotation of feature pair jp (0 .. r/2 - 1) at latent
 // position (t, y, x)
 template <int R>
@@ -794,6 +814,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   const float* SF = a.s_frag + (size_t)bh * NFE;
   const float* SPF = a.s_pfrag + (size_t)bh * R * D;
   const float* Z = a.z + (size_t)bh * R;
+  // the parameter fragments through buffer descriptors (see fload)
+  constexpr int FB = 64 * 8 * (int)sizeof(T);  // bytes of one operand fragment
+  const __amdgpu_buffer_rsrc_t r_uqf = make_rsrc(UQF, NRB * (D / 32) * FB);
+  const __amdgpu_buffer_rsrc_t r_uqp = make_rsrc(UQP, NDB * NRC * FB);
+  const __amdgpu_buffer_rsrc_t r_wob = make_rsrc(WOB, D * D * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t r_sf = make_rsrc(SF, NFE * 4);
+  const __amdgpu_buffer_rsrc_t r_spf = make_rsrc(SPF, R * D * 4);
+  const int lo_t = lane * 8 * (int)sizeof(T), lo_f = lane * 32;  // the lane's byte offsets in a fragment
   if constexpr (BF) {
     for (int i = tid; i < D * D / 8; i += 256)
       reinterpret_cast<u32x4*>(WOS)[i] = reinterpret_cast<const u32x4*>(WOB)[i];
@@ -852,7 +880,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
           Frag<T> uf;
-          load8(uf, UQF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+          fload(uf, r_uqf, lo_t, (rb * (D / 32) + c) * FB);
           mma(xq, uf, qf[c]);
         }
 #pragma unroll
@@ -900,7 +928,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
         for (int cc = 0; cc < D / 32; ++cc) {
           Frag<T> wf;
           if constexpr (BF) load8(wf, WOS + ((jd * (D / 32) + cc) * 64 + lane) * 8);
-          else load8(wf, WOB + ((size_t)(jd * (D / 32) + cc) * 64 + lane) * 8);
+          else fload(wf, r_wob, lo_t, (jd * (D / 32) + cc) * FB);
           mma(gw[hh], wf, gf[cc]);
         }
         *reinterpret_cast<float4*>(&GN[ql * GST + 16 * jd + 4 * g]) =
@@ -917,7 +945,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
         float x[8];
-        load8f(x, SF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        fload8f(x, r_sf, lo_f, (jd * NRC + rc) * 64 * 32);
         Frag<T> hi, lo;
         split8(x, hi, lo);
         mma_hl(num, hi, lo, qpf[rc]);
@@ -939,7 +967,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
         float x[8];
-        load8f(x, SPF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+        fload8f(x, r_spf, lo_f, (rb * (D / 32) + c) * 64 * 32);
         Frag<T> hi, lo;
         split8(x, hi, lo);
         mma_hl(dqp[rb], hi, lo, gnf[c]);
@@ -976,7 +1004,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
         Frag<T> uf;
-        load8(uf, UQP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        fload(uf, r_uqp, lo_t, (jd * NRC + rc) * FB);
         mma(acc, uf, dxf[rc]);
       }
       *reinterpret_cast<float4*>(dqo + 16 * jd + 4 * g) =

@@ -41,6 +41,7 @@ namespace hsa {
 
 struct BwdArgs {
   int N, N_pad, T, H, nchunk, tpc;
+  int tpc_k;  // key tiles per block of the key-side linear pass
   int gt, gh, gw;
   float scale;             // softmax scale
   const void* q;
@@ -1114,132 +1115,159 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdArgs a) {
 }
 
 // ------------------------------------------------------ linear: key side
-// One block per key tile, 2 waves x 32 keys (two 16-key column blocks per
-// wave, so every operand fragment fetched serves both): x_k, phi_k, k', then
-// dk' = dS v, dv = dS^T k' and dk = ((dz + rho^T dk') * phi'(x_k)) U_k^T,
-// written to dk and dv (pad rows 0; the sparse kernels add to them).
+// One block per (b, h, chunk of key tiles) = 8 waves.  The head's operands
+// (U_k^T and U_k fragments, dS^T fragments, and dS rows, the latter put in
+// fragment order here) are staged in LDS once per block: read per key tile
+// from L2 they were six times the tile's own K and V bytes.  Wave pair p
+// takes key tiles t0 + p, t0 + p + 4, ..., 2 waves x 32 keys per tile (two
+// 16-key column blocks per wave, so every operand fragment read serves both):
+// x_k, phi_k, k', then dk' = dS v, dv = dS^T k' and dk = ((dz + rho^T dk') *
+// phi'(x_k)) U_k^T, written to dk and dv (pad rows 0; the sparse kernels add
+// to them).
 template <typename T, int D, int R>
-__global__ __launch_bounds__(128) void k_bwd_k(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void k_bwd_k(BwdArgs a) {
   constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
   constexpr int NFE = NDB * NRC * 512;
   constexpr int NKB = 2;
-  const int L = uniform(head_interleaved_row(blockIdx.x, a.T));
-  if (L < 0) return;
-  const int bh = uniform(L / a.T), kt = uniform(L - bh * a.T);
-  const int h = bh % a.H;
+  constexpr int NUF = NRB * (D / 32) * 512, NUP = NDB * NRC * 512;  // elements of the U_k operands
+  __shared__ __align__(16) T UKF[NUF];
+  __shared__ __align__(16) T UKP[NUP];
+  __shared__ __align__(16) float DSF[NFE];
+  __shared__ __align__(16) float DSP[R * D];  // dS rows as A fragments: (rb, c) lane l16 + 16 g -> dS[16 rb + l16][32 c + 8 g ..]
+  const int bh = blockIdx.y, h = bh % a.H;
+  const int t0 = blockIdx.x * a.tpc_k, t1 = min(a.T, t0 + a.tpc_k);
+  if (t0 >= t1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int pair = w >> 1, wk = w & 1;
   const size_t base = (size_t)bh * a.N_pad * D;
   const T* K = reinterpret_cast<const T*>(a.k) + base;
   const T* V = reinterpret_cast<const T*>(a.v) + base;
-  const T* UKF = reinterpret_cast<const T*>(a.uk_frag) + (size_t)h * NRB * (D / 32) * 512;
-  const T* UKP = reinterpret_cast<const T*>(a.ukp_frag) + (size_t)h * NDB * NRC * 512;
-  const float* DSF = a.ds_frag + (size_t)bh * NFE;
-  const float* DSP = a.ds_plain + (size_t)bh * R * D;
+  {
+    const T* gu = reinterpret_cast<const T*>(a.uk_frag) + (size_t)h * NUF;
+    const T* gp = reinterpret_cast<const T*>(a.ukp_frag) + (size_t)h * NUP;
+    const float* gs = a.ds_frag + (size_t)bh * NFE;
+    const float* gd = a.ds_plain + (size_t)bh * R * D;
+    constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16 bytes
+    for (int i = tid; i < NUF / EPV; i += 512) reinterpret_cast<u32x4*>(UKF)[i] = reinterpret_cast<const u32x4*>(gu)[i];
+    for (int i = tid; i < NUP / EPV; i += 512) reinterpret_cast<u32x4*>(UKP)[i] = reinterpret_cast<const u32x4*>(gp)[i];
+    for (int i = tid; i < NFE / 4; i += 512) reinterpret_cast<float4*>(DSF)[i] = reinterpret_cast<const float4*>(gs)[i];
+    for (int i = tid; i < R * D / 8; i += 512) {  // 8 consecutive d of one row r: one lane's slots of a fragment
+      const int r = i / (D / 8), d0 = 8 * (i % (D / 8));
+      const int f = (r / 16) * (D / 32) + d0 / 32, l = (r % 16) + 16 * ((d0 % 32) / 8);
+      float4* dst = reinterpret_cast<float4*>(&DSP[(f * 64 + l) * 8]);
+      const float4* src = reinterpret_cast<const float4*>(gd + (size_t)r * D + d0);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    }
+    __syncthreads();
+  }
   const float* DZ = a.dz + (size_t)bh * R;
-  int krow[NKB];
-  bool kvalid[NKB];
-  Frag<T> kf[NKB][D / 32], vf[NKB][D / 32];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    krow[kb] = kt * 64 + 32 * w + 16 * kb + l16;
-    kvalid[kb] = krow[kb] < a.N;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      if (kvalid[kb]) {
-        load8(kf[kb][c], K + (size_t)krow[kb] * D + 32 * c + 8 * g);
-        load8(vf[kb][c], V + (size_t)krow[kb] * D + 32 * c + 8 * g);
-      } else {
-        kf[kb][c].zero();
-        vf[kb][c].zero();
-      }
-    }
-  }
-  f32x4 xk[NKB][NRB], dkp[NKB][NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
+  for (int kt = t0 + pair; kt < t1; kt += 4) {
+    int krow[NKB];
+    bool kvalid[NKB];
+    Frag<T> kf[NKB][D / 32], vf[NKB][D / 32];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      xk[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dkp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      krow[kb] = kt * 64 + 32 * wk + 16 * kb + l16;
+      kvalid[kb] = krow[kb] < a.N;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      Frag<T> uf;
-      load8(uf, UKF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
-      float x[8];
-      load8f(x, DSP + (size_t)(16 * rb + l16) * D + 32 * c + 8 * g);
-      Frag<T> hi, lo;
-      split8(x, hi, lo);
+      for (int c = 0; c < D / 32; ++c) {
+        if (kvalid[kb]) {
+          load8(kf[kb][c], K + (size_t)krow[kb] * D + 32 * c + 8 * g);
+          load8(vf[kb][c], V + (size_t)krow[kb] * D + 32 * c + 8 * g);
+        } else {
+          kf[kb][c].zero();
+          vf[kb][c].zero();
+        }
+      }
+    }
+    f32x4 xk[NKB][NRB], dkp[NKB][NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        mma(xk[kb][rb], uf, kf[kb][c]);
-        mma_hl(dkp[kb][rb], hi, lo, vf[kb][c]);
-      }
-    }
-  }
-  Frag<T> kpf[NKB][NRC], dxf[NKB][NRC];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const int tok = kvalid[kb] ? krow[kb] : 0;
-    const int hw = a.gh * a.gw, pt = tok / hw, rem = tok - pt * hw, py = rem / a.gw, px = rem - py * a.gw;
-    float kp[NRB][4], dx[NRB][4];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int m = 16 * rb + 4 * g + 2 * pr;
-        const float2 cs = rope_at<R>(a.rope, a.gt, a.gh, pt, py, px, m / 2);
-        const float e0 = xk[kb][rb][2 * pr], e1 = xk[kb][rb][2 * pr + 1];
-        const float f0 = elu1(e0), f1 = elu1(e1);
-        kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
-        kp[rb][2 * pr + 1] = f0 * cs.y + f1 * cs.x;
-        const float x0 = dkp[kb][rb][2 * pr], x1 = dkp[kb][rb][2 * pr + 1];
-        const float d0 = DZ[m] + (x0 * cs.x + x1 * cs.y);
-        const float d1 = DZ[m + 1] + (-x0 * cs.y + x1 * cs.x);
-        dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : f0);
-        dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : f1);
+        xk[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dkp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-    for (int rc = 0; rc < NRC; ++rc) {
-      const bool two = 2 * rc + 1 < NRB;
-      const int b1 = two ? 2 * rc + 1 : 2 * rc;
-      const float keep = two ? 1.f : 0.f;
-      pack_rows(kpf[kb][rc], f32x4{kp[2 * rc][0], kp[2 * rc][1], kp[2 * rc][2], kp[2 * rc][3]},
-                f32x4{keep * kp[b1][0], keep * kp[b1][1], keep * kp[b1][2], keep * kp[b1][3]}, 1.f);
-      pack_rows(dxf[kb][rc], f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]},
-                f32x4{keep * dx[b1][0], keep * dx[b1][1], keep * dx[b1][2], keep * dx[b1][3]}, 1.f);
-    }
-  }
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<T> uf;
+        load8(uf, UKF + ((size_t)(rb * (D / 32) + c) * 64 + lane) * 8);
+        float x[8];
+        load8f(x, DSP + ((rb * (D / 32) + c) * 64 + lane) * 8);
+        Frag<T> hi, lo;
+        split8(x, hi, lo);
 #pragma unroll
-  for (int jd = 0; jd < NDB; ++jd) {
-    f32x4 av[NKB], ak[NKB];
+        for (int kb = 0; kb < NKB; ++kb) {
+          mma(xk[kb][rb], uf, kf[kb][c]);
+          mma_hl(dkp[kb][rb], hi, lo, vf[kb][c]);
+        }
+      }
+    }
+    Frag<T> kpf[NKB][NRC], dxf[NKB][NRC];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      av[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      ak[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int tok = kvalid[kb] ? krow[kb] : 0;
+      const int hw = a.gh * a.gw, pt = tok / hw, rem = tok - pt * hw, py = rem / a.gw, px = rem - py * a.gw;
+      float kp[NRB][4], dx[NRB][4];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int m = 16 * rb + 4 * g + 2 * pr;
+          const float2 cs = rope_at<R>(a.rope, a.gt, a.gh, pt, py, px, m / 2);
+          const float e0 = xk[kb][rb][2 * pr], e1 = xk[kb][rb][2 * pr + 1];
+          const float f0 = elu1(e0), f1 = elu1(e1);
+          kp[rb][2 * pr] = f0 * cs.x - f1 * cs.y;
+          kp[rb][2 * pr + 1] = f0 * cs.y + f1 * cs.x;
+          const float x0 = dkp[kb][rb][2 * pr], x1 = dkp[kb][rb][2 * pr + 1];
+          const float d0 = DZ[m] + (x0 * cs.x + x1 * cs.y);
+          const float d1 = DZ[m + 1] + (-x0 * cs.y + x1 * cs.x);
+          dx[rb][2 * pr] = d0 * (e0 > 0.f ? 1.f : f0);
+          dx[rb][2 * pr + 1] = d1 * (e1 > 0.f ? 1.f : f1);
+        }
+#pragma unroll
+      for (int rc = 0; rc < NRC; ++rc) {
+        const bool two = 2 * rc + 1 < NRB;
+        const int b1 = two ? 2 * rc + 1 : 2 * rc;
+        const float keep = two ? 1.f : 0.f;
+        pack_rows(kpf[kb][rc], f32x4{kp[2 * rc][0], kp[2 * rc][1], kp[2 * rc][2], kp[2 * rc][3]},
+                  f32x4{keep * kp[b1][0], keep * kp[b1][1], keep * kp[b1][2], keep * kp[b1][3]}, 1.f);
+        pack_rows(dxf[kb][rc], f32x4{dx[2 * rc][0], dx[2 * rc][1], dx[2 * rc][2], dx[2 * rc][3]},
+                  f32x4{keep * dx[b1][0], keep * dx[b1][1], keep * dx[b1][2], keep * dx[b1][3]}, 1.f);
+      }
     }
 #pragma unroll
-    for (int rc = 0; rc < NRC; ++rc) {
-      float x[8];
-      load8f(x, DSF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
-      Frag<T> hi, lo;
-      split8(x, hi, lo);
-      Frag<T> uf;
-      load8(uf, UKP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+    for (int jd = 0; jd < NDB; ++jd) {
+      f32x4 av[NKB], ak[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        mma_hl(av[kb], hi, lo, kpf[kb][rc]);
-        mma(ak[kb], uf, dxf[kb][rc]);
+        av[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ak[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float* dko = a.dk + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
-      float* dvo = a.dv + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
-      *reinterpret_cast<float4*>(dko) = kvalid[kb] ? make_float4(ak[kb][0], ak[kb][1], ak[kb][2], ak[kb][3]) : zero;
-      *reinterpret_cast<float4*>(dvo) = kvalid[kb] ? make_float4(av[kb][0], av[kb][1], av[kb][2], av[kb][3]) : zero;
+      for (int rc = 0; rc < NRC; ++rc) {
+        float x[8];
+        load8f(x, DSF + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+        Frag<T> hi, lo;
+        split8(x, hi, lo);
+        Frag<T> uf;
+        load8(uf, UKP + ((size_t)(jd * NRC + rc) * 64 + lane) * 8);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          mma_hl(av[kb], hi, lo, kpf[kb][rc]);
+          mma(ak[kb], uf, dxf[kb][rc]);
+        }
+      }
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float* dko = a.dk + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
+        float* dvo = a.dv + base + (size_t)krow[kb] * D + 16 * jd + 4 * g;
+        *reinterpret_cast<float4*>(dko) = kvalid[kb] ? make_float4(ak[kb][0], ak[kb][1], ak[kb][2], ak[kb][3]) : zero;
+        *reinterpret_cast<float4*>(dvo) = kvalid[kb] ? make_float4(av[kb][0], av[kb][1], av[kb][2], av[kb][3]) : zero;
+      }
     }
   }
 }
@@ -1416,8 +1444,7 @@ static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_bwd_fin<T, D, R><<<dim3(s.B * s.H, R / 8), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long grid = 8 * (a.nrows / a.T) * ((a.T + 7) / 8);
-  k_bwd_k<T, D, R><<<grid, 128, 0, st>>>(a);
+  k_bwd_k<T, D, R><<<dim3((a.T + a.tpc_k - 1) / a.tpc_k, s.B * s.H), 512, 0, st>>>(a);
   return hipGetLastError();
 }
 

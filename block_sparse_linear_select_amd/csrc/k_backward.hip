@@ -12,6 +12,14 @@ hipError_t launch_backward(const Shape& s, const void* q, const void* k, const v
   a.N = s.N; a.N_pad = s.N_pad; a.T = s.T; a.H = s.H;
   a.nchunk = stream_chunks(s);
   a.tpc = (s.T + a.nchunk - 1) / a.nchunk;
+  {  // key-side linear pass: blocks of 8 waves over chunks of key tiles, about one block per CU in all
+    const int bhs = s.B * s.H;
+    int nk = 256 / bhs;
+    nk = nk < 1 ? 1 : nk;
+    const int maxk = (s.T + 3) / 4;  // at least four tiles (one per wave pair) per block
+    nk = nk > maxk ? maxk : nk;
+    a.tpc_k = (s.T + nk - 1) / nk;
+  }
   a.gt = s.gt; a.gh = s.gh; a.gw = s.gw;
   a.scale = s.scale;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.uq = uq; a.uk = uk; a.wo = wo;

@@ -768,14 +768,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(BwdArgs a) {
 }
 
 // ---------------------------------------------------- linear: query side
-// One block per (b, h, chunk of query tiles), 4 waves x 16 queries per tile.
-// Per query: the readout's forward quantities (x_q, phi_q, q', num, den), gW,
-// D = dO . O_s, the linear branch's dq (written to dq: the sparse kernel adds
-// to it), and the contributions to dS (through LDS: dnum and q' of the 64
-// queries, contracted over queries on the matrix cores) and dz.  One partial
-// dS, dz per block.
+// One block per (b, h, pair of chunks of query tiles) = two groups of 4 waves
+// x 16 queries per tile, one group per chunk.  Per query: the readout's
+// forward quantities (x_q, phi_q, q', num, den), gW, D = dO . O_s, the linear
+// branch's dq (written to dq: the sparse kernel adds to it), and the
+// contributions to dS (through LDS: dnum and q' of the 64 queries, contracted
+// over queries on the matrix cores) and dz.  One partial dS, dz per chunk.
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void k_bwd_q(BwdArgs a) {
   constexpr int NDB = D / 16, NRB = R / 16, NRC = (R + 31) / 32;
   constexpr int NFE = NDB * NRC * 512;
   constexpr int GST = D + 4, QST = R + 4;       // LDS row strides (floats)
@@ -787,22 +787,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   // gW step reads them from LDS instead of from L2 for every tile and wave
   constexpr bool BF = sizeof(T) == 2;
   constexpr int QSTB = R + 8;                    // bf16 q' row stride (elements)
-  __shared__ __align__(16) float GN[64 * GST];
-  __shared__ __align__(16) float QP[BF ? 4 : 64 * QST];
-  __shared__ __align__(16) uint16_t QPB[BF ? 64 * QSTB : 8];
+  constexpr int NUF = NRB * (D / 32) * 512, NUP = NDB * NRC * 512;  // elements of the U_q operands
+  // per group: dnum and q' of the group's tile; shared: W_o^T, U_q^T and U_q fragments
+  __shared__ __align__(16) float GNa[2][64 * GST];
+  __shared__ __align__(16) float QPa[2][BF ? 4 : 64 * QST];
+  __shared__ __align__(16) uint16_t QPBa[2][BF ? 64 * QSTB : 8];
   __shared__ __align__(16) T WOS[BF ? D * D : 8];
-  __shared__ float zred[4][R];
+  __shared__ __align__(16) T UQFS[BF ? NUF : 8];
+  __shared__ __align__(16) T UQPS[BF ? NUP : 8];
+  __shared__ float zred[2][4][R];
 
   // XCD-aware order: the hardware hands block i to XCD i % 8; all chunks of
   // (b, h) run on XCD bh % 8, so each XCD's L2 holds the per-head operand
   // fragments (~128 KB) of a few heads only.
+  // Two groups of 4 waves per block: group grp takes chunk 2 c + grp of the
+  // (b, h)'s query tiles, exactly the tiles (and order) a chunk's own block
+  // would take, and writes that chunk's partial sums; the groups share the
+  // head's operand fragments staged in LDS.
+  const int npair = (a.nchunk + 1) / 2;
   const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-  const int bh = xcd + 8 * (jx / a.nchunk), chunk = jx % a.nchunk;
+  const int bh = xcd + 8 * (jx / npair), cpair = jx % npair;
   if (bh >= (int)(a.nrows / a.T)) return;
   const int h = bh % a.H;
-  const int t0 = chunk * a.tpc, t1 = min(a.T, t0 + a.tpc);
-  if (t0 >= t1) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 8, w = (tid >> 6) & 3;
+  const int chunk = 2 * cpair + grp;
+  const int t0 = chunk * a.tpc, t1 = min(a.T, t0 + a.tpc);  // empty for a chunk past the last
+  const int niter = min(a.T - 2 * cpair * a.tpc, a.tpc);     // the first chunk of the pair is the longer
+  float* GN = GNa[grp];
+  float* QP = QPa[grp];
+  uint16_t* QPB = QPBa[grp];
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)bh * a.N_pad * D;
   const T* Q = reinterpret_cast<const T*>(a.q) + base;
@@ -824,8 +837,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t r_spf = make_rsrc(SPF, R * D * 4);
   const int lo_t = lane * 8 * (int)sizeof(T), lo_f = lane * 32;  // the lane's byte offsets in a fragment
   if constexpr (BF) {
-    for (int i = tid; i < D * D / 8; i += 256)
+    for (int i = tid; i < D * D / 8; i += 512)
       reinterpret_cast<u32x4*>(WOS)[i] = reinterpret_cast<const u32x4*>(WOB)[i];
+    for (int i = tid; i < NUF / 8; i += 512)
+      reinterpret_cast<u32x4*>(UQFS)[i] = reinterpret_cast<const u32x4*>(UQF)[i];
+    for (int i = tid; i < NUP / 8; i += 512)
+      reinterpret_cast<u32x4*>(UQPS)[i] = reinterpret_cast<const u32x4*>(UQP)[i];
     __syncthreads();
   }
 
@@ -838,7 +855,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dzl[rb][i] = 0.f;
 
-  for (int t = t0; t < t1; ++t) {
+  for (int it = 0; it < niter; ++it) {  // the same count in both groups (the barriers pair up)
+    const int t = t0 + it;
+    const bool live = t < t1;
+    if (live) {
     const int qrow = t * 64 + 16 * w + l16;
     const bool qvalid = qrow < a.N;
     Frag<T> qf[D / 32], gf[D / 32];
@@ -881,7 +901,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
           Frag<T> uf;
-          fload(uf, r_uqf, lo_t, (rb * (D / 32) + c) * FB);
+          if constexpr (BF) load8(uf, UQFS + ((rb * (D / 32) + c) * 64 + lane) * 8);
+          else fload(uf, r_uqf, lo_t, (rb * (D / 32) + c) * FB);
           mma(xq, uf, qf[c]);
         }
 #pragma unroll
@@ -1005,7 +1026,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
 #pragma unroll
       for (int rc = 0; rc < NRC; ++rc) {
         Frag<T> uf;
-        fload(uf, r_uqp, lo_t, (jd * NRC + rc) * FB);
+        if constexpr (BF) load8(uf, UQPS + ((jd * NRC + rc) * 64 + lane) * 8);
+        else fload(uf, r_uqp, lo_t, (jd * NRC + rc) * FB);
         mma(acc, uf, dxf[rc]);
       }
       *reinterpret_cast<float4*>(dqo + 16 * jd + 4 * g) =
@@ -1016,7 +1038,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dzl[rb][i] = fmaf(gden, fq[rb][i], dzl[rb][i]);
+    }
     __syncthreads();
+    if (live) {
     // dS^T (d x r) += dnum^T q' over the tile's 64 queries
 #pragma unroll
     for (int ii = 0; ii < NBW; ++ii) {
@@ -1044,12 +1068,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
         mma_hl(dsacc[ii], hi, lo, qb);
       }
     }
+    }
     __syncthreads();
   }
   // partials: dS [r][d] rows m = 16 rb + l16, columns 16 je + 4 g .. + 3
   const size_t pb = (size_t)bh * a.nchunk + chunk;
+  const bool own = t0 < t1;  // this group's chunk exists
 #pragma unroll
-  for (int ii = 0; ii < NBW; ++ii) {
+  for (int ii = 0; ii < (own ? NBW : 0); ++ii) {
     const int bi = w + 4 * ii, je = bi % NDB, rb = bi / NDB;
     *reinterpret_cast<float4*>(&a.part_ds[(pb * R + 16 * rb + l16) * D + 16 * je + 4 * g]) =
         make_float4(dsacc[ii][0], dsacc[ii][1], dsacc[ii][2], dsacc[ii][3]);
@@ -1064,10 +1090,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_q(BwdArgs a) {
       x += wave_xor(x, 2);
       x += wave_xor(x, 4);
       x += wave_xor(x, 8);
-      if (l16 == 0) zred[w][16 * rb + 4 * g + i] = x;
+      if (l16 == 0) zred[grp][w][16 * rb + 4 * g + i] = x;
     }
   __syncthreads();
-  if (tid < R) a.part_dz[pb * R + tid] = (zred[0][tid] + zred[1][tid]) + (zred[2][tid] + zred[3][tid]);
+  const int gt_ = tid & 255;
+  if (own && gt_ < R)
+    a.part_dz[pb * R + gt_] = (zred[grp][0][gt_] + zred[grp][1][gt_]) + (zred[grp][2][gt_] + zred[grp][3][gt_]);
 }
 
 // ------------------------------------------------ linear: partial sums
@@ -1440,7 +1468,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv_bf16(BwdArgs a) {
 template <typename T, int D, int R>
 static hipError_t bwd_launch_linear(const Shape& s, const BwdArgs& a, hipStream_t st) {
   hipError_t e;
-  k_bwd_q<T, D, R><<<8 * a.nchunk * ((s.B * s.H + 7) / 8), 256, 0, st>>>(a);
+  k_bwd_q<T, D, R><<<8 * ((a.nchunk + 1) / 2) * ((s.B * s.H + 7) / 8), 512, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_bwd_fin<T, D, R><<<dim3(s.B * s.H, R / 8), 256, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -271,7 +271,7 @@ static __global__ __launch_bounds__(1024) void k_csc_scan(int n, const int32_t* 
 // handled by one block wherever it stands).  One block per (b, h): a bitonic
 // sort of (bucket << 16 | tile) keys in LDS, for T <= kOrderMaxT.
 constexpr int kOrderShift = 6;
-constexpr int kOrderRun = 32;
+constexpr int kOrderRun = 16;
 constexpr int kOrderMaxT = 2048;
 static __global__ __launch_bounds__(1024) void k_csc_order(int T, const int32_t* __restrict__ col_ptr, long cap,
                                                            int32_t* __restrict__ order) {
